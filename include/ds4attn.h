@@ -1,0 +1,201 @@
+/*
+ * ds4attn.h -- C ABI of the fused multi-query FlashAttention step for MI355X (gfx950).
+ *
+ * One attention step of the DeepSeek V4 Flash engine: every query head of a
+ * token attends, with one shared K/V head, to the rows of two KV regions under
+ * one softmax.  Region 0 holds the raw sliding-window rows, region 1 the pooled
+ * compressed rows, either all of them or a per-token index list.  It runs in three
+ * stages:
+ *
+ *   ds4attn_pad       KV rows padded to 32-row blocks
+ *   ds4attn_blockmap  one status byte per (query tile, KV block): skip / partial / full
+ *   ds4attn_decode    fused Q.K^T, online softmax and P.V (tuned for few tokens)
+ *   ds4attn_prefill   the same computation, tuned for long token chunks
+ *
+ * Pages the operations follow:
+ *   [P-Metal] "How DeepSeek V4 Flash Model Inference Works on Apple Silicon with
+ *             Metal Backend" (instagit.com, antirez/ds4)
+ *   [P-DS4]   "DwarfStar 4 (DS4) -- DeepSeek V4 Flash Inference Engine"
+ *             (wikichat.gnat.co, summary of ds4.md)
+ *
+ * Conventions shared by every entry point:
+ *   - Pointers marked "device" are HIP device addresses; the caller owns every
+ *     buffer.  The library allocates nothing, frees nothing, keeps no pointer past
+ *     the call and has no mutable global state; calls are thread-safe.
+ *   - All work is enqueued on `stream` (a hipStream_t, NULL = the null stream)
+ *     and runs asynchronously; the library never synchronises.
+ *   - Arguments are checked before anything is enqueued.  On any nonzero
+ *     return nothing was enqueued (except DS4ATTN_E_HIP, which reports a
+ *     failed launch).  A fault while the kernels run surfaces at the caller's
+ *     next synchronisation.  No C++ exception crosses this boundary.
+ *   - Byte strides: every stride is in bytes and must be a multiple of 16;
+ *     every device pointer to K, V, Q or O must be 16-byte aligned.  Rows of K,
+ *     V, Q and O are contiguous along the head dimension.
+ *   - Output O is always float32, [batch][n_tok][n_head][head_dim] by strides.
+ */
+#ifndef DS4ATTN_H
+#define DS4ATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Status codes returned by every entry point. */
+enum {
+  DS4ATTN_OK = 0,
+  DS4ATTN_E_INVAL = 1,        /* a null pointer, a negative size, a bad stride or alignment */
+  DS4ATTN_E_UNSUPPORTED = 2,  /* a valid request this build has no kernel for */
+  DS4ATTN_E_HIP = 4           /* the HIP runtime refused a launch */
+};
+
+/* Element types of Q, K and V (Q and K/V must match).  O is always float32. */
+enum { DS4ATTN_F16 = 0, DS4ATTN_F32 = 1 };
+
+/* Status byte values of the block map ([P-Metal] "Mask Handling and Block Skipping":
+ * a single-byte status per block; fully masked blocks are skipped).  FULL marks a
+ * block whose every (token, row) pair is visible, so the mask need not be read. */
+enum { DS4ATTN_BLK_SKIP = 0, DS4ATTN_BLK_PARTIAL = 1, DS4ATTN_BLK_FULL = 2 };
+
+/* Flags of ds4attn_args.flags. */
+enum {
+  /* Run the generic vector-ALU kernel even where the matrix-core kernel applies
+   * ([P-Metal] "Vector vs Non-Vector Execution Paths": a path that handles any
+   * head size).  Results agree within rounding; it exists for cross-checks. */
+  DS4ATTN_FLAG_GENERIC = 1
+};
+
+/* One KV region.  Row r of sequence b starts at  k + b*stride_b + r*stride_row
+ * (same for v).  K and V may alias (one "KV" row, [P-DS4] KV Cache Design).
+ * Rows [0, n_rows) are live; the attention kernels read whole 32-row blocks, so
+ * rows [n_rows, ceil32(n_rows)) must exist (ds4attn_pad provides them).  Rows
+ * that are masked are never allowed to reach the result, whatever they hold.
+ * valid: device uint8 [batch][valid_stride_b bytes], nonzero = row visible, or
+ * NULL = every live row visible. */
+typedef struct ds4attn_region {
+  const void *k;
+  const void *v;
+  const uint8_t *valid;
+  int64_t stride_b;
+  int64_t stride_row;
+  int64_t valid_stride_b;
+  int32_t n_rows;
+  int32_t reserved;
+} ds4attn_region;
+
+/* Description of one attention call ([P-DS4] "Architecture Deep Dive":
+ * 64 query heads, 1 KV head, head dim 512, 128-token sliding window, raw plus
+ * compressed rows; ratio-4 layers attend an indexer's top-512 compressed rows).
+ *
+ * Visibility of key rows for token t of sequence b (t in [0, n_tok)):
+ *   region 0 row j:  j < r0.n_rows, r0.valid[b][j] != 0 (if given), and when
+ *                    window > 0:  0 <= (q_pos0 + t) - (k_pos0 + j) < window.
+ *   region 1 row c:  r1_index == NULL: c < r1.n_rows and r1.valid[b][c] != 0 (if given);
+ *                    r1_index != NULL: c = r1_index[(b*n_tok + t)*r1_k + e] for each
+ *                    entry e with 0 <= c < r1.n_rows and r1.valid[b][c] != 0 (if
+ *                    given); entries act as a multiset; other entries are unused.
+ * O[b][t][h] = sum_a p_a V_a,  p = softmax_a(scale * Q[b][t][h] . K_a) over the
+ * visible rows a of both regions; a token with no visible row gets O = 0. */
+typedef struct ds4attn_args {
+  int32_t batch;        /* B >= 0 independent sequences */
+  int32_t n_tok;        /* T >= 0 query tokens per sequence */
+  int32_t n_head;       /* H >= 1 query heads (one KV head) */
+  int32_t head_dim;     /* D: 64, 128, 256 or 512 */
+  int32_t dtype;        /* DS4ATTN_F16 or DS4ATTN_F32, for Q, K and V */
+  int32_t flags;        /* DS4ATTN_FLAG_* */
+  int64_t q_stride_b, q_stride_t, q_stride_h;   /* bytes */
+  int64_t o_stride_b, o_stride_t, o_stride_h;   /* bytes (float32 output) */
+  float scale;          /* softmax scale, normally (float)(1/sqrt(head_dim)) */
+  int32_t window;       /* 0 = no positional mask on region 0 */
+  int64_t q_pos0;       /* position of token 0 */
+  int64_t k_pos0;       /* position of region-0 row 0 */
+  ds4attn_region r0;    /* raw rows */
+  ds4attn_region r1;    /* compressed rows; n_rows = 0 if absent */
+  const int32_t *r1_index;  /* device int32 [B][T][r1_k], or NULL */
+  int32_t r1_k;             /* entries per token when r1_index != NULL (1..2048) */
+  int32_t reserved;
+} ds4attn_args;
+
+/*
+ * ds4attn_pad -- pad one KV region to whole 32-row blocks
+ * ([P-Metal] "KV-Cache Management on Metal Device Buffers": the cache is
+ * padded to a multiple of 32 rows so the attention kernel reads full blocks;
+ * "FlashAttention Kernel Architecture": the pad kernel aligns accesses to
+ * 32-row boundaries).
+ *
+ *   in       region with in->n_rows live rows; in->k, in->v device [B][n_rows][head_dim]
+ *            by in->stride_b / in->stride_row; in->valid optional.
+ *   k_pad, v_pad  device outputs [B][ceil32(n_rows)][head_dim] by out_stride_b /
+ *            out_stride_row.  Rows < n_rows are copied bit for bit; rows
+ *            [n_rows, ceil32(n_rows)) are set to +0.0 (all bits zero).  If
+ *            k_pad == in->k with equal strides (in place, the buffer already has
+ *            the capacity) the live rows are left as they are; partly
+ *            overlapping buffers are rejected.
+ *   valid_pad  optional device uint8 [B][valid_pad_stride_b] output: byte r =
+ *            in->valid[b][r] (or 1 without in->valid) for r < n_rows, 0 for the tail.
+ * Returns DS4ATTN_OK, DS4ATTN_E_INVAL or DS4ATTN_E_HIP.
+ */
+int ds4attn_pad(const ds4attn_region *in, int32_t batch, int32_t head_dim, int32_t dtype,
+                void *k_pad, void *v_pad, int64_t out_stride_b, int64_t out_stride_row,
+                uint8_t *valid_pad, int64_t valid_pad_stride_b, void *stream);
+
+/*
+ * ds4attn_blockmap -- the skip map ([P-Metal] "Mask Handling and Block Skipping":
+ * the mask is scanned and one status byte is written per block; the attention
+ * kernel skips fully masked blocks).
+ *
+ * Blocks are 32 KV rows of the dense part of the key space: the ceil32(r0.n_rows)/32
+ * blocks of region 0, followed, when r1_index == NULL, by the ceil32(r1.n_rows)/32
+ * blocks of region 1 (an indexed region has no shared blocks and is not mapped).
+ * Query tiles are bq consecutive tokens (the last tile may be shorter).
+ *   blk  device uint8 [B][ceil(n_tok/bq)][nb] written here, nb from ds4attn_blockmap_dims;
+ *        byte = SKIP if no (token, row) pair of the tile x block is visible,
+ *        FULL if every pair is (padding rows are never visible), else PARTIAL.
+ * Only the mask fields of *a are read (sizes, window, positions, validity, r1_index
+ * presence); q/o strides and dtype are ignored.
+ * Returns DS4ATTN_OK, DS4ATTN_E_INVAL or DS4ATTN_E_HIP.
+ */
+int ds4attn_blockmap(const ds4attn_args *a, int32_t bq, uint8_t *blk, void *stream);
+
+/* Sizes of the map for *a and bq: *n_tiles = ceil(n_tok/bq), *n_blocks = nb.
+ * Host only; returns DS4ATTN_OK or DS4ATTN_E_INVAL. */
+int ds4attn_blockmap_dims(const ds4attn_args *a, int32_t bq, int64_t *n_tiles, int32_t *n_blocks);
+
+/*
+ * ds4attn_decode / ds4attn_prefill -- fused Q.K^T, online softmax and P.V in one
+ * dispatch ([P-Metal] "FlashAttention Kernel Architecture": dot products,
+ * softmax and weighted value sum fused into a single GPU dispatch), skipping the
+ * blocks the map marks SKIP ([P-Metal] "Mask Handling and Block Skipping").
+ *
+ *   q    device [B][T][H][D] of a->dtype by a->q_stride_*
+ *   blk  device map from ds4attn_blockmap with the same *a and this bq, or NULL
+ *        (then no block is skipped and every block is masked pair by pair; the
+ *        result is the same)
+ *   o    device float32 [B][T][H][D] by a->o_stride_*; every element is written.
+ * Both compute the same result.  decode splits the heads of a token over
+ * several workgroups (for T = 1 and small batches); prefill keeps all heads of a
+ * token in one workgroup (for 2048-token chunks,
+ * [P-DS4] Whole-Model Graph Execution).  Supported: D in {64,128,256,512},
+ * F16 or F32; D = 512 F16 with H % 16 == 0 runs on the matrix cores, the rest
+ * on the vector-ALU kernel.
+ * Returns DS4ATTN_OK, DS4ATTN_E_INVAL, DS4ATTN_E_UNSUPPORTED or DS4ATTN_E_HIP.
+ */
+int ds4attn_decode(const ds4attn_args *a, const void *q, const uint8_t *blk, int32_t bq,
+                   float *o, void *stream);
+int ds4attn_prefill(const ds4attn_args *a, const void *q, const uint8_t *blk, int32_t bq,
+                    float *o, void *stream);
+
+/* The query-tile size the prefill kernel is tuned for (a map built with any
+ * bq >= 1 is accepted). */
+int32_t ds4attn_prefill_bq(void);
+
+/* A static, NUL-terminated description of a status code. */
+const char *ds4attn_status_string(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* DS4ATTN_H */

@@ -1,0 +1,223 @@
+// C ABI of libds4attn: argument checks, parameter resolution and kernel dispatch.
+// Every check runs on the host before anything is enqueued (see include/ds4attn.h).
+#include "ds4attn.h"
+#include "ds4attn_internal.h"
+
+#include <cmath>
+
+using namespace ds4attn;
+
+namespace {
+
+constexpr int kMaxIndexK = kIdxCap;
+
+inline int64_t ceil32(int64_t n) { return (n + 31) / 32 * 32; }
+inline bool aligned16(const void *ptr) { return ((uintptr_t)ptr & 15u) == 0; }
+inline bool stride16(int64_t s) { return s >= 0 && (s & 15) == 0; }
+inline int elem_bytes(int32_t dtype) { return dtype == DS4ATTN_F16 ? 2 : 4; }
+inline bool head_dim_ok(int32_t d) { return d == 64 || d == 128 || d == 256 || d == 512; }
+
+// A region with n_rows > 0 needs K, V and strides that hold whole padded rows.
+int check_region(const ds4attn_region &r, int32_t batch, int row_bytes, bool need_kv) {
+  if (r.n_rows < 0) return DS4ATTN_E_INVAL;
+  if (r.n_rows == 0 || batch == 0) return DS4ATTN_OK;
+  if (r.valid && (batch > 1 && r.valid_stride_b < r.n_rows)) return DS4ATTN_E_INVAL;
+  if (!need_kv) return DS4ATTN_OK;
+  if (!r.k || !r.v || !aligned16(r.k) || !aligned16(r.v)) return DS4ATTN_E_INVAL;
+  if (!stride16(r.stride_row) || r.stride_row < row_bytes || !stride16(r.stride_b))
+    return DS4ATTN_E_INVAL;
+  if (batch > 1 && r.stride_b < ceil32(r.n_rows) * r.stride_row) return DS4ATTN_E_INVAL;
+  return DS4ATTN_OK;
+}
+
+// Mask-side checks shared by blockmap and attention; fills the mask fields of P.
+int resolve_mask(const ds4attn_args *a, int row_bytes, bool need_kv, AttnParams &P) {
+  if (!a) return DS4ATTN_E_INVAL;
+  if (a->batch < 0 || a->n_tok < 0 || a->n_head < 1) return DS4ATTN_E_INVAL;
+  if (a->window < 0) return DS4ATTN_E_INVAL;
+  int st = check_region(a->r0, a->batch, row_bytes, need_kv);
+  if (st) return st;
+  st = check_region(a->r1, a->batch, row_bytes, need_kv);
+  if (st) return st;
+  if (a->r1_index && (a->r1_k < 1 || a->r1_k > kMaxIndexK)) return DS4ATTN_E_INVAL;
+  P = AttnParams{};
+  P.B = a->batch;
+  P.T = a->n_tok;
+  P.H = a->n_head;
+  P.D = a->head_dim;
+  P.window = a->window;
+  P.qk_delta = a->q_pos0 - a->k_pos0;
+  P.k0 = (const char *)a->r0.k;
+  P.v0 = (const char *)a->r0.v;
+  P.kv0_sb = a->r0.stride_b;
+  P.kv0_sr = a->r0.stride_row;
+  P.valid0 = a->r0.valid;
+  P.valid0_sb = a->r0.valid_stride_b;
+  P.n0 = a->r0.n_rows;
+  P.nb0 = (int)(ceil32(a->r0.n_rows) / 32);
+  P.k1 = (const char *)a->r1.k;
+  P.v1 = (const char *)a->r1.v;
+  P.kv1_sb = a->r1.stride_b;
+  P.kv1_sr = a->r1.stride_row;
+  P.valid1 = a->r1.valid;
+  P.valid1_sb = a->r1.valid_stride_b;
+  P.n1 = a->r1.n_rows;
+  P.indexed = a->r1_index != nullptr;
+  P.idx = a->r1_index;
+  P.r1_k = P.indexed ? a->r1_k : 0;
+  if (P.n1 == 0) P.nb1 = 0;
+  else P.nb1 = P.indexed ? (P.r1_k + 31) / 32 : (int)(ceil32(P.n1) / 32);
+  P.nbd = P.nb0 + (P.indexed ? 0 : P.nb1);
+  return DS4ATTN_OK;
+}
+
+int run_attention(const ds4attn_args *a, const void *q, const uint8_t *blk, int32_t bq, float *o,
+                  void *stream, int heads_per_group) {
+  if (!a) return DS4ATTN_E_INVAL;
+  if (a->dtype != DS4ATTN_F16 && a->dtype != DS4ATTN_F32) return DS4ATTN_E_INVAL;
+  if (a->head_dim <= 0) return DS4ATTN_E_INVAL;
+  if (!head_dim_ok(a->head_dim)) return DS4ATTN_E_UNSUPPORTED;
+  if (!std::isfinite(a->scale)) return DS4ATTN_E_INVAL;
+  const int eb = elem_bytes(a->dtype);
+  const int row_bytes = a->head_dim * eb;
+  AttnParams P;
+  int st = resolve_mask(a, row_bytes, true, P);
+  if (st) return st;
+  const int64_t work = (int64_t)a->batch * a->n_tok;
+  if (work == 0) return DS4ATTN_OK;
+  if (!q || !o || !aligned16(q) || !aligned16(o)) return DS4ATTN_E_INVAL;
+  if (!stride16(a->q_stride_b) || !stride16(a->q_stride_t) || !stride16(a->q_stride_h) ||
+      !stride16(a->o_stride_b) || !stride16(a->o_stride_t) || !stride16(a->o_stride_h))
+    return DS4ATTN_E_INVAL;
+  if (a->n_head > 1 && (a->q_stride_h < row_bytes || a->o_stride_h < a->head_dim * 4))
+    return DS4ATTN_E_INVAL;
+  if (blk && bq < 1) return DS4ATTN_E_INVAL;
+  if (P.indexed && !a->r1_index) return DS4ATTN_E_INVAL;
+  if (work * a->n_head > 0x7fffffffLL) return DS4ATTN_E_UNSUPPORTED;
+  P.q = (const char *)q;
+  P.o = (char *)o;
+  P.q_sb = a->q_stride_b;
+  P.q_st = a->q_stride_t;
+  P.q_sh = a->q_stride_h;
+  P.o_sb = a->o_stride_b;
+  P.o_st = a->o_stride_t;
+  P.o_sh = a->o_stride_h;
+  P.scale_log2 = a->scale * 1.4426950408889634f;
+  P.blk = blk;
+  P.bq = blk ? bq : 1;
+  P.ntiles = (a->n_tok + P.bq - 1) / P.bq;
+  hipStream_t s = (hipStream_t)stream;
+  hipError_t e;
+  const bool mfma = a->dtype == DS4ATTN_F16 && a->head_dim == 512 && a->n_head % 16 == 0 &&
+                    !(a->flags & DS4ATTN_FLAG_GENERIC);
+  if (mfma) {
+    int hg = heads_per_group;
+    while (a->n_head % hg) hg >>= 1;   // 64 -> 32 -> 16, n_head % 16 == 0 holds
+    e = launch_attn_mfma(P, hg, s);
+  } else {
+    e = launch_attn_generic(P, eb, s);
+  }
+  return e == hipSuccess ? DS4ATTN_OK : DS4ATTN_E_HIP;
+}
+
+bool ranges_overlap(const void *a, int64_t alen, const void *b, int64_t blen) {
+  const uintptr_t a0 = (uintptr_t)a, b0 = (uintptr_t)b;
+  return a0 < b0 + (uintptr_t)blen && b0 < a0 + (uintptr_t)alen;
+}
+
+}  // namespace
+
+extern "C" {
+
+int ds4attn_pad(const ds4attn_region *in, int32_t batch, int32_t head_dim, int32_t dtype,
+                void *k_pad, void *v_pad, int64_t out_stride_b, int64_t out_stride_row,
+                uint8_t *valid_pad, int64_t valid_pad_stride_b, void *stream) {
+  if (!in || batch < 0 || in->n_rows < 0) return DS4ATTN_E_INVAL;
+  if (dtype != DS4ATTN_F16 && dtype != DS4ATTN_F32) return DS4ATTN_E_INVAL;
+  if (head_dim <= 0 || (head_dim * elem_bytes(dtype)) % 16) return DS4ATTN_E_INVAL;
+  const int row_bytes = head_dim * elem_bytes(dtype);
+  const int64_t n = in->n_rows, npad = ceil32(n);
+  if (batch == 0 || npad == 0) return DS4ATTN_OK;
+  if (!k_pad || !v_pad || !aligned16(k_pad) || !aligned16(v_pad)) return DS4ATTN_E_INVAL;
+  if (!stride16(out_stride_row) || out_stride_row < row_bytes || !stride16(out_stride_b))
+    return DS4ATTN_E_INVAL;
+  if (batch > 1 && out_stride_b < npad * out_stride_row) return DS4ATTN_E_INVAL;
+  if (n > 0) {
+    if (!in->k || !in->v || !aligned16(in->k) || !aligned16(in->v)) return DS4ATTN_E_INVAL;
+    if (!stride16(in->stride_row) || in->stride_row < row_bytes || !stride16(in->stride_b))
+      return DS4ATTN_E_INVAL;
+    if (batch > 1 && in->stride_b < n * in->stride_row) return DS4ATTN_E_INVAL;
+  }
+  if (valid_pad && batch > 1 && valid_pad_stride_b < npad) return DS4ATTN_E_INVAL;
+  if (in->valid && batch > 1 && in->valid_stride_b < n) return DS4ATTN_E_INVAL;
+  if (npad > 0x7fffffffLL) return DS4ATTN_E_UNSUPPORTED;
+  const bool same_layout = in->stride_b == out_stride_b && in->stride_row == out_stride_row;
+  const bool inplace_k = n > 0 && k_pad == in->k && same_layout;
+  const bool inplace_v = n > 0 && v_pad == in->v && same_layout;
+  const int64_t out_len = (batch - 1) * out_stride_b + (npad - 1) * out_stride_row + row_bytes;
+  if (n > 0) {
+    const int64_t in_len = (batch - 1) * in->stride_b + (n - 1) * in->stride_row + row_bytes;
+    if (!inplace_k && ranges_overlap(k_pad, out_len, in->k, in_len)) return DS4ATTN_E_INVAL;
+    if (!inplace_v && ranges_overlap(v_pad, out_len, in->v, in_len)) return DS4ATTN_E_INVAL;
+    if (!inplace_k && ranges_overlap(k_pad, out_len, in->v, in_len) && in->k != in->v)
+      return DS4ATTN_E_INVAL;
+  }
+  // K and V outputs may be one buffer only when K and V inputs are one buffer too.
+  if (ranges_overlap(k_pad, out_len, v_pad, out_len) && !(k_pad == v_pad && in->k == in->v))
+    return DS4ATTN_E_INVAL;
+  hipError_t e = launch_pad(in->k, in->v, in->valid, in->stride_b, in->stride_row,
+                            in->valid_stride_b, k_pad, v_pad, valid_pad, out_stride_b,
+                            out_stride_row, valid_pad_stride_b, batch, (int)n, (int)npad,
+                            row_bytes, !inplace_k, !inplace_v, (hipStream_t)stream);
+  return e == hipSuccess ? DS4ATTN_OK : DS4ATTN_E_HIP;
+}
+
+int ds4attn_blockmap_dims(const ds4attn_args *a, int32_t bq, int64_t *n_tiles, int32_t *n_blocks) {
+  if (!a || bq < 1 || !n_tiles || !n_blocks) return DS4ATTN_E_INVAL;
+  if (a->n_tok < 0 || a->r0.n_rows < 0 || a->r1.n_rows < 0) return DS4ATTN_E_INVAL;
+  *n_tiles = ((int64_t)a->n_tok + bq - 1) / bq;
+  int64_t nb = ceil32(a->r0.n_rows) / 32;
+  if (!a->r1_index) nb += ceil32(a->r1.n_rows) / 32;
+  *n_blocks = (int32_t)nb;
+  return DS4ATTN_OK;
+}
+
+int ds4attn_blockmap(const ds4attn_args *a, int32_t bq, uint8_t *blk, void *stream) {
+  if (!a || bq < 1) return DS4ATTN_E_INVAL;
+  AttnParams P;
+  // Only the mask side is read: sizes, window, positions, validity, index presence.
+  int st = resolve_mask(a, 16, false, P);
+  if (st) return st;
+  P.bq = bq;
+  P.ntiles = ((int64_t)a->n_tok + bq - 1) / bq;
+  const int64_t total = (int64_t)P.B * P.ntiles * P.nbd;
+  if (total == 0) return DS4ATTN_OK;
+  if (!blk) return DS4ATTN_E_INVAL;
+  if ((total + 3) / 4 > 0x7fffffffLL) return DS4ATTN_E_UNSUPPORTED;
+  hipError_t e = launch_blockmap(P, blk, (hipStream_t)stream);
+  return e == hipSuccess ? DS4ATTN_OK : DS4ATTN_E_HIP;
+}
+
+int ds4attn_decode(const ds4attn_args *a, const void *q, const uint8_t *blk, int32_t bq, float *o,
+                   void *stream) {
+  return run_attention(a, q, blk, bq, o, stream, 16);
+}
+
+int ds4attn_prefill(const ds4attn_args *a, const void *q, const uint8_t *blk, int32_t bq, float *o,
+                    void *stream) {
+  return run_attention(a, q, blk, bq, o, stream, 64);
+}
+
+int32_t ds4attn_prefill_bq(void) { return 16; }
+
+const char *ds4attn_status_string(int status) {
+  switch (status) {
+    case DS4ATTN_OK: return "ok";
+    case DS4ATTN_E_INVAL: return "invalid argument";
+    case DS4ATTN_E_UNSUPPORTED: return "unsupported configuration";
+    case DS4ATTN_E_HIP: return "HIP launch failed";
+    default: return "unknown status";
+  }
+}
+
+}  // extern "C"

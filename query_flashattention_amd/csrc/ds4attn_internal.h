@@ -1,0 +1,116 @@
+// Internal declarations shared by the ds4attn HIP sources (not part of the ABI).
+//
+// [P-Metal] = page "How DeepSeek V4 Flash Model Inference Works on Apple Silicon
+//             with Metal Backend";
+// [P-DS4]   = page "DwarfStar 4 (DS4) -- DeepSeek V4 Flash Inference Engine".
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace ds4attn {
+
+constexpr int kRowsPerBlock = 32;   // [P-Metal] KV-Cache Management: 32-row padding
+constexpr int kNumXcd = 8;          // MI355X: 8 accelerator dies, workgroups dealt round-robin
+constexpr int kIdxCap = 2048;       // largest index list held in LDS by the matrix-core kernel
+
+enum : int { kSkip = 0, kPartial = 1, kFull = 2 };
+
+// Everything a kernel needs, resolved on the host from ds4attn_args.
+struct AttnParams {
+  const char *q;
+  char *o;
+  int64_t q_sb, q_st, q_sh;
+  int64_t o_sb, o_st, o_sh;
+  int B, T, H, D;
+  float scale_log2;        // scale * log2(e): softmax runs in base 2
+  int window;              // 0 = no positional mask on region 0
+  int64_t qk_delta;        // q_pos0 - k_pos0
+  // region 0 (raw rows)
+  const char *k0, *v0;
+  int64_t kv0_sb, kv0_sr;
+  const uint8_t *valid0;
+  int64_t valid0_sb;
+  int n0, nb0;             // live rows, 32-row blocks
+  // region 1 (compressed rows)
+  const char *k1, *v1;
+  int64_t kv1_sb, kv1_sr;
+  const uint8_t *valid1;
+  int64_t valid1_sb;
+  int n1, nb1;             // live rows; blocks in the key space (dense: ceil32(n1)/32,
+                           // indexed: ceil(r1_k/32), 0 when n1 == 0)
+  const int32_t *idx;      // [B][T][r1_k] or null
+  int r1_k;
+  int indexed;
+  // block map
+  const uint8_t *blk;      // [B][ntiles][nbd] or null (every block treated as PARTIAL)
+  int bq;
+  int64_t ntiles;
+  int nbd;                 // blocks covered by the map: nb0 (+ nb1 when not indexed)
+};
+
+// ----------------------------------------------------------------------------- device helpers
+
+// Workgroups are dealt to the dies round-robin; give each die a contiguous run of
+// logical work items so neighbours (head groups of one token, adjacent tokens)
+// share that die's L2.  A bijection on [0, n) for any n.
+__device__ __forceinline__ int64_t xcd_remap(int64_t i, int64_t n) {
+  const int64_t x = i % kNumXcd, k = i / kNumXcd;
+  const int64_t per = n / kNumXcd, rem = n % kNumXcd;
+  return (x < rem ? x * (per + 1) : rem * (per + 1) + (x - rem) * per) + k;
+}
+
+// Visibility of region-0 row `row` for token t (the allowed-row rule of the header).
+__device__ __forceinline__ bool r0_visible(const AttnParams &p, int b, int t, int row) {
+  if (row >= p.n0) return false;
+  if (p.valid0 && p.valid0[(int64_t)b * p.valid0_sb + row] == 0) return false;
+  if (p.window > 0) {
+    const int64_t d = p.qk_delta + t - row;
+    if (d < 0 || d >= p.window) return false;
+  }
+  return true;
+}
+
+// Visibility of region-1 row c (dense or gathered through the index list).
+__device__ __forceinline__ bool r1_visible(const AttnParams &p, int b, int c) {
+  if (c < 0 || c >= p.n1) return false;
+  if (p.valid1 && p.valid1[(int64_t)b * p.valid1_sb + c] == 0) return false;
+  return true;
+}
+
+// Status of key block j for the token's query tile: map entries for the dense
+// blocks, PARTIAL for gathered blocks (their rows differ per token).
+// Wave-uniform: returns the first block >= j that is not SKIP (or nbt), and its status.
+__device__ __forceinline__ int next_block(const uint8_t *row, int nbd, int nbt, int j, int lane,
+                                          int &status) {
+  while (j < nbt) {
+    if (j >= nbd) {
+      status = kPartial;
+      return j;
+    }
+    const int jj = j + lane;
+    int s = 0;
+    if (jj < nbt) s = (jj < nbd) ? (row ? (int)row[jj] : kPartial) : kPartial;
+    const unsigned long long m = __ballot(s != 0);
+    if (m) {
+      const int k = __ffsll((unsigned long long)m) - 1;
+      status = __builtin_amdgcn_readfirstlane(__shfl(s, k));
+      return j + k;
+    }
+    j += 64;
+  }
+  status = kSkip;
+  return nbt;
+}
+
+// ----------------------------------------------------------------------------- launchers
+
+hipError_t launch_pad(const void *k, const void *v, const uint8_t *valid, int64_t in_sb,
+                      int64_t in_sr, int64_t valid_sb, void *kp, void *vp, uint8_t *validp,
+                      int64_t out_sb, int64_t out_sr, int64_t validp_sb, int B, int n, int npad,
+                      int row_bytes, bool copy_k, bool copy_v, hipStream_t s);
+hipError_t launch_blockmap(const AttnParams &p, uint8_t *blk, hipStream_t s);
+hipError_t launch_attn_generic(const AttnParams &p, int elem_bytes, hipStream_t s);
+hipError_t launch_attn_mfma(const AttnParams &p, int heads_per_group, hipStream_t s);
+
+}  // namespace ds4attn

@@ -1,0 +1,124 @@
+// Padding and block-map kernels.
+//
+// pad: a KV region becomes whole 32-row blocks -- live rows copied bit for bit,
+// the tail rows zero, and a validity byte per row ([P-Metal] "KV-Cache
+// Management on Metal Device Buffers"; "FlashAttention Kernel Architecture",
+// the pad kernel).
+//
+// blockmap: one status byte per (query tile, 32-row key block) -- skip, partial or
+// full -- so the attention kernel can pass over fully masked blocks ([P-Metal]
+// "Mask Handling and Block Skipping").
+#include "ds4attn_internal.h"
+
+namespace ds4attn {
+
+// One thread per 16-byte chunk of one row in [row_lo, npad) of each sequence.
+__global__ __launch_bounds__(256) void pad_rows_kernel(
+    const char *__restrict__ k, const char *__restrict__ v, int64_t in_sb, int64_t in_sr,
+    char *__restrict__ kp, char *__restrict__ vp, int64_t out_sb, int64_t out_sr, int n,
+    int row_lo, int nrows_out, int chunks_per_row, int64_t total, bool copy_k, bool copy_v) {
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= total) return;
+  const int64_t per_seq = (int64_t)nrows_out * chunks_per_row;
+  const int b = (int)(i / per_seq);
+  const int64_t rem = i - (int64_t)b * per_seq;
+  const int row = row_lo + (int)(rem / chunks_per_row);
+  const int c = (int)(rem % chunks_per_row);
+  const int64_t src = (int64_t)b * in_sb + (int64_t)row * in_sr + 16 * c;
+  const int64_t dst = (int64_t)b * out_sb + (int64_t)row * out_sr + 16 * c;
+  if (row < n) {
+    if (copy_k) *(uint4 *)(kp + dst) = *(const uint4 *)(k + src);
+    if (copy_v) *(uint4 *)(vp + dst) = *(const uint4 *)(v + src);
+  } else {
+    const uint4 z = make_uint4(0u, 0u, 0u, 0u);
+    *(uint4 *)(kp + dst) = z;
+    *(uint4 *)(vp + dst) = z;
+  }
+}
+
+__global__ __launch_bounds__(256) void pad_valid_kernel(const uint8_t *__restrict__ valid,
+                                                        int64_t valid_sb, uint8_t *__restrict__ validp,
+                                                        int64_t validp_sb, int n, int npad,
+                                                        int64_t total) {
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= total) return;
+  const int b = (int)(i / npad);
+  const int row = (int)(i - (int64_t)b * npad);
+  uint8_t x = 0;
+  if (row < n) x = valid ? valid[(int64_t)b * valid_sb + row] : (uint8_t)1;
+  validp[(int64_t)b * validp_sb + row] = x;
+}
+
+hipError_t launch_pad(const void *k, const void *v, const uint8_t *valid, int64_t in_sb,
+                      int64_t in_sr, int64_t valid_sb, void *kp, void *vp, uint8_t *validp,
+                      int64_t out_sb, int64_t out_sr, int64_t validp_sb, int B, int n, int npad,
+                      int row_bytes, bool copy_k, bool copy_v, hipStream_t s) {
+  const int row_lo = (copy_k || copy_v) ? 0 : n;
+  const int nrows_out = npad - row_lo;
+  const int cpr = row_bytes / 16;
+  const int64_t total = (int64_t)B * nrows_out * cpr;
+  if (total > 0) {
+    const int64_t blocks = (total + 255) / 256;
+    hipLaunchKernelGGL(pad_rows_kernel, dim3((unsigned)blocks), dim3(256), 0, s,
+                       (const char *)k, (const char *)v, in_sb, in_sr, (char *)kp, (char *)vp,
+                       out_sb, out_sr, n, row_lo, nrows_out, cpr, total, copy_k, copy_v);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  if (validp) {
+    const int64_t tv = (int64_t)B * npad;
+    if (tv > 0) {
+      hipLaunchKernelGGL(pad_valid_kernel, dim3((unsigned)((tv + 255) / 256)), dim3(256), 0, s,
+                         valid, valid_sb, validp, validp_sb, n, npad, tv);
+      return hipGetLastError();
+    }
+  }
+  return hipSuccess;
+}
+
+// One wave per (sequence, query tile, key block).  Lane r (mod 32) owns row r of
+// the block; lanes 0-31 take the tile's even tokens, lanes 32-63 the odd ones.
+// The block is SKIP when no lane saw a visible pair, FULL when every lane saw
+// only visible pairs (all 32 rows for every token), PARTIAL otherwise.
+__global__ __launch_bounds__(256) void blockmap_kernel(const AttnParams p, uint8_t *__restrict__ blk,
+                                                       int64_t total) {
+  const int lane = threadIdx.x & 63;
+  const int64_t wid = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (wid >= total) return;  // whole wave exits together
+  const int j = (int)(wid % p.nbd);
+  const int64_t bt = wid / p.nbd;
+  const int64_t tile = bt % p.ntiles;
+  const int b = (int)(bt / p.ntiles);
+  const int r = lane & 31;
+  const int t0 = (int)(tile * p.bq);
+  const int t1 = min(p.T, t0 + p.bq);
+  bool any = false, all = true;
+  if (j < p.nb0) {
+    const int row = j * kRowsPerBlock + r;
+    for (int t = t0 + (lane >> 5); t < t1; t += 2) {
+      const bool vis = r0_visible(p, b, t, row);
+      any |= vis;
+      all &= vis;
+    }
+  } else {
+    // dense region 1: visibility does not depend on the token
+    const bool vis = r1_visible(p, b, (j - p.nb0) * kRowsPerBlock + r);
+    if (t0 + (lane >> 5) < t1) {
+      any = vis;
+      all = vis;
+    }
+  }
+  const unsigned long long many = __ballot(any);
+  const unsigned long long mall = __ballot(all);
+  if (lane == 0) blk[wid] = (uint8_t)(many == 0ull ? kSkip : (mall == ~0ull ? kFull : kPartial));
+}
+
+hipError_t launch_blockmap(const AttnParams &p, uint8_t *blk, hipStream_t s) {
+  const int64_t total = (int64_t)p.B * p.ntiles * p.nbd;
+  if (total == 0) return hipSuccess;
+  hipLaunchKernelGGL(blockmap_kernel, dim3((unsigned)((total + 3) / 4)), dim3(256), 0, s, p, blk,
+                     total);
+  return hipGetLastError();
+}
+
+}  // namespace ds4attn

@@ -1,0 +1,203 @@
+"""Python binding of libds4attn (ctypes): argument marshalling only.
+
+The functions keep the C names (``ds4attn_pad``, ``ds4attn_blockmap``,
+``ds4attn_decode``, ``ds4attn_prefill``, ...).  Tensors are PyTorch tensors on
+the GPU: the binding reads their data pointers, byte strides and torch's
+current HIP stream and passes them through; every step of the computation runs
+in the library's HIP kernels.  There is no fallback: if the library is not
+built, or a call returns an error, a ``RuntimeError`` is raised.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+import torch
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libds4attn.so")
+
+OK, E_INVAL, E_UNSUPPORTED, E_HIP = 0, 1, 2, 4
+F16, F32 = 0, 1
+BLK_SKIP, BLK_PARTIAL, BLK_FULL = 0, 1, 2
+FLAG_GENERIC = 1
+
+_c_void_p = ctypes.c_void_p
+_i32, _i64 = ctypes.c_int32, ctypes.c_int64
+
+
+class Region(ctypes.Structure):
+    _fields_ = [("k", _c_void_p), ("v", _c_void_p), ("valid", _c_void_p),
+                ("stride_b", _i64), ("stride_row", _i64), ("valid_stride_b", _i64),
+                ("n_rows", _i32), ("reserved", _i32)]
+
+
+class Args(ctypes.Structure):
+    _fields_ = [("batch", _i32), ("n_tok", _i32), ("n_head", _i32), ("head_dim", _i32),
+                ("dtype", _i32), ("flags", _i32),
+                ("q_stride_b", _i64), ("q_stride_t", _i64), ("q_stride_h", _i64),
+                ("o_stride_b", _i64), ("o_stride_t", _i64), ("o_stride_h", _i64),
+                ("scale", ctypes.c_float), ("window", _i32),
+                ("q_pos0", _i64), ("k_pos0", _i64),
+                ("r0", Region), ("r1", Region),
+                ("r1_index", _c_void_p), ("r1_k", _i32), ("reserved", _i32)]
+
+
+EXPORTS = ("ds4attn_pad", "ds4attn_blockmap", "ds4attn_blockmap_dims", "ds4attn_decode",
+           "ds4attn_prefill", "ds4attn_prefill_bq", "ds4attn_status_string")
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """Load libds4attn.so (built in-tree by ``__graft_entry__.build()``)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: build it first (python __graft_entry__.py build)")
+        h = ctypes.CDLL(LIB_PATH)
+        h.ds4attn_pad.argtypes = [ctypes.POINTER(Region), _i32, _i32, _i32, _c_void_p, _c_void_p,
+                                  _i64, _i64, _c_void_p, _i64, _c_void_p]
+        h.ds4attn_blockmap.argtypes = [ctypes.POINTER(Args), _i32, _c_void_p, _c_void_p]
+        h.ds4attn_blockmap_dims.argtypes = [ctypes.POINTER(Args), _i32, ctypes.POINTER(_i64),
+                                            ctypes.POINTER(_i32)]
+        for name in ("ds4attn_decode", "ds4attn_prefill"):
+            getattr(h, name).argtypes = [ctypes.POINTER(Args), _c_void_p, _c_void_p, _i32,
+                                         _c_void_p, _c_void_p]
+        for name in ("ds4attn_pad", "ds4attn_blockmap", "ds4attn_blockmap_dims", "ds4attn_decode",
+                     "ds4attn_prefill", "ds4attn_prefill_bq"):
+            getattr(h, name).restype = _i32
+        h.ds4attn_status_string.argtypes = [_i32]
+        h.ds4attn_status_string.restype = ctypes.c_char_p
+        _lib = h
+    return _lib
+
+
+def status_string(status: int) -> str:
+    return lib().ds4attn_status_string(status).decode()
+
+
+def _check(status: int, what: str):
+    if status != OK:
+        raise RuntimeError(f"{what} failed: {status_string(status)} ({status})")
+
+
+def _ptr(t: Optional[torch.Tensor]) -> Optional[int]:
+    return None if t is None else t.data_ptr()
+
+
+def _stream(stream) -> Optional[int]:
+    if stream is None:
+        return torch.cuda.current_stream().cuda_stream if torch.cuda.is_available() else None
+    return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+
+
+def _dtype_code(dt: torch.dtype) -> int:
+    if dt == torch.float16:
+        return F16
+    if dt == torch.float32:
+        return F32
+    raise ValueError(f"unsupported element type {dt}")
+
+
+# --------------------------------------------------------------------------- marshalling
+
+def region(k: Optional[torch.Tensor] = None, v: Optional[torch.Tensor] = None, n_rows: int = 0,
+           valid: Optional[torch.Tensor] = None) -> Region:
+    """A ``Region`` over [B, N, D] K/V tensors (rows contiguous) and optional uint8 [B, N] validity."""
+    r = Region()
+    r.n_rows = int(n_rows)
+    if k is not None:
+        es = k.element_size()
+        r.k, r.v = k.data_ptr(), v.data_ptr()
+        r.stride_b, r.stride_row = k.stride(0) * es, k.stride(1) * es
+        if v.stride() != k.stride():
+            raise ValueError("K and V of one region must share strides")
+    if valid is not None:
+        r.valid = valid.data_ptr()
+        r.valid_stride_b = valid.stride(0)
+    return r
+
+
+def args(q: torch.Tensor, o: Optional[torch.Tensor], r0: Region, r1: Optional[Region] = None,
+         r1_index: Optional[torch.Tensor] = None, scale: float = None, window: int = 0,
+         q_pos0: int = 0, k_pos0: int = 0, flags: int = 0) -> Args:
+    """``Args`` for q [B, T, H, D] and float32 o [B, T, H, D] (o may be None for a map)."""
+    a = Args()
+    b, t, h, d = q.shape
+    a.batch, a.n_tok, a.n_head, a.head_dim = b, t, h, d
+    a.dtype = _dtype_code(q.dtype)
+    a.flags = flags
+    es = q.element_size()
+    a.q_stride_b, a.q_stride_t, a.q_stride_h = (s * es for s in q.stride()[:3])
+    if o is not None:
+        a.o_stride_b, a.o_stride_t, a.o_stride_h = (s * 4 for s in o.stride()[:3])
+    a.scale = float(scale) if scale is not None else 1.0 / d ** 0.5
+    a.window, a.q_pos0, a.k_pos0 = int(window), int(q_pos0), int(k_pos0)
+    a.r0 = r0
+    a.r1 = r1 if r1 is not None else Region()
+    if r1_index is not None:
+        a.r1_index = r1_index.data_ptr()
+        a.r1_k = r1_index.shape[-1]
+    return a
+
+
+# --------------------------------------------------------------------------- entry points
+
+def ds4attn_pad(reg: Region, batch: int, head_dim: int, dtype: int, k_pad: torch.Tensor,
+                v_pad: torch.Tensor, valid_pad: Optional[torch.Tensor] = None, stream=None) -> None:
+    es = k_pad.element_size()
+    _check(lib().ds4attn_pad(ctypes.byref(reg), batch, head_dim, dtype, k_pad.data_ptr(),
+                             v_pad.data_ptr(), k_pad.stride(0) * es, k_pad.stride(1) * es,
+                             _ptr(valid_pad), 0 if valid_pad is None else valid_pad.stride(0),
+                             _stream(stream)), "ds4attn_pad")
+
+
+def ds4attn_blockmap_dims(a: Args, bq: int):
+    nt, nb = _i64(), _i32()
+    _check(lib().ds4attn_blockmap_dims(ctypes.byref(a), bq, ctypes.byref(nt), ctypes.byref(nb)),
+           "ds4attn_blockmap_dims")
+    return int(nt.value), int(nb.value)
+
+
+def ds4attn_blockmap(a: Args, bq: int, blk: Optional[torch.Tensor], stream=None) -> None:
+    _check(lib().ds4attn_blockmap(ctypes.byref(a), bq, _ptr(blk), _stream(stream)), "ds4attn_blockmap")
+
+
+def ds4attn_decode(a: Args, q: torch.Tensor, blk: Optional[torch.Tensor], bq: int, o: torch.Tensor,
+                   stream=None) -> None:
+    _check(lib().ds4attn_decode(ctypes.byref(a), q.data_ptr(), _ptr(blk), bq, o.data_ptr(),
+                                _stream(stream)), "ds4attn_decode")
+
+
+def ds4attn_prefill(a: Args, q: torch.Tensor, blk: Optional[torch.Tensor], bq: int, o: torch.Tensor,
+                    stream=None) -> None:
+    _check(lib().ds4attn_prefill(ctypes.byref(a), q.data_ptr(), _ptr(blk), bq, o.data_ptr(),
+                                 _stream(stream)), "ds4attn_prefill")
+
+
+def ds4attn_prefill_bq() -> int:
+    return int(lib().ds4attn_prefill_bq())
+
+
+# --------------------------------------------------------------------------- the three stages on GPU tensors
+
+def pad_region(k: torch.Tensor, v: torch.Tensor, n_rows: int, valid: Optional[torch.Tensor] = None,
+               stream=None):
+    """Stage 1: new padded K/V [B, ceil32(n), D] and validity [B, ceil32(n)] on k's device."""
+    b, _, d = k.shape
+    npad = -(-n_rows // 32) * 32
+    kp = torch.empty((b, npad, d), dtype=k.dtype, device=k.device)
+    vp = torch.empty((b, npad, d), dtype=v.dtype, device=v.device)
+    vap = torch.empty((b, npad), dtype=torch.uint8, device=k.device)
+    ds4attn_pad(region(k, v, n_rows, valid), b, d, _dtype_code(k.dtype), kp, vp, vap, stream)
+    return kp, vp, vap
+
+
+def blockmap(a: Args, bq: int, device, stream=None) -> torch.Tensor:
+    """Stage 2: the uint8 skip map [B, ceil(T/bq), nb]."""
+    nt, nb = ds4attn_blockmap_dims(a, bq)
+    blk = torch.empty((a.batch, nt, nb), dtype=torch.uint8, device=device)
+    ds4attn_blockmap(a, bq, blk if blk.numel() else None, stream)
+    return blk

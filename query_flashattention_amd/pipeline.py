@@ -1,0 +1,105 @@
+"""The three stages of the attention step on device-resident inputs.
+
+``to_device`` places a seeded workload in GPU memory the way an engine holds its
+KV cache: each region in a buffer with capacity for whole 32-row blocks, the
+tail rows not yet initialised ([P-Metal] "KV-Cache Management on Metal Device
+Buffers").  ``step`` then runs pad (in place) -> block map -> fused attention,
+all in libds4attn's kernels on torch's current stream ([P-Metal]
+"FlashAttention Kernel Architecture": pad, blk and impl kernels).
+
+[P-Metal] = the page "How DeepSeek V4 Flash Model Inference Works on Apple
+Silicon with Metal Backend".
+"""
+
+from __future__ import annotations
+
+from dataclasses import dataclass
+from typing import Optional
+
+import torch
+
+from . import ds4attn as da
+
+
+def _ceil32(n: int) -> int:
+    return -(-n // 32) * 32
+
+
+@dataclass
+class DeviceRegion:
+    k: torch.Tensor              # [B, ceil32(n), D] storage, rows >= n uninitialised until padded
+    v: torch.Tensor
+    n_rows: int
+    valid_in: Optional[torch.Tensor]   # caller's validity [B, n] (uint8) or None
+    valid: Optional[torch.Tensor]      # padded validity [B, ceil32(n)] written by pad, or None
+
+    def region(self) -> da.Region:
+        return da.region(self.k, self.v, self.n_rows, self.valid)
+
+    def pad_in_place(self, stream=None):
+        """Stage 1 in place: zero the tail rows, write the padded validity bytes."""
+        b, _, d = self.k.shape
+        src = da.region(self.k, self.v, self.n_rows, self.valid_in)
+        da.ds4attn_pad(src, b, d, da._dtype_code(self.k.dtype), self.k, self.v, self.valid, stream)
+
+
+@dataclass
+class DeviceProblem:
+    q: torch.Tensor
+    o: torch.Tensor
+    r0: DeviceRegion
+    r1: Optional[DeviceRegion]
+    idx: Optional[torch.Tensor]
+    scale: float
+    window: int
+    q_pos0: int
+    k_pos0: int
+    flags: int = 0
+
+    def args(self) -> da.Args:
+        return da.args(self.q, self.o, self.r0.region(), None if self.r1 is None else self.r1.region(),
+                       self.idx, self.scale, self.window, self.q_pos0, self.k_pos0, self.flags)
+
+
+def _region_to_device(r, device) -> Optional[DeviceRegion]:
+    if r is None:
+        return None
+    b, n, d = r.k.shape
+    cap = _ceil32(r.n_rows)
+    k = torch.empty((b, cap, d), dtype=r.k.dtype, device=device)
+    v = torch.empty((b, cap, d), dtype=r.v.dtype, device=device)
+    k[:, :r.n_rows].copy_(r.k[:, :r.n_rows])
+    v[:, :r.n_rows].copy_(r.v[:, :r.n_rows])
+    valid_in = valid = None
+    if r.valid is not None:
+        valid_in = r.valid[:, :r.n_rows].contiguous().to(device)
+        valid = torch.empty((b, cap), dtype=torch.uint8, device=device)
+    return DeviceRegion(k, v, r.n_rows, valid_in, valid)
+
+
+def to_device(w, device="cuda") -> DeviceProblem:
+    """Copy a seeded workload to the GPU (physical ring order, unpadded tails)."""
+    q = w.q.to(device)
+    o = torch.empty(q.shape, dtype=torch.float32, device=device)
+    idx = None if w.r1_index is None else w.r1_index.contiguous().to(device)
+    return DeviceProblem(q, o, _region_to_device(w.r0, device), _region_to_device(w.r1, device), idx,
+                         w.scale, w.window, w.q_pos0, w.k_pos0)
+
+
+def step(dp: DeviceProblem, entry: str = "decode", bq: int = 1, blk: Optional[torch.Tensor] = None,
+         stream=None) -> torch.Tensor:
+    """One pass of the hot path: pad (in place) -> block map -> fused attention.
+
+    ``blk`` may be a preallocated map buffer of the right size; the output is
+    ``dp.o`` (float32 [B, T, H, D])."""
+    dp.r0.pad_in_place(stream)
+    if dp.r1 is not None:
+        dp.r1.pad_in_place(stream)
+    a = dp.args()
+    if blk is None:
+        blk = da.blockmap(a, bq, dp.q.device, stream)
+    else:
+        da.ds4attn_blockmap(a, bq, blk if blk.numel() else None, stream)
+    fn = da.ds4attn_decode if entry == "decode" else da.ds4attn_prefill
+    fn(a, dp.q, blk if blk.numel() else None, bq, dp.o, stream)
+    return dp.o

@@ -1,0 +1,175 @@
+"""Host-side checks of the C ABI (no GPU needed; no kernel is launched).
+
+* the built library loads and exports every function include/ds4attn.h declares;
+* the ctypes structures have the C layout (checked against gcc's offsetof/sizeof);
+* argument checks return their status codes before anything would be enqueued.
+"""
+
+import ctypes
+import os
+import re
+import subprocess
+import sys
+
+import pytest
+
+from query_flashattention_amd import ds4attn as da
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "ds4attn.h")
+FAKE = 0x7F0000000000  # an aligned address that is never dereferenced on the host
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"^\s*(?:int|int32_t|const char \*)\s*(ds4attn_\w+)\s*\(", text, re.M)))
+
+
+def test_library_exports_every_declared_function():
+    names = _declared_functions()
+    assert len(names) >= 7
+    lib = da.lib()
+    for n in names:
+        assert hasattr(lib, n), f"{n} declared in ds4attn.h but not exported"
+    assert set(names) == set(da.EXPORTS)
+
+
+def test_struct_layout_matches_c_header(tmp_path):
+    fields = {
+        "ds4attn_region": [f[0] for f in da.Region._fields_],
+        "ds4attn_args": [f[0] for f in da.Args._fields_],
+    }
+    lines = ["#include <stdio.h>", "#include <stddef.h>", f'#include "{HEADER}"', "int main(void){"]
+    for st, names in fields.items():
+        lines.append(f'printf("{st} size %zu\\n", sizeof({st}));')
+        for n in names:
+            lines.append(f'printf("{st} {n} %zu\\n", offsetof({st}, {n}));')
+    lines.append("return 0;}")
+    src = tmp_path / "layout.c"
+    src.write_text("\n".join(lines))
+    exe = tmp_path / "layout"
+    subprocess.run(["gcc", "-std=c99", "-o", str(exe), str(src)], check=True)
+    out = subprocess.run([str(exe)], check=True, capture_output=True, text=True).stdout.split("\n")
+    c = {}
+    for line in out:
+        if line:
+            st, key, val = line.split()
+            c[(st, key)] = int(val)
+    for st, cls in (("ds4attn_region", da.Region), ("ds4attn_args", da.Args)):
+        assert c[(st, "size")] == ctypes.sizeof(cls)
+        for n in fields[st]:
+            assert c[(st, n)] == getattr(cls, n).offset, (st, n)
+
+
+def _good_args(head_dim=512, dtype=da.F16, heads=64):
+    a = da.Args()
+    es = 2 if dtype == da.F16 else 4
+    a.batch, a.n_tok, a.n_head, a.head_dim, a.dtype = 1, 1, heads, head_dim, dtype
+    a.q_stride_h = head_dim * es
+    a.q_stride_t = heads * head_dim * es
+    a.q_stride_b = a.q_stride_t
+    a.o_stride_h = head_dim * 4
+    a.o_stride_t = heads * head_dim * 4
+    a.o_stride_b = a.o_stride_t
+    a.scale = 0.044194173
+    a.r0.k = a.r0.v = FAKE
+    a.r0.n_rows = 128
+    a.r0.stride_row = head_dim * es
+    a.r0.stride_b = 128 * head_dim * es
+    return a
+
+
+def _decode(a, q=FAKE, o=FAKE, blk=None, bq=1):
+    return da.lib().ds4attn_decode(ctypes.byref(a), q, blk, bq, o, None)
+
+
+@pytest.mark.parametrize("mutate,expect", [
+    (lambda a: setattr(a, "head_dim", 96), da.E_UNSUPPORTED),
+    (lambda a: setattr(a, "head_dim", 0), da.E_INVAL),
+    (lambda a: setattr(a, "dtype", 7), da.E_INVAL),
+    (lambda a: setattr(a, "n_head", 0), da.E_INVAL),
+    (lambda a: setattr(a, "n_tok", -1), da.E_INVAL),
+    (lambda a: setattr(a, "window", -3), da.E_INVAL),
+    (lambda a: setattr(a, "scale", float("nan")), da.E_INVAL),
+    (lambda a: setattr(a, "q_stride_h", 1000), da.E_INVAL),          # not a multiple of 16
+    (lambda a: setattr(a, "q_stride_h", 512), da.E_INVAL),           # rows overlap
+    (lambda a: setattr(a.r0, "stride_row", 8), da.E_INVAL),
+    (lambda a: setattr(a.r0, "k", FAKE + 8), da.E_INVAL),            # misaligned
+    (lambda a: setattr(a.r0, "v", None), da.E_INVAL),
+    (lambda a: setattr(a.r0, "n_rows", -1), da.E_INVAL),
+    (lambda a: (setattr(a, "r1_index", FAKE), setattr(a, "r1_k", 4097)), da.E_INVAL),
+    (lambda a: (setattr(a, "r1_index", FAKE), setattr(a, "r1_k", 0)), da.E_INVAL),
+])
+def test_decode_rejects_bad_arguments(mutate, expect):
+    a = _good_args()
+    mutate(a)
+    assert _decode(a) == expect
+
+
+def test_null_pointers_and_tile_size():
+    lib = da.lib()
+    assert lib.ds4attn_decode(None, FAKE, None, 1, FAKE, None) == da.E_INVAL
+    a = _good_args()
+    assert _decode(a, q=None) == da.E_INVAL
+    assert _decode(a, o=FAKE + 4) == da.E_INVAL
+    assert _decode(a, blk=FAKE, bq=0) == da.E_INVAL
+    assert lib.ds4attn_blockmap(ctypes.byref(a), 0, FAKE, None) == da.E_INVAL
+    assert lib.ds4attn_blockmap(None, 1, FAKE, None) == da.E_INVAL
+    assert lib.ds4attn_blockmap(ctypes.byref(a), 1, None, None) == da.E_INVAL
+
+
+def test_empty_problems_succeed_without_launch():
+    a = _good_args()
+    a.batch = 0
+    assert _decode(a, q=None, o=None) == da.OK
+    a = _good_args()
+    a.n_tok = 0
+    assert da.lib().ds4attn_prefill(ctypes.byref(a), None, None, 16, None, None) == da.OK
+    assert da.lib().ds4attn_blockmap(ctypes.byref(a), 16, None, None) == da.OK
+
+
+def test_blockmap_dims():
+    a = _good_args()
+    a.n_tok = 2048
+    a.r0.n_rows = 2175
+    assert da.ds4attn_blockmap_dims(a, 16) == (128, 68)
+    a.r1.n_rows = 256
+    assert da.ds4attn_blockmap_dims(a, 1) == (2048, 68 + 8)
+    a.r1_index = FAKE
+    a.r1_k = 512
+    assert da.ds4attn_blockmap_dims(a, 1) == (2048, 68)   # indexed rows are not mapped
+
+
+def test_pad_rejects_bad_arguments():
+    lib = da.lib()
+    r = da.Region()
+    r.k = r.v = FAKE
+    r.n_rows, r.stride_row, r.stride_b = 27, 256, 27 * 256
+    out = FAKE + (1 << 30)
+    assert lib.ds4attn_pad(ctypes.byref(r), 1, 64, da.F32, out, out + (1 << 20), 32 * 256 + 16, 8,
+                           None, 0, None) == da.E_INVAL          # output row stride too small
+    assert lib.ds4attn_pad(ctypes.byref(r), 1, 64, 5, out, out + (1 << 20), 0, 256, None, 0,
+                           None) == da.E_INVAL                   # dtype
+    # outputs overlapping the inputs without being the same buffer
+    assert lib.ds4attn_pad(ctypes.byref(r), 1, 64, da.F32, FAKE + 256, out, 32 * 256, 256, None, 0,
+                           None) == da.E_INVAL
+    # K and V outputs sharing a buffer while the inputs differ
+    r.v = FAKE + (1 << 24)
+    assert lib.ds4attn_pad(ctypes.byref(r), 1, 64, da.F32, out, out, 32 * 256, 256, None, 0,
+                           None) == da.E_INVAL
+    r0 = da.Region()
+    assert lib.ds4attn_pad(ctypes.byref(r0), 1, 64, da.F32, None, None, 0, 0, None, 0, None) == da.OK
+
+
+def test_status_strings_and_tile():
+    assert da.status_string(da.OK) == "ok"
+    assert "invalid" in da.status_string(da.E_INVAL)
+    assert da.ds4attn_prefill_bq() >= 1
+
+
+def test_binding_fails_loudly_without_library(tmp_path, monkeypatch):
+    """The Python side has no fallback path: a missing library is an error."""
+    code = ("import query_flashattention_amd.ds4attn as d; d.LIB_PATH='/nonexistent/libds4attn.so';"
+            "\ntry:\n d.lib()\nexcept RuntimeError as e:\n print('raised', e)")
+    out = subprocess.run([sys.executable, "-c", code], capture_output=True, text=True, cwd=ROOT)
+    assert "raised" in out.stdout
