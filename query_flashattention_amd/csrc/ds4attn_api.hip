@@ -2,6 +2,7 @@
 // Every check runs on the host before anything is enqueued (see include/ds4attn.h).
 #include "ds4attn.h"
 #include "ds4attn_internal.h"
+#include "mfma_common.h"
 
 #include <cmath>
 
@@ -72,7 +73,7 @@ int resolve_mask(const ds4attn_args *a, int row_bytes, bool need_kv, AttnParams 
 }
 
 int run_attention(const ds4attn_args *a, const void *q, const uint8_t *blk, int32_t bq, float *o,
-                  void *stream, int heads_per_group) {
+                  void *stream, bool prefill) {
   if (!a) return DS4ATTN_E_INVAL;
   if (a->dtype != DS4ATTN_F16 && a->dtype != DS4ATTN_F32) return DS4ATTN_E_INVAL;
   if (a->head_dim <= 0) return DS4ATTN_E_INVAL;
@@ -108,15 +109,16 @@ int run_attention(const ds4attn_args *a, const void *q, const uint8_t *blk, int3
   P.ntiles = (a->n_tok + P.bq - 1) / P.bq;
   hipStream_t s = (hipStream_t)stream;
   hipError_t e;
+  // The matrix-core kernels list the token's non-skipped map blocks in LDS
+  // (up to kListCap of them); longer dense regions run on the vector-ALU kernel.
+  // ... and address each sequence's K/V region with 32-bit offsets (< 2^31 bytes).
+  const int64_t rows1 = P.indexed ? ceil32(P.n1) : (int64_t)P.nb1 * 32;
+  const bool fits32 = (int64_t)P.nb0 * 32 * P.kv0_sr < 0x80000000LL && rows1 * P.kv1_sr < 0x80000000LL;
   const bool mfma = a->dtype == DS4ATTN_F16 && a->head_dim == 512 && a->n_head % 16 == 0 &&
-                    !(a->flags & DS4ATTN_FLAG_GENERIC);
-  if (mfma) {
-    int hg = heads_per_group;
-    while (a->n_head % hg) hg >>= 1;   // 64 -> 32 -> 16, n_head % 16 == 0 holds
-    e = launch_attn_mfma(P, hg, s);
-  } else {
-    e = launch_attn_generic(P, eb, s);
-  }
+                    !(a->flags & DS4ATTN_FLAG_GENERIC) && P.nbd <= kListCap && fits32;
+  if (mfma && prefill && a->n_head % 64 == 0) e = launch_attn_prefill(P, s);
+  else if (mfma) e = launch_attn_decode(P, s);
+  else e = launch_attn_generic(P, eb, s);
   return e == hipSuccess ? DS4ATTN_OK : DS4ATTN_E_HIP;
 }
 
@@ -200,12 +202,12 @@ int ds4attn_blockmap(const ds4attn_args *a, int32_t bq, uint8_t *blk, void *stre
 
 int ds4attn_decode(const ds4attn_args *a, const void *q, const uint8_t *blk, int32_t bq, float *o,
                    void *stream) {
-  return run_attention(a, q, blk, bq, o, stream, 16);
+  return run_attention(a, q, blk, bq, o, stream, false);
 }
 
 int ds4attn_prefill(const ds4attn_args *a, const void *q, const uint8_t *blk, int32_t bq, float *o,
                     void *stream) {
-  return run_attention(a, q, blk, bq, o, stream, 64);
+  return run_attention(a, q, blk, bq, o, stream, true);
 }
 
 int32_t ds4attn_prefill_bq(void) { return 16; }

@@ -111,6 +111,9 @@ hipError_t launch_pad(const void *k, const void *v, const uint8_t *valid, int64_
                       int row_bytes, bool copy_k, bool copy_v, hipStream_t s);
 hipError_t launch_blockmap(const AttnParams &p, uint8_t *blk, hipStream_t s);
 hipError_t launch_attn_generic(const AttnParams &p, int elem_bytes, hipStream_t s);
-hipError_t launch_attn_mfma(const AttnParams &p, int heads_per_group, hipStream_t s);
+// Matrix-core kernels (head dim 512, float16): decode splits a token's heads over
+// workgroups of 16; prefill keeps 64 heads of a token in one workgroup.
+hipError_t launch_attn_decode(const AttnParams &p, hipStream_t s);
+hipError_t launch_attn_prefill(const AttnParams &p, hipStream_t s);
 
 }  // namespace ds4attn
