@@ -36,7 +36,7 @@ if ROOT not in sys.path:
 METRIC = "attn decode KV GB/s (%HBM peak) + 2048-tok prefill TFLOP/s (%MFMA peak), d=512"
 HBM_PEAK_GBS = 8000.0           # MI355X HBM3E, published
 MFMA_F16_PEAK_TFLOPS = 2500.0   # MI355X dense fp16 matrix throughput, published
-DECODE_KERNEL_SRC = os.path.join(ROOT, "query_flashattention_amd", "csrc", "attn_mfma.hip")
+DECODE_KERNEL_SRC = os.path.join(ROOT, "query_flashattention_amd", "csrc", "attn_staged.hip")
 
 DESCRIPTIONS = {
     "decode_swa": "decode, raw sliding-window layer: 64 sequences x 1 token x 64 q-heads x d512, "
@@ -336,7 +336,7 @@ def main():
         roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": round(achieved / HBM_PEAK_GBS, 4),
                 "traffic": traffic_from_profiles(DECODE_KERNEL_SRC) if name == "decode_swa" else None,
-                "kernel": "attn_mfma_kernel<16,false> (ds4attn_decode)",
+                "kernel": "attn_staged_kernel<1,false> (ds4attn_decode)",
                 "bytes_per_launch": compulsory, "kernel_ms_mean": round(kern["mean"], 5),
                 "kernel_ms_median": round(kern["median"], 5)}
     else:
@@ -345,7 +345,7 @@ def main():
         achieved = c["flops"] / kern_s / 1e12
         roof = {"bound": "mfma", "achieved": round(achieved, 2), "peak": MFMA_F16_PEAK_TFLOPS,
                 "unit": "TFLOP/s", "frac": round(achieved / MFMA_F16_PEAK_TFLOPS, 4), "traffic": None,
-                "kernel": "attn_mfma_kernel<64,...> (ds4attn_prefill)", "flops_per_launch": c["flops"],
+                "kernel": "attn_staged_kernel<0,...> (ds4attn_prefill)", "flops_per_launch": c["flops"],
                 "kernel_ms_mean": round(kern["mean"], 5)}
 
     out = {

@@ -13,8 +13,8 @@
 //   * each key block is staged once in LDS and read by all four waves: K and V
 //     rows travel global -> LDS directly (16 bytes per lane, a whole 1 KiB row per
 //     instruction, no registers), into tiles whose padded row strides keep the
-//     operand reads on distinct banks; tiles are double-buffered, so block i+1 is
-//     in flight while block i is consumed;
+//     operand reads on distinct banks; with two tile pairs, blocks i+1 and i+2
+//     are in flight while block i is consumed;
 //   * S^T = K Q^T: A operand = 16 K rows from LDS, B operand = Q^T in registers;
 //     in the S^T accumulator layout a lane holds 8 rows of one head, so the
 //     softmax max is in-lane plus two cross-lane steps and the float16 P values
@@ -35,6 +35,8 @@
 //         for small decode batches.
 #include "mfma_common.h"
 
+#include <type_traits>
+
 namespace ds4attn {
 
 typedef short short4_t __attribute__((ext_vector_type(4)));
@@ -43,19 +45,55 @@ typedef __attribute__((address_space(3))) char lds_char;
 
 enum : int { kSplitHeads = 0, kSplitDims = 1 };
 
-// 16 bytes per lane, global -> LDS at byte address `lds` (uniform) + 16 * lane.
-// Issued through asm so that the compiler does not order LDS reads of the other
-// tile buffer behind it; completion is awaited explicitly (s_waitcnt vmcnt(0))
-// before the barrier that publishes the tile.  m0 is not used by anything else in
-// these kernels.
-__device__ __forceinline__ void dma16(const void *src, uint32_t lds) {
-  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
-               :: "v"(src), "s"(lds) : "memory");
+// One row: 16 bytes per lane from `row` + 16 * lane (`row` uniform) into LDS at
+// `lds` + 16 * lane (`lds` uniform).  The row address travels in scalar registers
+// and the lane offset is one shared vector register.  Issued through asm, so the
+// compiler's hazard tracking does not see it: the tracking cannot always tell the
+// tile buffers from the other LDS arrays and would drain every transfer in flight
+// before unrelated LDS reads.  Completion is awaited explicitly (wait_vmcnt)
+// before the barrier that publishes a tile, and a buffer is refilled only after
+// the barrier that ends its reads.  m0 is written only here in these kernels.
+__device__ __forceinline__ void dma16(const char *row, uint32_t lane16, uint32_t lds) {
+  // (the builtin returns int: widen each half as unsigned, never sign-extended)
+  const uint64_t r = (uint64_t)row;
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)r);
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)(r >> 32));
+  const uint64_t ru = ((uint64_t)hi << 32) | (uint64_t)lo;
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1"
+               :: "v"(lane16), "s"(ru), "s"(__builtin_amdgcn_readfirstlane(lds)) : "memory");
 }
 
+// LDS byte address of a shared-memory pointer.
 __device__ __forceinline__ uint32_t lds_addr(const void *p) {
   return (uint32_t)(size_t)(__attribute__((address_space(3))) const void *)p;
 }
+
+// Source of the rows a mask hides: they arrive in LDS as zeros (from L2).
+static __device__ __attribute__((aligned(16))) const char kZeroRow[1024] = {};
+
+// Workgroup barrier for LDS data only: this wave's LDS operations complete, then
+// s_barrier.  (The generic barrier also waits for every outstanding global load,
+// which would drain the tile transfers kept in flight across it.)
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
+// s_waitcnt vmcnt(N) (other counters untouched), issued through the builtin so
+// that the compiler's own wait insertion knows what it has already waited for.
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt is a 6-bit counter");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+  asm volatile("" ::: "memory");
+}
+
+// A stage is exactly 16 vector-memory instructions per wave (8 K rows, 8 V rows);
+// waiting with vmcnt(16) right after issuing one completes every older stage.
+constexpr int kStageOps = 16;
+
+// Visibility masks of list entries live in an LDS ring of 128, filled 64 entries
+// at a time, so the half in use is never overwritten.
+constexpr int kMaskRing = 128, kMaskChunk = 64;
 
 // Tile rows are padded so that rows start on different banks while every operand
 // address stays affine (base + immediate): K rows every 1040 bytes (the 16 rows of
@@ -64,13 +102,6 @@ __device__ __forceinline__ uint32_t lds_addr(const void *p) {
 constexpr int kKRow = 1040, kVRow = 1056;
 constexpr int kKTile = 32 * kKRow, kVTile = 32 * kVRow;
 
-struct StageInfo {
-  int vis_arith;   // lane's row (lane & 31): inside the region and the window
-  int use_byte;    // whether `vbyte` (the row's validity byte) decides visibility
-  int vbyte;
-  int full;
-};
-
 template <int MODE, bool INDEXED>
 __global__ __launch_bounds__(256) void attn_staged_kernel(const AttnParams p) {
   constexpr int HG = MODE == kSplitHeads ? 64 : 16;   // heads per workgroup
@@ -78,9 +109,10 @@ __global__ __launch_bounds__(256) void attn_staged_kernel(const AttnParams p) {
   constexpr int NDT = MODE == kSplitHeads ? 32 : 8;    // 16-dim output tiles per wave
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int w = tid >> 6;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave index (uniform)
   const int g = lane >> 4;       // lane group: operand k-slots 8g..8g+7
   const int c16 = lane & 15;     // MFMA row/column of this lane
+  const uint32_t lane16 = 16u * lane;   // this lane's byte offset in a transferred row
 
   const int ngroups = p.H / HG;
   const int64_t L = xcd_remap(blockIdx.x, gridDim.x);
@@ -99,6 +131,7 @@ __global__ __launch_bounds__(256) void attn_staged_kernel(const AttnParams p) {
   __shared__ uint16_t blist[kListCap];
   __shared__ int cnt[4];
   __shared__ int idx_s[INDEXED ? kIdxCap : 1];
+  __shared__ uint32_t vmask[kMaskRing];   // bit r: row r of the entry's block is visible
 
   // Q^T operand fragments: head h, dims d0 + 32ks + 8g .. +7
   half8 qf[NKS];
@@ -113,7 +146,9 @@ __global__ __launch_bounds__(256) void attn_staged_kernel(const AttnParams p) {
   const int ndense = build_block_list<256>(blkrow, p.nbd, blist, cnt);   // ends with a barrier
   const int nlist = ndense + (INDEXED ? p.nb1 : 0);
 
-  auto entry = [&](int i, int &j, int &status) {
+  // List entry i: key block j (dense blocks of both regions, then the gathered
+  // blocks of an indexed region) and its map status.
+  auto entry_at = [&](int i, int &j, int &status) {
     if (i < ndense) {
       const int e = blist[i];
       j = e & 0x3fff;
@@ -126,103 +161,117 @@ __global__ __launch_bounds__(256) void attn_staged_kernel(const AttnParams p) {
   // validity arrays of this sequence (size 0 when absent: every load out of range)
   const rsrc_t rb0 = make_rsrc(p.valid0 + (int64_t)b * p.valid0_sb, p.valid0 ? (uint32_t)p.n0 : 0u);
   const rsrc_t rb1 = make_rsrc(p.valid1 + (int64_t)b * p.valid1_sb, p.valid1 ? (uint32_t)p.n1 : 0u);
-  // gathered row of index entry e (unused entries read row 0; they are masked)
-  auto rid = [&](int e) {
-    const int c = (e < p.r1_k) ? idx_s[e] : -1;
-    return (c >= 0 && c < p.n1) ? c : 0;
+  // Visibility masks of list entries [c0, c0 + n) into the ring, K rounds of 8
+  // entries per batch of loads: half-wave (w, lane >> 5) takes entry 8k + 2w + (lane >> 5)
+  // of a round, lane & 31 its row.  Every thread must call it (ballots, LDS writes).
+  auto build_masks = [&](int c0, int n, auto rounds) __attribute__((always_inline)) {
+    constexpr int K = decltype(rounds)::value;
+    const int r = lane & 31, half = lane >> 5;
+    for (int e0 = 0; e0 < n; e0 += 8 * K) {
+      int ok[K], full[K], vb0[K], vb1[K];
+      uint32_t off0[K], off1[K];
+#pragma unroll
+      for (int k = 0; k < K; ++k) {
+        const int el = e0 + 8 * k + 2 * w + half;
+        ok[k] = 0;
+        full[k] = 0;
+        off0[k] = off1[k] = kOutOfRange;
+        if (el < n) {
+          int j, status;
+          entry_at(c0 + el, j, status);
+          full[k] = status == kFull;
+          if (j < p.nb0) {
+            const int row = j * kRowsPerBlock + r;
+            bool v = row < p.n0;
+            if (p.window > 0) {
+              const int64_t d = p.qk_delta + t - row;
+              v = v && d >= 0 && d < p.window;
+            }
+            ok[k] = v;
+            if (p.valid0 && row < p.n0) off0[k] = row;
+          } else {
+            const int e = (j - p.nb0) * kRowsPerBlock + r;
+            const int c = INDEXED ? ((e < p.r1_k) ? idx_s[e] : -1) : e;
+            const bool v = c >= 0 && c < p.n1;
+            ok[k] = v;
+            if (p.valid1 && v) off1[k] = c;
+          }
+        }
+      }
+#pragma unroll
+      for (int k = 0; k < K; ++k) {
+        vb0[k] = buf_load_u8(rb0, off0[k]);
+        vb1[k] = buf_load_u8(rb1, off1[k]);
+      }
+#pragma unroll
+      for (int k = 0; k < K; ++k) {
+        const int el = e0 + 8 * k + 2 * w + half;
+        const bool vis = ok[k] && (off0[k] == kOutOfRange || vb0[k] != 0) &&
+                         (off1[k] == kOutOfRange || vb1[k] != 0);
+        const uint64_t bal = __ballot(vis);
+        if (el < n && r == 0)
+          vmask[(c0 + el) & (kMaskRing - 1)] = full[k] ? 0xffffffffu : (uint32_t)(bal >> (32 * half));
+      }
+    }
   };
 
-  // Start the transfers of list entry i into tiles kt / vt (wave w moves rows
-  // 8w..8w+7 of K and of V, one row per instruction) and load the visibility
-  // inputs.  Past the end of the list nothing is transferred.
-  auto stage = [&](int i, const char *kt, const char *vt, StageInfo &st) {
-    int j = 0, status = kFull;
-    const bool real = i < nlist;
-    if (real) entry(i, j, status);
-    st.full = status == kFull;
-    const int r = lane & 31;
-    st.vis_arith = 1;
-    st.use_byte = 0;
-    uint32_t offb = kOutOfRange;   // lane's validity byte offset (out of range when unused)
-    const char *kb = p.q, *vb = p.q;
-    int64_t sr = 0;
-    int base = 0;
-    bool gathered = false;
-    if (!real) {
-      // nothing to stage
-    } else if (j < p.nb0) {
-      base = j * kRowsPerBlock;
+  // Tile buffer pair 0 or 1, chosen at compile time so the compiler can tell the
+  // transfers into one pair from the reads of the other.
+  auto ktile = [&](auto buf) -> char * { return decltype(buf)::value ? kt1 : kt0; };
+  auto vtile = [&](auto buf) -> char * { return decltype(buf)::value ? vt1 : vt0; };
+
+  // Start the transfers of list entry i (< nlist) into buffer pair `buf`: wave w
+  // moves rows 8w..8w+7 of K and of V, one 1 KiB row per instruction, kStageOps
+  // instructions in all.  MASKED: rows the entry's mask hides arrive as zeros (and
+  // are not read from the cache); otherwise every row is transferred (gathered
+  // entries that are unused read row 0) and hidden rows are cleared afterwards.
+  auto stage = [&](int i, auto buf, auto masked) __attribute__((always_inline)) {
+    constexpr bool MASKED = decltype(masked)::value;
+    int j, status;
+    entry_at(i, j, status);
+    j = __builtin_amdgcn_readfirstlane(j);   // uniform: scalar branches and descriptors
+    const uint32_t vm = MASKED ? __builtin_amdgcn_readfirstlane(vmask[i & (kMaskRing - 1)]) : 0xffffffffu;
+    const uint32_t kbase = lds_addr(ktile(buf)), vbase = lds_addr(vtile(buf));
+    const char *kb, *vb;
+    int64_t sr;
+    int base;
+    if (j < p.nb0) {
       kb = p.k0 + b * p.kv0_sb;
       vb = p.v0 + b * p.kv0_sb;
       sr = p.kv0_sr;
-      if (!st.full) {
-        const int row = base + r;
-        bool ok = row < p.n0;
-        if (p.window > 0) {
-          const int64_t d = p.qk_delta + t - row;
-          ok = ok && d >= 0 && d < p.window;
-        }
-        st.vis_arith = ok;
-        if (p.valid0 && row < p.n0) {
-          offb = row;
-          st.use_byte = 1;
-        }
-      }
+      base = j * kRowsPerBlock;
     } else {
-      base = (j - p.nb0) * kRowsPerBlock;
       kb = p.k1 + b * p.kv1_sb;
       vb = p.v1 + b * p.kv1_sb;
       sr = p.kv1_sr;
-      if (INDEXED) {
-        gathered = true;
-        const int e = base + r;
-        const int c = (e < p.r1_k) ? idx_s[e] : -1;
-        const bool ok = c >= 0 && c < p.n1;
-        st.vis_arith = ok;
-        if (p.valid1 && ok) {
-          offb = c;
-          st.use_byte = 1;
-        }
-      } else if (!st.full) {
-        const int c = base + r;
-        st.vis_arith = c < p.n1;
-        if (p.valid1 && c < p.n1) {
-          offb = c;
-          st.use_byte = 1;
-        }
-      }
+      base = (j - p.nb0) * kRowsPerBlock;
     }
-    // the validity byte: an out-of-range (zero, no traffic) load when unused
-    st.vbyte = buf_load_u8(real && j >= p.nb0 ? rb1 : rb0, offb);
-    if (!real) return;
-    const uint32_t kbase = lds_addr(kt), vbase = lds_addr(vt);
+    const bool gathered = INDEXED && j >= p.nb0;
 #pragma unroll
     for (int q = 0; q < 8; ++q) {
       const int rr = 8 * w + q;
-      const int row = gathered ? rid(base + rr) : base + rr;
-      const uint32_t koff = __builtin_amdgcn_readfirstlane(kbase + rr * kKRow);
-      const uint32_t voff = __builtin_amdgcn_readfirstlane(vbase + rr * kVRow);
-      dma16(kb + row * sr + 16 * lane, koff);
-      dma16(vb + row * sr + 16 * lane, voff);
+      int row = base + rr;
+      if (gathered) {
+        const int c = (row < p.r1_k) ? __builtin_amdgcn_readfirstlane(idx_s[row]) : -1;
+        row = (c >= 0 && c < p.n1) ? c : 0;
+      }
+      const bool shown = (vm >> rr) & 1u;
+      dma16(shown ? kb + row * sr : kZeroRow, lane16, kbase + rr * kKRow);
+      dma16(shown ? vb + row * sr : kZeroRow, lane16, vbase + rr * kVRow);
     }
   };
 
-  // Wait for the transfers, resolve visibility, zero masked V rows.  Returns the
-  // block's visibility mask (bit r = row r visible; all ones for a FULL block).
-  auto commit = [&](char *vt, const StageInfo &st) -> uint32_t {
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    if (st.full) return 0xffffffffu;
-    const uint32_t vis = (uint32_t)__ballot(st.vis_arith && (!st.use_byte || st.vbyte != 0));
-    // each wave clears the masked rows among the ones its own transfers wrote
-    // (rows 8w..8w+7): its vmcnt wait above covers exactly those transfers
-    uint32_t masked = (~vis >> (8 * w)) & 0xffu;
-    const uint4 z = make_uint4(0u, 0u, 0u, 0u);
-    while (masked) {
-      const int r = 8 * w + __ffs(masked) - 1;
-      masked &= masked - 1;
-      *(uint4 *)(vt + r * kVRow + 16 * lane) = z;
+  // Clear the V rows of entry i that its mask hides, among this wave's own rows
+  // 8w..8w+7 (its own completed transfers wrote them).
+  auto clear_masked = [&](int i, auto buf) __attribute__((always_inline)) {
+    if (i >= nlist) return;
+    uint32_t hidden = (~vmask[i & (kMaskRing - 1)] >> (8 * w)) & 0xffu;
+    char *vt = vtile(buf);
+    while (hidden) {
+      const int rr = 8 * w + __ffs(hidden) - 1;
+      hidden &= hidden - 1;
+      *(uint4 *)(vt + rr * kVRow + 16 * lane) = make_uint4(0u, 0u, 0u, 0u);
     }
-    return vis;
   };
 
   floatx4 o[NDT];
@@ -236,19 +285,29 @@ __global__ __launch_bounds__(256) void attn_staged_kernel(const AttnParams p) {
   const int tr_e = (lane >> 2) & 3, tr_a = lane & 3;
   const int tr_r0 = 4 * g + tr_e;   // slot rows 0-3 of group g; rows 16 + ... for slots 4-7
 
-  StageInfo st;
-  stage(0, kt0, vt0, st);
-  uint32_t vis_cur = commit(vt0, st);
-  int full_cur = st.full;
-  __syncthreads();
+  // Pipeline: blocks i+1 and i+2 are in flight while block i is consumed.
+  //   prologue: stage 0 -> pair 0 and 1 -> pair 1 unmasked, meanwhile compute the
+  //             masks of the first entries; clear the hidden rows of 0 and 1
+  //   block i (pair B): consume from B; barrier (B free); stage i+2 -> B masked;
+  //                     wait for this wave's transfers of i+1; barrier (publishes i+1)
+  using Pair0 = std::integral_constant<int, 0>;
+  using Pair1 = std::integral_constant<int, 1>;
+  using Masked = std::integral_constant<bool, true>;
+  using Unmasked = std::integral_constant<bool, false>;
+  if (nlist > 0) stage(0, Pair0{}, Unmasked{});
+  if (nlist > 1) stage(1, Pair1{}, Unmasked{});
+  build_masks(0, nlist < kMaskChunk ? nlist : kMaskChunk, std::integral_constant<int, 8>{});
+  wait_vmcnt<0>();
+  lds_barrier();   // masks visible
+  clear_masked(0, Pair0{});
+  clear_masked(1, Pair1{});
+  lds_barrier();   // blocks 0 and 1 ready
 
-  // One block: start the transfers of list position i+1 into the other buffers,
-  // consume block i, then wait for the transfers and publish them.
-  auto iteration = [&](int i, const char *ktc, const char *vtc, char *ktn, char *vtn) {
-    stage(i + 1, ktn, vtn, st);
-
+  auto iteration = [&](int i, auto buf) __attribute__((always_inline)) {
+    constexpr int B = decltype(buf)::value;
     // ---- S^T = K Q^T over this wave's head dims (operand loads one step ahead)
     floatx4 s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
+    const char *ktc = ktile(buf), *vtc = vtile(buf);
     const char *krow0 = ktc + c16 * kKRow + 2 * (d0 + 8 * g), *krow1 = krow0 + 16 * kKRow;
     uint4 a0 = *(const uint4 *)krow0;
     uint4 a1 = *(const uint4 *)krow1;
@@ -269,7 +328,7 @@ __global__ __launch_bounds__(256) void attn_staged_kernel(const AttnParams p) {
       // partial tiles meet in LDS; every wave adds them in the same order
       xs[(w * 2 + 0) * 64 + lane] = s0;
       xs[(w * 2 + 1) * 64 + lane] = s1;
-      __syncthreads();
+      lds_barrier();
       s0 = xs[0 * 64 + lane];
       s1 = xs[1 * 64 + lane];
 #pragma unroll
@@ -285,8 +344,9 @@ __global__ __launch_bounds__(256) void attn_staged_kernel(const AttnParams p) {
       sv[i2] = s0[i2] * p.scale_log2;
       sv[4 + i2] = s1[i2] * p.scale_log2;
     }
-    if (!full_cur) {
-      const uint32_t sm = slot_mask(vis_cur, g);
+    const uint32_t vis = __builtin_amdgcn_readfirstlane(vmask[i & (kMaskRing - 1)]);
+    if (vis != 0xffffffffu) {
+      const uint32_t sm = slot_mask(vis, g);
 #pragma unroll
       for (int i2 = 0; i2 < 8; ++i2)
         if (!((sm >> i2) & 1u)) sv[i2] = -INFINITY;
@@ -332,16 +392,25 @@ __global__ __launch_bounds__(256) void attn_staged_kernel(const AttnParams p) {
       if ((dt & 3) == 3) __builtin_amdgcn_sched_barrier(0);
     }
 
-    const uint32_t vis_next = commit(vtn, st);
-    const int full_next = st.full;
-    __syncthreads();   // publishes tiles i+1; also orders the next exchange after these reads
-    vis_cur = vis_next;
-    full_cur = full_next;
+    lds_barrier();   // every wave is done with pair B
+    if (i + 2 < nlist) {
+      if (((i + 2) & (kMaskChunk - 1)) == 0) {
+        // next chunk of masks (one batch of loads per 8 entries; drains block i+1)
+        const int n = nlist - (i + 2);
+        build_masks(i + 2, n < kMaskChunk ? n : kMaskChunk, std::integral_constant<int, 1>{});
+        lds_barrier();
+      }
+      stage(i + 2, buf, Masked{});
+      wait_vmcnt<kStageOps>();
+    } else {
+      wait_vmcnt<0>();
+    }
+    lds_barrier();   // publishes block i+1
   };
 
   for (int i = 0; i < nlist; i += 2) {
-    iteration(i, kt0, vt0, kt1, vt1);
-    if (i + 1 < nlist) iteration(i + 1, kt1, vt1, kt0, vt0);
+    iteration(i, std::integral_constant<int, 0>{});
+    if (i + 1 < nlist) iteration(i + 1, std::integral_constant<int, 1>{});
   }
 
   // ---- epilogue: O = O / l, float32 stores (4 consecutive dims per lane)
