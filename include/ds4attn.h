@@ -135,6 +135,10 @@ typedef struct ds4attn_args {
  *            overlapping buffers are rejected.
  *   valid_pad  optional device uint8 [B][valid_pad_stride_b] output: byte r =
  *            in->valid[b][r] (or 1 without in->valid) for r < n_rows, 0 for the tail.
+ *            valid_pad == in->valid with equal strides is in place (only the tail
+ *            is written); other overlap with in->valid is rejected.
+ * When every output is its input and n_rows is a multiple of 32 there is nothing
+ * to write and no kernel is launched.
  * Returns DS4ATTN_OK, DS4ATTN_E_INVAL or DS4ATTN_E_HIP.
  */
 int ds4attn_pad(const ds4attn_region *in, int32_t batch, int32_t head_dim, int32_t dtype,

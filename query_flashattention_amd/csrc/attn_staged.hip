@@ -94,6 +94,7 @@ constexpr int kStageOps = 16;
 // Visibility masks of list entries live in an LDS ring of 128, filled 64 entries
 // at a time, so the half in use is never overwritten.
 constexpr int kMaskRing = 128, kMaskChunk = 64;
+constexpr int kTable = 256 / kRowsPerBlock;   // dense blocks masked at the start, a row per thread
 
 // Tile rows are padded so that rows start on different banks while every operand
 // address stays affine (base + immediate): K rows every 1040 bytes (the 16 rows of
@@ -132,105 +133,19 @@ __global__ __launch_bounds__(256) void attn_staged_kernel(const AttnParams p) {
   __shared__ int cnt[4];
   __shared__ int idx_s[INDEXED ? kIdxCap : 1];
   __shared__ uint32_t vmask[kMaskRing];   // bit r: row r of the entry's block is visible
-
-  // Q^T operand fragments: head h, dims d0 + 32ks + 8g .. +7
-  half8 qf[NKS];
-  const char *qrow = p.q + b * p.q_sb + t * p.q_st + (int64_t)h * p.q_sh;
-#pragma unroll
-  for (int ks = 0; ks < NKS; ++ks) qf[ks] = *(const half8 *)(qrow + 2 * (d0 + 32 * ks + 8 * g));
-  if (INDEXED) {
-    const int32_t *src = p.idx + ((int64_t)b * p.T + t) * p.r1_k;
-    for (int e = tid; e < p.r1_k; e += 256) idx_s[e] = src[e];
-  }
-  const uint8_t *blkrow = p.blk ? p.blk + ((int64_t)b * p.ntiles + t / p.bq) * p.nbd : nullptr;
-  const int ndense = build_block_list<256>(blkrow, p.nbd, blist, cnt);   // ends with a barrier
-  const int nlist = ndense + (INDEXED ? p.nb1 : 0);
-
-  // List entry i: key block j (dense blocks of both regions, then the gathered
-  // blocks of an indexed region) and its map status.
-  auto entry_at = [&](int i, int &j, int &status) {
-    if (i < ndense) {
-      const int e = blist[i];
-      j = e & 0x3fff;
-      status = e >> 14;
-    } else {
-      j = p.nb0 + (i - ndense);
-      status = kPartial;
-    }
-  };
-  // validity arrays of this sequence (size 0 when absent: every load out of range)
-  const rsrc_t rb0 = make_rsrc(p.valid0 + (int64_t)b * p.valid0_sb, p.valid0 ? (uint32_t)p.n0 : 0u);
-  const rsrc_t rb1 = make_rsrc(p.valid1 + (int64_t)b * p.valid1_sb, p.valid1 ? (uint32_t)p.n1 : 0u);
-  // Visibility masks of list entries [c0, c0 + n) into the ring, K rounds of 8
-  // entries per batch of loads: half-wave (w, lane >> 5) takes entry 8k + 2w + (lane >> 5)
-  // of a round, lane & 31 its row.  Every thread must call it (ballots, LDS writes).
-  auto build_masks = [&](int c0, int n, auto rounds) __attribute__((always_inline)) {
-    constexpr int K = decltype(rounds)::value;
-    const int r = lane & 31, half = lane >> 5;
-    for (int e0 = 0; e0 < n; e0 += 8 * K) {
-      int ok[K], full[K], vb0[K], vb1[K];
-      uint32_t off0[K], off1[K];
-#pragma unroll
-      for (int k = 0; k < K; ++k) {
-        const int el = e0 + 8 * k + 2 * w + half;
-        ok[k] = 0;
-        full[k] = 0;
-        off0[k] = off1[k] = kOutOfRange;
-        if (el < n) {
-          int j, status;
-          entry_at(c0 + el, j, status);
-          full[k] = status == kFull;
-          if (j < p.nb0) {
-            const int row = j * kRowsPerBlock + r;
-            bool v = row < p.n0;
-            if (p.window > 0) {
-              const int64_t d = p.qk_delta + t - row;
-              v = v && d >= 0 && d < p.window;
-            }
-            ok[k] = v;
-            if (p.valid0 && row < p.n0) off0[k] = row;
-          } else {
-            const int e = (j - p.nb0) * kRowsPerBlock + r;
-            const int c = INDEXED ? ((e < p.r1_k) ? idx_s[e] : -1) : e;
-            const bool v = c >= 0 && c < p.n1;
-            ok[k] = v;
-            if (p.valid1 && v) off1[k] = c;
-          }
-        }
-      }
-#pragma unroll
-      for (int k = 0; k < K; ++k) {
-        vb0[k] = buf_load_u8(rb0, off0[k]);
-        vb1[k] = buf_load_u8(rb1, off1[k]);
-      }
-#pragma unroll
-      for (int k = 0; k < K; ++k) {
-        const int el = e0 + 8 * k + 2 * w + half;
-        const bool vis = ok[k] && (off0[k] == kOutOfRange || vb0[k] != 0) &&
-                         (off1[k] == kOutOfRange || vb1[k] != 0);
-        const uint64_t bal = __ballot(vis);
-        if (el < n && r == 0)
-          vmask[(c0 + el) & (kMaskRing - 1)] = full[k] ? 0xffffffffu : (uint32_t)(bal >> (32 * half));
-      }
-    }
-  };
+  __shared__ uint32_t dmask[kTable];      // the same for dense blocks 0..kTable-1
 
   // Tile buffer pair 0 or 1, chosen at compile time so the compiler can tell the
   // transfers into one pair from the reads of the other.
   auto ktile = [&](auto buf) -> char * { return decltype(buf)::value ? kt1 : kt0; };
   auto vtile = [&](auto buf) -> char * { return decltype(buf)::value ? vt1 : vt0; };
 
-  // Start the transfers of list entry i (< nlist) into buffer pair `buf`: wave w
+  // Start the transfers of key block j (uniform) into buffer pair `buf`: wave w
   // moves rows 8w..8w+7 of K and of V, one 1 KiB row per instruction, kStageOps
-  // instructions in all.  MASKED: rows the entry's mask hides arrive as zeros (and
-  // are not read from the cache); otherwise every row is transferred (gathered
+  // instructions in all.  Rows whose bit in `vm` is clear arrive as zeros (and are
+  // not read from memory); with vm = all ones every row is transferred (gathered
   // entries that are unused read row 0) and hidden rows are cleared afterwards.
-  auto stage = [&](int i, auto buf, auto masked) __attribute__((always_inline)) {
-    constexpr bool MASKED = decltype(masked)::value;
-    int j, status;
-    entry_at(i, j, status);
-    j = __builtin_amdgcn_readfirstlane(j);   // uniform: scalar branches and descriptors
-    const uint32_t vm = MASKED ? __builtin_amdgcn_readfirstlane(vmask[i & (kMaskRing - 1)]) : 0xffffffffu;
+  auto stage_rows = [&](int j, uint32_t vm, auto buf) __attribute__((always_inline)) {
     const uint32_t kbase = lds_addr(ktile(buf)), vbase = lds_addr(vtile(buf));
     const char *kb, *vb;
     int64_t sr;
@@ -260,6 +175,146 @@ __global__ __launch_bounds__(256) void attn_staged_kernel(const AttnParams p) {
       dma16(shown ? vb + row * sr : kZeroRow, lane16, vbase + rr * kVRow);
     }
   };
+  using Pair0 = std::integral_constant<int, 0>;
+  using Pair1 = std::integral_constant<int, 1>;
+  using Masked = std::integral_constant<bool, true>;
+  using Unmasked = std::integral_constant<bool, false>;
+
+  // The first two list entries are guessed before the map row arrives, and their
+  // transfers start at once: without a map (or for the token's own tile) the list
+  // starts at the first block the window reaches.  A wrong guess is redone below.
+  int spec0 = -1, spec1 = -1;
+  {
+    int jlo = 0;
+    if (p.blk && p.window > 0) {
+      const int64_t lo = p.qk_delta + (int64_t)(t / p.bq) * p.bq - p.window + 1;   // tile's first row
+      jlo = lo <= 0 ? 0 : (int)(lo / kRowsPerBlock < p.nb0 ? lo / kRowsPerBlock : p.nb0);
+    }
+    if (jlo < p.nbd) spec0 = jlo;
+    if (jlo + 1 < p.nbd) spec1 = jlo + 1;
+  }
+  if (spec0 >= 0) stage_rows(spec0, 0xffffffffu, Pair0{});
+  if (spec1 >= 0) stage_rows(spec1, 0xffffffffu, Pair1{});
+
+  // validity arrays of this sequence (size 0 when absent: every load out of range)
+  const rsrc_t rb0 = make_rsrc(p.valid0 + (int64_t)b * p.valid0_sb, p.valid0 ? (uint32_t)p.n0 : 0u);
+  const rsrc_t rb1 = make_rsrc(p.valid1 + (int64_t)b * p.valid1_sb, p.valid1 ? (uint32_t)p.n1 : 0u);
+  // Row r of key block j for this token: `ok` = visible by the arithmetic rules
+  // (inside the region, the window, a used index entry); off0 / off1 = the
+  // validity byte that must also be nonzero (out of range when none applies).
+  // Gathered blocks read the index list, so they are resolved only after it is
+  // in LDS.
+  auto row_rule = [&](int j, int r, int &ok, uint32_t &off0, uint32_t &off1)
+      __attribute__((always_inline)) {
+    off0 = off1 = kOutOfRange;
+    if (j < p.nb0) {
+      const int row = j * kRowsPerBlock + r;
+      bool v = row < p.n0;
+      if (p.window > 0) {
+        const int64_t d = p.qk_delta + t - row;
+        v = v && d >= 0 && d < p.window;
+      }
+      ok = v;
+      if (p.valid0 && row < p.n0) off0 = row;
+    } else {
+      const int e = (j - p.nb0) * kRowsPerBlock + r;
+      const int c = INDEXED ? ((e < p.r1_k) ? idx_s[e] : -1) : e;
+      const bool v = c >= 0 && c < p.n1;
+      ok = v;
+      if (p.valid1 && v) off1 = c;
+    }
+  };
+  // The masks of the first kTable dense blocks (one row per thread) are loaded
+  // together with the map row, so short lists need no second round trip.
+  const int tj = tid >> 5;
+  int tok = 0;
+  uint32_t toff0 = kOutOfRange, toff1 = kOutOfRange;
+  if (tj < p.nbd) row_rule(tj, tid & 31, tok, toff0, toff1);
+  const int tv0 = buf_load_u8(rb0, toff0), tv1 = buf_load_u8(rb1, toff1);
+
+  // Q^T operand fragments: head h, dims d0 + 32ks + 8g .. +7
+  half8 qf[NKS];
+  const char *qrow = p.q + b * p.q_sb + t * p.q_st + (int64_t)h * p.q_sh;
+#pragma unroll
+  for (int ks = 0; ks < NKS; ++ks) qf[ks] = *(const half8 *)(qrow + 2 * (d0 + 32 * ks + 8 * g));
+  if (INDEXED) {
+    const int32_t *src = p.idx + ((int64_t)b * p.T + t) * p.r1_k;
+    for (int e = tid; e < p.r1_k; e += 256) idx_s[e] = src[e];
+  }
+  const uint8_t *blkrow = p.blk ? p.blk + ((int64_t)b * p.ntiles + t / p.bq) * p.nbd : nullptr;
+  const int ndense = build_block_list<256>(blkrow, p.nbd, blist, cnt);   // ends with a barrier
+  const int nlist = ndense + (INDEXED ? p.nb1 : 0);
+  {
+    const bool vis = tok && (toff0 == kOutOfRange || tv0 != 0) && (toff1 == kOutOfRange || tv1 != 0);
+    const uint64_t bal = __ballot(vis);
+    if ((lane & 31) == 0) dmask[tj] = (uint32_t)(bal >> (lane & 32));
+  }
+  lds_barrier();
+
+  // List entry i: key block j (dense blocks of both regions, then the gathered
+  // blocks of an indexed region) and its map status.
+  auto entry_at = [&](int i, int &j, int &status) {
+    if (i < ndense) {
+      const int e = blist[i];
+      j = e & 0x3fff;
+      status = e >> 14;
+    } else {
+      j = p.nb0 + (i - ndense);
+      status = kPartial;
+    }
+  };
+  // Visibility masks of list entries [c0, c0 + n) into the ring, K rounds of 8
+  // entries per batch of loads: half-wave (w, lane >> 5) takes entry 8k + 2w + (lane >> 5)
+  // of a round, lane & 31 its row.  Dense blocks below kTable come from the table.
+  // Every thread must call it (ballots, LDS writes).
+  auto build_masks = [&](int c0, int n, auto rounds) __attribute__((always_inline)) {
+    constexpr int K = decltype(rounds)::value;
+    const int r = lane & 31, half = lane >> 5;
+    for (int e0 = 0; e0 < n; e0 += 8 * K) {
+      int ok[K], full[K], tab[K], vb0[K], vb1[K];
+      uint32_t off0[K], off1[K];
+#pragma unroll
+      for (int k = 0; k < K; ++k) {
+        const int el = e0 + 8 * k + 2 * w + half;
+        ok[k] = 0;
+        full[k] = 0;
+        tab[k] = -1;
+        off0[k] = off1[k] = kOutOfRange;
+        if (el < n) {
+          int j, status;
+          entry_at(c0 + el, j, status);
+          full[k] = status == kFull;
+          if (j < kTable && !(INDEXED && j >= p.nb0)) tab[k] = j;
+          else if (!full[k]) row_rule(j, r, ok[k], off0[k], off1[k]);
+        }
+      }
+#pragma unroll
+      for (int k = 0; k < K; ++k) {
+        vb0[k] = buf_load_u8(rb0, off0[k]);
+        vb1[k] = buf_load_u8(rb1, off1[k]);
+      }
+#pragma unroll
+      for (int k = 0; k < K; ++k) {
+        const int el = e0 + 8 * k + 2 * w + half;
+        const bool vis = ok[k] && (off0[k] == kOutOfRange || vb0[k] != 0) &&
+                         (off1[k] == kOutOfRange || vb1[k] != 0);
+        const uint64_t bal = __ballot(vis);
+        if (el < n && r == 0)
+          vmask[(c0 + el) & (kMaskRing - 1)] =
+              full[k] ? 0xffffffffu : (tab[k] >= 0 ? dmask[tab[k]] : (uint32_t)(bal >> (32 * half)));
+      }
+    }
+  };
+
+  // Start the transfers of list entry i (< nlist) into buffer pair `buf`, with the
+  // entry's mask (MASKED) or unmasked.
+  auto stage = [&](int i, auto buf, auto masked) __attribute__((always_inline)) {
+    constexpr bool MASKED = decltype(masked)::value;
+    int j, status;
+    entry_at(i, j, status);
+    const uint32_t vm = MASKED ? __builtin_amdgcn_readfirstlane(vmask[i & (kMaskRing - 1)]) : 0xffffffffu;
+    stage_rows(__builtin_amdgcn_readfirstlane(j), vm, buf);
+  };
 
   // Clear the V rows of entry i that its mask hides, among this wave's own rows
   // 8w..8w+7 (its own completed transfers wrote them).
@@ -286,16 +341,24 @@ __global__ __launch_bounds__(256) void attn_staged_kernel(const AttnParams p) {
   const int tr_r0 = 4 * g + tr_e;   // slot rows 0-3 of group g; rows 16 + ... for slots 4-7
 
   // Pipeline: blocks i+1 and i+2 are in flight while block i is consumed.
-  //   prologue: stage 0 -> pair 0 and 1 -> pair 1 unmasked, meanwhile compute the
-  //             masks of the first entries; clear the hidden rows of 0 and 1
+  //   prologue: entries 0 -> pair 0 and 1 -> pair 1 unmasked (already in flight
+  //             when guessed right), meanwhile compute the masks of the first
+  //             entries; clear the hidden rows of 0 and 1
   //   block i (pair B): consume from B; barrier (B free); stage i+2 -> B masked;
   //                     wait for this wave's transfers of i+1; barrier (publishes i+1)
-  using Pair0 = std::integral_constant<int, 0>;
-  using Pair1 = std::integral_constant<int, 1>;
-  using Masked = std::integral_constant<bool, true>;
-  using Unmasked = std::integral_constant<bool, false>;
-  if (nlist > 0) stage(0, Pair0{}, Unmasked{});
-  if (nlist > 1) stage(1, Pair1{}, Unmasked{});
+  {
+    int j0 = -1, j1 = -1, st;
+    if (nlist > 0) entry_at(0, j0, st);
+    if (nlist > 1) entry_at(1, j1, st);
+    j0 = __builtin_amdgcn_readfirstlane(j0);
+    j1 = __builtin_amdgcn_readfirstlane(j1);
+    const bool hit0 = nlist < 1 || j0 == spec0, hit1 = nlist < 2 || j1 == spec1;
+    if (!(hit0 && hit1)) {
+      wait_vmcnt<0>();   // the guessed transfers land before their buffers are refilled
+      if (!hit0) stage(0, Pair0{}, Unmasked{});
+      if (!hit1) stage(1, Pair1{}, Unmasked{});
+    }
+  }
   build_masks(0, nlist < kMaskChunk ? nlist : kMaskChunk, std::integral_constant<int, 8>{});
   wait_vmcnt<0>();
   lds_barrier();   // masks visible

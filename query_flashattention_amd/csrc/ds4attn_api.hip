@@ -167,10 +167,22 @@ int ds4attn_pad(const ds4attn_region *in, int32_t batch, int32_t head_dim, int32
   // K and V outputs may be one buffer only when K and V inputs are one buffer too.
   if (ranges_overlap(k_pad, out_len, v_pad, out_len) && !(k_pad == v_pad && in->k == in->v))
     return DS4ATTN_E_INVAL;
+  // Validity in place: the output is the input buffer with the same stride.
+  const bool inplace_valid = valid_pad && in->valid == valid_pad &&
+                             (batch == 1 || in->valid_stride_b == valid_pad_stride_b);
+  if (valid_pad && in->valid && !inplace_valid && n > 0) {
+    const int64_t vout_len = (batch - 1) * valid_pad_stride_b + npad;
+    const int64_t vin_len = (batch - 1) * in->valid_stride_b + n;
+    if (ranges_overlap(valid_pad, vout_len, in->valid, vin_len)) return DS4ATTN_E_INVAL;
+  }
+  // Nothing to write: every output is its input and there is no tail.
+  if (npad == n && (n == 0 || (inplace_k && inplace_v)) && (!valid_pad || inplace_valid))
+    return DS4ATTN_OK;
   hipError_t e = launch_pad(in->k, in->v, in->valid, in->stride_b, in->stride_row,
                             in->valid_stride_b, k_pad, v_pad, valid_pad, out_stride_b,
                             out_stride_row, valid_pad_stride_b, batch, (int)n, (int)npad,
-                            row_bytes, !inplace_k, !inplace_v, (hipStream_t)stream);
+                            row_bytes, !inplace_k, !inplace_v, !inplace_valid,
+                            (hipStream_t)stream);
   return e == hipSuccess ? DS4ATTN_OK : DS4ATTN_E_HIP;
 }
 

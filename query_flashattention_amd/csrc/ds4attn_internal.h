@@ -108,7 +108,7 @@ __device__ __forceinline__ int next_block(const uint8_t *row, int nbd, int nbt, 
 hipError_t launch_pad(const void *k, const void *v, const uint8_t *valid, int64_t in_sb,
                       int64_t in_sr, int64_t valid_sb, void *kp, void *vp, uint8_t *validp,
                       int64_t out_sb, int64_t out_sr, int64_t validp_sb, int B, int n, int npad,
-                      int row_bytes, bool copy_k, bool copy_v, hipStream_t s);
+                      int row_bytes, bool copy_k, bool copy_v, bool copy_valid, hipStream_t s);
 hipError_t launch_blockmap(const AttnParams &p, uint8_t *blk, hipStream_t s);
 hipError_t launch_attn_generic(const AttnParams &p, int elem_bytes, hipStream_t s);
 // Matrix-core kernels (head dim 512, float16): decode splits a token's heads over

@@ -36,14 +36,17 @@ __global__ __launch_bounds__(256) void pad_rows_kernel(
   }
 }
 
+// Validity rows [row_lo, npad) of every sequence (row_lo = n when the output is the
+// input buffer: only the tail is written).
 __global__ __launch_bounds__(256) void pad_valid_kernel(const uint8_t *__restrict__ valid,
                                                         int64_t valid_sb, uint8_t *__restrict__ validp,
-                                                        int64_t validp_sb, int n, int npad,
+                                                        int64_t validp_sb, int n, int row_lo, int npad,
                                                         int64_t total) {
   const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (i >= total) return;
-  const int b = (int)(i / npad);
-  const int row = (int)(i - (int64_t)b * npad);
+  const int per_seq = npad - row_lo;
+  const int b = (int)(i / per_seq);
+  const int row = row_lo + (int)(i - (int64_t)b * per_seq);
   uint8_t x = 0;
   if (row < n) x = valid ? valid[(int64_t)b * valid_sb + row] : (uint8_t)1;
   validp[(int64_t)b * validp_sb + row] = x;
@@ -52,7 +55,7 @@ __global__ __launch_bounds__(256) void pad_valid_kernel(const uint8_t *__restric
 hipError_t launch_pad(const void *k, const void *v, const uint8_t *valid, int64_t in_sb,
                       int64_t in_sr, int64_t valid_sb, void *kp, void *vp, uint8_t *validp,
                       int64_t out_sb, int64_t out_sr, int64_t validp_sb, int B, int n, int npad,
-                      int row_bytes, bool copy_k, bool copy_v, hipStream_t s) {
+                      int row_bytes, bool copy_k, bool copy_v, bool copy_valid, hipStream_t s) {
   const int row_lo = (copy_k || copy_v) ? 0 : n;
   const int nrows_out = npad - row_lo;
   const int cpr = row_bytes / 16;
@@ -66,10 +69,11 @@ hipError_t launch_pad(const void *k, const void *v, const uint8_t *valid, int64_
     if (e != hipSuccess) return e;
   }
   if (validp) {
-    const int64_t tv = (int64_t)B * npad;
+    const int vrow_lo = copy_valid ? 0 : n;
+    const int64_t tv = (int64_t)B * (npad - vrow_lo);
     if (tv > 0) {
       hipLaunchKernelGGL(pad_valid_kernel, dim3((unsigned)((tv + 255) / 256)), dim3(256), 0, s,
-                         valid, valid_sb, validp, validp_sb, n, npad, tv);
+                         valid, valid_sb, validp, validp_sb, n, vrow_lo, npad, tv);
       return hipGetLastError();
     }
   }

@@ -30,17 +30,18 @@ class DeviceRegion:
     k: torch.Tensor              # [B, ceil32(n), D] storage, rows >= n uninitialised until padded
     v: torch.Tensor
     n_rows: int
-    valid_in: Optional[torch.Tensor]   # caller's validity [B, n] (uint8) or None
-    valid: Optional[torch.Tensor]      # padded validity [B, ceil32(n)] written by pad, or None
+    valid: Optional[torch.Tensor]      # [B, ceil32(n)] uint8 storage: the caller's bytes in
+                                       # [0, n), the tail uninitialised until padded; or None
 
     def region(self) -> da.Region:
         return da.region(self.k, self.v, self.n_rows, self.valid)
 
     def pad_in_place(self, stream=None):
-        """Stage 1 in place: zero the tail rows, write the padded validity bytes."""
+        """Stage 1 in place: zero the tail rows and tail validity bytes (nothing is
+        launched when the region already fills whole blocks)."""
         b, _, d = self.k.shape
-        src = da.region(self.k, self.v, self.n_rows, self.valid_in)
-        da.ds4attn_pad(src, b, d, da._dtype_code(self.k.dtype), self.k, self.v, self.valid, stream)
+        da.ds4attn_pad(self.region(), b, d, da._dtype_code(self.k.dtype), self.k, self.v, self.valid,
+                       stream)
 
 
 @dataclass
@@ -70,11 +71,11 @@ def _region_to_device(r, device) -> Optional[DeviceRegion]:
     v = torch.empty((b, cap, d), dtype=r.v.dtype, device=device)
     k[:, :r.n_rows].copy_(r.k[:, :r.n_rows])
     v[:, :r.n_rows].copy_(r.v[:, :r.n_rows])
-    valid_in = valid = None
+    valid = None
     if r.valid is not None:
-        valid_in = r.valid[:, :r.n_rows].contiguous().to(device)
         valid = torch.empty((b, cap), dtype=torch.uint8, device=device)
-    return DeviceRegion(k, v, r.n_rows, valid_in, valid)
+        valid[:, :r.n_rows].copy_(r.valid[:, :r.n_rows])
+    return DeviceRegion(k, v, r.n_rows, valid)
 
 
 def to_device(w, device="cuda") -> DeviceProblem:

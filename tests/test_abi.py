@@ -159,6 +159,25 @@ def test_pad_rejects_bad_arguments():
                            None) == da.E_INVAL
     r0 = da.Region()
     assert lib.ds4attn_pad(ctypes.byref(r0), 1, 64, da.F32, None, None, 0, 0, None, 0, None) == da.OK
+    # validity output overlapping the validity input without being it
+    r.v = r.k
+    r.valid, r.valid_stride_b = FAKE + (1 << 28), 64
+    assert lib.ds4attn_pad(ctypes.byref(r), 2, 64, da.F32, out, out, 32 * 256 * 2, 256,
+                           r.valid + 1, 64, None) == da.E_INVAL
+
+
+def test_pad_with_nothing_to_write_launches_nothing():
+    """A region that already fills whole blocks, padded in place (K, V and validity
+    outputs are their inputs): no kernel is needed, so this succeeds without a GPU."""
+    lib = da.lib()
+    r = da.Region()
+    r.k, r.v = FAKE, FAKE + (1 << 24)
+    r.n_rows, r.stride_row, r.stride_b = 64, 256, 64 * 256
+    r.valid, r.valid_stride_b = FAKE + (1 << 28), 64
+    assert lib.ds4attn_pad(ctypes.byref(r), 3, 64, da.F32, r.k, r.v, r.stride_b, r.stride_row,
+                           r.valid, r.valid_stride_b, None) == da.OK
+    assert lib.ds4attn_pad(ctypes.byref(r), 3, 64, da.F32, r.k, r.v, r.stride_b, r.stride_row,
+                           None, 0, None) == da.OK
 
 
 def test_status_strings_and_tile():

@@ -83,6 +83,7 @@ def test_pad_in_place_zeroes_only_the_tail():
                           valid0_frac=0.5)
     dp = pipeline.to_device(w, DEV)
     dp.r0.k[:, 45:].fill_(float("nan"))
+    dp.r0.valid[:, 45:].fill_(7)          # the validity tail is padded in place too
     dp.r0.pad_in_place()
     torch.cuda.synchronize()
     kp, _, vap = ref.pad_layout(w.r0.k.numpy(), w.r0.v.numpy(), w.r0.valid.numpy(), 45)
