@@ -12,18 +12,12 @@ constexpr int kListCap = 4096;  // non-skipped map blocks a workgroup can list i
 
 // Buffer descriptors: loads through them take a 32-bit byte offset, and an offset
 // at or beyond the descriptor's size returns zero without touching memory.  The
-// kernels issue such out-of-range loads where a load must be counted but no data
-// is needed, so every loop trip issues the same instructions.
+// validity-byte loads use this for rows that have no byte to check.
 typedef __amdgpu_buffer_rsrc_t rsrc_t;
 constexpr uint32_t kOutOfRange = 0x80000000u;   // regions are limited to < 2^31 bytes per sequence
-typedef int int4v __attribute__((ext_vector_type(4)));
 
 __device__ __forceinline__ rsrc_t make_rsrc(const void *base, uint32_t bytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), 0, (int)bytes, 0x00020000);
-}
-__device__ __forceinline__ uint4 buf_load16(rsrc_t r, uint32_t off) {
-  const int4v v = __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
-  return make_uint4((uint32_t)v.x, (uint32_t)v.y, (uint32_t)v.z, (uint32_t)v.w);
 }
 __device__ __forceinline__ int buf_load_u8(rsrc_t r, uint32_t off) {
   return (int)__builtin_amdgcn_raw_buffer_load_b8(r, off, 0, 0);
@@ -33,42 +27,10 @@ __device__ __forceinline__ floatx4 mfma16(const half8 &a, const half8 &b, const 
   return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
 }
 
-// Position (in 16-byte units) of the transposed-V chunk holding key slots 8G..8G+7
-// of head-dim row d.  Rows and slot groups are swizzled so that both the
-// transposing 16-byte stores and the 16-byte operand loads spread over the banks.
-__device__ __forceinline__ int vt_index(int d, int G) {
-  return ((d ^ ((d >> 3) & 1)) << 2) | (G ^ ((d >> 1) & 3));
-}
-
-__device__ __forceinline__ uint32_t word_of(const uint4 &a, int k) {
-  return k == 0 ? a.x : (k == 1 ? a.y : (k == 2 ? a.z : a.w));
-}
-
-// Half i of a in the low half, half i of b in the high half.
-__device__ __forceinline__ uint32_t pair_halves(const uint4 &a, const uint4 &b, int i) {
-  const uint32_t wa = word_of(a, i >> 1), wb = word_of(b, i >> 1);
-  return (i & 1) ? ((wa >> 16) | (wb & 0xffff0000u)) : ((wa & 0xffffu) | (wb << 16));
-}
-
 // Key slot k (0..31) of an MFMA operand group: slots 8G..8G+3 hold block rows
 // 4G..4G+3 and slots 8G+4..8G+7 hold rows 16+4G..16+4G+3, which is exactly the
 // set of rows one lane holds in the 16x16 score accumulators of both row tiles.
 __device__ __forceinline__ int slot_row(int G, int i) { return i < 4 ? 4 * G + i : 16 + 4 * G + (i - 4); }
-
-// Transpose 8 rows x 8 halves (rows ordered as slot_row(G, 0..7)) into 8 chunks,
-// chunk i = the 8 rows' halves at column i, masked rows zeroed.
-__device__ __forceinline__ void transpose8(const uint4 (&in)[8], uint32_t keep_mask, uint4 (&out)[8]) {
-  uint4 vv[8];
-#pragma unroll
-  for (int i = 0; i < 8; ++i) vv[i] = ((keep_mask >> i) & 1u) ? in[i] : make_uint4(0u, 0u, 0u, 0u);
-#pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    out[i].x = pair_halves(vv[0], vv[1], i);
-    out[i].y = pair_halves(vv[2], vv[3], i);
-    out[i].z = pair_halves(vv[4], vv[5], i);
-    out[i].w = pair_halves(vv[6], vv[7], i);
-  }
-}
 
 // Bits 0..7 of the result: which of the rows slot_row(G, 0..7) are set in `vis`.
 __device__ __forceinline__ uint32_t slot_mask(uint32_t vis, int G) {
