@@ -22,8 +22,12 @@ LIB = os.path.join(PKG, "libds4attn.so")
 ARCH = "gfx950"
 
 # Packed fp32 instructions stay off: only scalar/vector fp32 code is emitted.
+# MFMA accumulators are allocated in ordinary VGPRs: the attention kernels keep
+# the output tile across the key loop and rescale it with vector ALU code, which
+# would otherwise shuttle it between AGPRs and VGPRs on every iteration.
 COMMON = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", "-mcode-object-version=5",
           "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+          "-mllvm", "-amdgpu-mfma-vgpr-form=1",
           "-I", INCLUDE, "-I", CSRC, "-Wall", "-Wno-unused-function"]
 
 

@@ -104,10 +104,16 @@ constexpr int kKRow = 1040, kVRow = 1056;
 constexpr int kKTile = 32 * kKRow, kVTile = 32 * kVRow;
 
 template <int MODE, bool INDEXED>
-__global__ __launch_bounds__(256) void attn_staged_kernel(const AttnParams p) {
+__global__ __launch_bounds__(256, MODE == kSplitHeads ? 2 : 1) void attn_staged_kernel(const AttnParams p) {
   constexpr int HG = MODE == kSplitHeads ? 64 : 16;   // heads per workgroup
   constexpr int NKS = MODE == kSplitHeads ? 16 : 4;    // 32-dim k-steps of S per wave
   constexpr int NDT = MODE == kSplitHeads ? 32 : 8;    // 16-dim output tiles per wave
+  // Tile buffers: DIMS double-buffers (block i+1 and i+2 in flight while block i
+  // is consumed); HEADS keeps one block so that two workgroups share a CU and one
+  // computes while the other's transfers are in flight.
+  constexpr int NBUF = MODE == kSplitHeads ? 1 : 2;
+  constexpr int KPD = 2;   // K operand reads in flight (k-steps)
+  constexpr int VPD = 4;   // V operand reads in flight (output tiles)
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave index (uniform)
@@ -126,12 +132,12 @@ __global__ __launch_bounds__(256) void attn_staged_kernel(const AttnParams p) {
   const int d0 = MODE == kSplitHeads ? 0 : 128 * w;
 
   // Two tile buffers as separate LDS objects.
-  __shared__ __attribute__((aligned(16))) char kt0[kKTile], kt1[kKTile];
-  __shared__ __attribute__((aligned(16))) char vt0[kVTile], vt1[kVTile];
+  __shared__ __attribute__((aligned(16))) char kt0[kKTile], kt1[NBUF == 2 ? kKTile : 16];
+  __shared__ __attribute__((aligned(16))) char vt0[kVTile], vt1[NBUF == 2 ? kVTile : 16];
   __shared__ floatx4 xs[MODE == kSplitDims ? 4 * 2 * 64 : 1];   // partial S^T exchange
   __shared__ uint16_t blist[kListCap];
   __shared__ int cnt[4];
-  __shared__ int idx_s[INDEXED ? kIdxCap : 1];
+  __shared__ __attribute__((aligned(16))) int idx_s[INDEXED ? kIdxCap : 4];
   __shared__ uint32_t vmask[kMaskRing];   // bit r: row r of the entry's block is visible
   __shared__ uint32_t dmask[kTable];      // the same for dense blocks 0..kTable-1
 
@@ -161,15 +167,26 @@ __global__ __launch_bounds__(256) void attn_staged_kernel(const AttnParams p) {
       sr = p.kv1_sr;
       base = (j - p.nb0) * kRowsPerBlock;
     }
-    const bool gathered = INDEXED && j >= p.nb0;
+    int rows[8];
+    if (INDEXED && j >= p.nb0) {
+      // the wave's eight list entries in two 16-byte LDS reads (entries past r1_k
+      // hold -1); unused entries read row 0, they are masked
+      const int4 *src = (const int4 *)&idx_s[base + 8 * w];
+      const int4 c0 = src[0], c1 = src[1];
+      const int cs[8] = {c0.x, c0.y, c0.z, c0.w, c1.x, c1.y, c1.z, c1.w};
+#pragma unroll
+      for (int q = 0; q < 8; ++q) {
+        const int c = __builtin_amdgcn_readfirstlane(cs[q]);
+        rows[q] = (c >= 0 && c < p.n1) ? c : 0;
+      }
+    } else {
+#pragma unroll
+      for (int q = 0; q < 8; ++q) rows[q] = base + 8 * w + q;
+    }
 #pragma unroll
     for (int q = 0; q < 8; ++q) {
       const int rr = 8 * w + q;
-      int row = base + rr;
-      if (gathered) {
-        const int c = (row < p.r1_k) ? __builtin_amdgcn_readfirstlane(idx_s[row]) : -1;
-        row = (c >= 0 && c < p.n1) ? c : 0;
-      }
+      const int row = rows[q];
       const bool shown = (vm >> rr) & 1u;
       dma16(shown ? kb + row * sr : kZeroRow, lane16, kbase + rr * kKRow);
       dma16(shown ? vb + row * sr : kZeroRow, lane16, vbase + rr * kVRow);
@@ -191,10 +208,12 @@ __global__ __launch_bounds__(256) void attn_staged_kernel(const AttnParams p) {
       jlo = lo <= 0 ? 0 : (int)(lo / kRowsPerBlock < p.nb0 ? lo / kRowsPerBlock : p.nb0);
     }
     if (jlo < p.nbd) spec0 = jlo;
-    if (jlo + 1 < p.nbd) spec1 = jlo + 1;
+    if (NBUF == 2 && jlo + 1 < p.nbd) spec1 = jlo + 1;
   }
   if (spec0 >= 0) stage_rows(spec0, 0xffffffffu, Pair0{});
-  if (spec1 >= 0) stage_rows(spec1, 0xffffffffu, Pair1{});
+  if constexpr (NBUF == 2) {
+    if (spec1 >= 0) stage_rows(spec1, 0xffffffffu, Pair1{});
+  }
 
   // validity arrays of this sequence (size 0 when absent: every load out of range)
   const rsrc_t rb0 = make_rsrc(p.valid0 + (int64_t)b * p.valid0_sb, p.valid0 ? (uint32_t)p.n0 : 0u);
@@ -238,8 +257,11 @@ __global__ __launch_bounds__(256) void attn_staged_kernel(const AttnParams p) {
 #pragma unroll
   for (int ks = 0; ks < NKS; ++ks) qf[ks] = *(const half8 *)(qrow + 2 * (d0 + 32 * ks + 8 * g));
   if (INDEXED) {
+    // the token's index list; entries up to the end of its last 32-entry block
+    // that lie past r1_k read as unused (-1)
     const int32_t *src = p.idx + ((int64_t)b * p.T + t) * p.r1_k;
-    for (int e = tid; e < p.r1_k; e += 256) idx_s[e] = src[e];
+    const int padded = p.nb1 * kRowsPerBlock;
+    for (int e = tid; e < padded; e += 256) idx_s[e] = e < p.r1_k ? src[e] : -1;
   }
   const uint8_t *blkrow = p.blk ? p.blk + ((int64_t)b * p.ntiles + t / p.bq) * p.nbd : nullptr;
   const int ndense = build_block_list<256>(blkrow, p.nbd, blist, cnt);   // ends with a barrier
@@ -352,40 +374,43 @@ __global__ __launch_bounds__(256) void attn_staged_kernel(const AttnParams p) {
     if (nlist > 1) entry_at(1, j1, st);
     j0 = __builtin_amdgcn_readfirstlane(j0);
     j1 = __builtin_amdgcn_readfirstlane(j1);
-    const bool hit0 = nlist < 1 || j0 == spec0, hit1 = nlist < 2 || j1 == spec1;
+    const bool hit0 = nlist < 1 || j0 == spec0, hit1 = NBUF == 1 || nlist < 2 || j1 == spec1;
     if (!(hit0 && hit1)) {
       wait_vmcnt<0>();   // the guessed transfers land before their buffers are refilled
       if (!hit0) stage(0, Pair0{}, Unmasked{});
-      if (!hit1) stage(1, Pair1{}, Unmasked{});
+      if constexpr (NBUF == 2) {
+        if (!hit1) stage(1, Pair1{}, Unmasked{});
+      }
     }
   }
   build_masks(0, nlist < kMaskChunk ? nlist : kMaskChunk, std::integral_constant<int, 8>{});
   wait_vmcnt<0>();
   lds_barrier();   // masks visible
   clear_masked(0, Pair0{});
-  clear_masked(1, Pair1{});
+  if constexpr (NBUF == 2) clear_masked(1, Pair1{});
   lds_barrier();   // blocks 0 and 1 ready
 
   auto iteration = [&](int i, auto buf) __attribute__((always_inline)) {
     constexpr int B = decltype(buf)::value;
-    // ---- S^T = K Q^T over this wave's head dims (operand loads one step ahead)
+    // ---- S^T = K Q^T over this wave's head dims; operand reads run KPD steps ahead
     floatx4 s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
     const char *ktc = ktile(buf), *vtc = vtile(buf);
     const char *krow0 = ktc + c16 * kKRow + 2 * (d0 + 8 * g), *krow1 = krow0 + 16 * kKRow;
-    uint4 a0 = *(const uint4 *)krow0;
-    uint4 a1 = *(const uint4 *)krow1;
+    uint4 ka[KPD], kb[KPD];
+#pragma unroll
+    for (int u = 0; u < KPD; ++u) {
+      ka[u] = *(const uint4 *)(krow0 + 64 * u);
+      kb[u] = *(const uint4 *)(krow1 + 64 * u);
+    }
 #pragma unroll
     for (int ks = 0; ks < NKS; ++ks) {
-      uint4 n0 = a0, n1 = a1;
-      if (ks + 1 < NKS) {
-        n0 = *(const uint4 *)(krow0 + 64 * (ks + 1));
-        n1 = *(const uint4 *)(krow1 + 64 * (ks + 1));
+      s0 = mfma16(*(const half8 *)&ka[ks % KPD], qf[ks], s0);
+      s1 = mfma16(*(const half8 *)&kb[ks % KPD], qf[ks], s1);
+      if (ks + KPD < NKS) {
+        ka[ks % KPD] = *(const uint4 *)(krow0 + 64 * (ks + KPD));
+        kb[ks % KPD] = *(const uint4 *)(krow1 + 64 * (ks + KPD));
       }
-      s0 = mfma16(*(const half8 *)&a0, qf[ks], s0);
-      s1 = mfma16(*(const half8 *)&a1, qf[ks], s1);
-      a0 = n0;
-      a1 = n1;
-      if ((ks & 3) == 3) __builtin_amdgcn_sched_barrier(0);
+      __builtin_amdgcn_sched_barrier(0);   // keep this order: MFMAs, then the reads they free
     }
     if (MODE == kSplitDims) {
       // partial tiles meet in LDS; every wave adds them in the same order
@@ -437,43 +462,55 @@ __global__ __launch_bounds__(256) void attn_staged_kernel(const AttnParams p) {
 #pragma unroll
       for (int dt = 0; dt < NDT; ++dt) o[dt] *= alpha;
     }
-    // ---- O^T += V^T P^T; V^T operand = two transpose reads (slots 0-3, 4-7)
+    // ---- O^T += V^T P^T; V^T operand = two transpose reads (slots 0-3, 4-7), VPD
+    // output tiles ahead
     const lds_char *vrow0 = (const lds_char *)(__attribute__((address_space(3))) const void *)vtc +
                             tr_r0 * kVRow + 2 * d0 + 8 * tr_a;
     const lds_char *vrow1 = vrow0 + 16 * kVRow;
-#pragma unroll
-    for (int dt = 0; dt < NDT; ++dt) {
+    auto vload = [&](int dt) __attribute__((always_inline)) -> half8 {
       const short4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
           (__attribute__((address_space(3))) short4_t *)(vrow0 + 32 * dt));
       const short4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
           (__attribute__((address_space(3))) short4_t *)(vrow1 + 32 * dt));
       // whole-vector casts: slots 0-3 from the first read, 4-7 from the second
-      const half8 vf = __builtin_shufflevector(__builtin_bit_cast(half4, lo),
-                                               __builtin_bit_cast(half4, hi), 0, 1, 2, 3, 4, 5, 6, 7);
-      o[dt] = mfma16(vf, pf, o[dt]);
-      // keep the scheduler from hoisting every operand read ahead of the MFMAs
-      if ((dt & 3) == 3) __builtin_amdgcn_sched_barrier(0);
+      return __builtin_shufflevector(__builtin_bit_cast(half4, lo), __builtin_bit_cast(half4, hi), 0,
+                                     1, 2, 3, 4, 5, 6, 7);
+    };
+    half8 vq[VPD];
+#pragma unroll
+    for (int u = 0; u < VPD; ++u) vq[u] = vload(u);
+#pragma unroll
+    for (int dt = 0; dt < NDT; ++dt) {
+      o[dt] = mfma16(vq[dt % VPD], pf, o[dt]);
+      if (dt + VPD < NDT) vq[dt % VPD] = vload(dt + VPD);
+      __builtin_amdgcn_sched_barrier(0);   // keep this order: MFMA, then the reads it frees
     }
 
-    lds_barrier();   // every wave is done with pair B
-    if (i + 2 < nlist) {
-      if (((i + 2) & (kMaskChunk - 1)) == 0) {
-        // next chunk of masks (one batch of loads per 8 entries; drains block i+1)
-        const int n = nlist - (i + 2);
-        build_masks(i + 2, n < kMaskChunk ? n : kMaskChunk, std::integral_constant<int, 1>{});
+    lds_barrier();   // every wave is done with buffer B
+    const int nx = i + NBUF;   // the entry buffer B takes next
+    if (nx < nlist) {
+      if ((nx & (kMaskChunk - 1)) == 0) {
+        // next chunk of masks (one batch of loads per 8 entries; drains the transfers)
+        const int n = nlist - nx;
+        build_masks(nx, n < kMaskChunk ? n : kMaskChunk, std::integral_constant<int, 1>{});
         lds_barrier();
       }
-      stage(i + 2, buf, Masked{});
-      wait_vmcnt<kStageOps>();
+      stage(nx, buf, Masked{});
+      if constexpr (NBUF == 2) wait_vmcnt<kStageOps>();   // block i+1 (staged earlier) landed
+      else wait_vmcnt<0>();
     } else {
       wait_vmcnt<0>();
     }
     lds_barrier();   // publishes block i+1
   };
 
-  for (int i = 0; i < nlist; i += 2) {
-    iteration(i, std::integral_constant<int, 0>{});
-    if (i + 1 < nlist) iteration(i + 1, std::integral_constant<int, 1>{});
+  if constexpr (NBUF == 2) {
+    for (int i = 0; i < nlist; i += 2) {
+      iteration(i, std::integral_constant<int, 0>{});
+      if (i + 1 < nlist) iteration(i + 1, std::integral_constant<int, 1>{});
+    }
+  } else {
+    for (int i = 0; i < nlist; ++i) iteration(i, std::integral_constant<int, 0>{});
   }
 
   // ---- epilogue: O = O / l, float32 stores (4 consecutive dims per lane)

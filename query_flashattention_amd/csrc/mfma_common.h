@@ -8,7 +8,7 @@ namespace ds4attn {
 typedef _Float16 half8 __attribute__((ext_vector_type(8)));
 typedef float floatx4 __attribute__((ext_vector_type(4)));
 
-constexpr int kListCap = 4096;  // non-skipped map blocks a workgroup can list in LDS (131072 rows)
+constexpr int kListCap = 2048;  // non-skipped map blocks a workgroup can list in LDS (65536 rows)
 
 // Buffer descriptors: loads through them take a 32-bit byte offset, and an offset
 // at or beyond the descriptor's size returns zero without touching memory.  The
