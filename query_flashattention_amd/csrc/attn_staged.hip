@@ -33,75 +33,13 @@
 //         16 heads; the four partial score tiles meet in LDS and every wave sums
 //         them in the same order; 4 workgroups per 64-head token fill the chip
 //         for small decode batches.
-#include "mfma_common.h"
+#include "staging.h"
 
 #include <type_traits>
 
 namespace ds4attn {
 
-typedef short short4_t __attribute__((ext_vector_type(4)));
-typedef _Float16 half4 __attribute__((ext_vector_type(4)));
-typedef __attribute__((address_space(3))) char lds_char;
-
 enum : int { kSplitHeads = 0, kSplitDims = 1 };
-
-// One row: 16 bytes per lane from `row` + 16 * lane (`row` uniform) into LDS at
-// `lds` + 16 * lane (`lds` uniform).  The row address travels in scalar registers
-// and the lane offset is one shared vector register.  Issued through asm, so the
-// compiler's hazard tracking does not see it: the tracking cannot always tell the
-// tile buffers from the other LDS arrays and would drain every transfer in flight
-// before unrelated LDS reads.  Completion is awaited explicitly (wait_vmcnt)
-// before the barrier that publishes a tile, and a buffer is refilled only after
-// the barrier that ends its reads.  m0 is written only here in these kernels.
-__device__ __forceinline__ void dma16(const char *row, uint32_t lane16, uint32_t lds) {
-  // (the builtin returns int: widen each half as unsigned, never sign-extended)
-  const uint64_t r = (uint64_t)row;
-  const uint32_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)r);
-  const uint32_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)(r >> 32));
-  const uint64_t ru = ((uint64_t)hi << 32) | (uint64_t)lo;
-  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1"
-               :: "v"(lane16), "s"(ru), "s"(__builtin_amdgcn_readfirstlane(lds)) : "memory");
-}
-
-// LDS byte address of a shared-memory pointer.
-__device__ __forceinline__ uint32_t lds_addr(const void *p) {
-  return (uint32_t)(size_t)(__attribute__((address_space(3))) const void *)p;
-}
-
-// Source of the rows a mask hides: they arrive in LDS as zeros (from L2).
-static __device__ __attribute__((aligned(16))) const char kZeroRow[1024] = {};
-
-// Workgroup barrier for LDS data only: this wave's LDS operations complete, then
-// s_barrier.  (The generic barrier also waits for every outstanding global load,
-// which would drain the tile transfers kept in flight across it.)
-__device__ __forceinline__ void lds_barrier() {
-  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
-}
-
-// s_waitcnt vmcnt(N) (other counters untouched), issued through the builtin so
-// that the compiler's own wait insertion knows what it has already waited for.
-template <int N>
-__device__ __forceinline__ void wait_vmcnt() {
-  static_assert(N >= 0 && N < 64, "vmcnt is a 6-bit counter");
-  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
-  asm volatile("" ::: "memory");
-}
-
-// A stage is exactly 16 vector-memory instructions per wave (8 K rows, 8 V rows);
-// waiting with vmcnt(16) right after issuing one completes every older stage.
-constexpr int kStageOps = 16;
-
-// Visibility masks of list entries live in an LDS ring of 128, filled 64 entries
-// at a time, so the half in use is never overwritten.
-constexpr int kMaskRing = 128, kMaskChunk = 64;
-constexpr int kTable = 256 / kRowsPerBlock;   // dense blocks masked at the start, a row per thread
-
-// Tile rows are padded so that rows start on different banks while every operand
-// address stays affine (base + immediate): K rows every 1040 bytes (the 16 rows of
-// an A operand spread over 16-byte bank groups), V rows every 1056 bytes (the 4
-// rows x 32 bytes of a transpose read spread over 8-byte bank groups).
-constexpr int kKRow = 1040, kVRow = 1056;
-constexpr int kKTile = 32 * kKRow, kVTile = 32 * kVRow;
 
 template <int MODE, bool INDEXED>
 __global__ __launch_bounds__(256, MODE == kSplitHeads ? 2 : 1) void attn_staged_kernel(const AttnParams p) {
