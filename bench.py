@@ -44,6 +44,8 @@ DESCRIPTIONS = {
     "decode_r128": "decode, ratio-128 layer at 32K context: 1 sequence x 1 token x 64 q-heads x d512, "
                    "128 ring rows + 256 compressed slots (last block partly valid)",
     "decode_r128_b64": "decode, ratio-128 layer at 32K context, 64 sequences",
+    "decode_r4": "decode, ratio-4 indexed layer at 8K context: 64 sequences x 1 token x 64 q-heads x d512, "
+                 "128 ring rows + top-512 of 2048 compressed rows per sequence",
     "prefill_swa": "prefill chunk, raw layer: 2048 tokens x 64 q-heads x d512, causal + 128 window",
     "prefill_r4": "prefill chunk, ratio-4 layer at position 30720: 2048 tokens x 64 q-heads x d512, "
                   "2175 raw rows (causal + 128 window) + top-512 of 7680 compressed rows per token",
@@ -383,8 +385,8 @@ def main():
 
     if not args.no_extra and name == "decode_swa":
         extra = {}
-        for other in ("prefill_swa", "prefill_r4", "decode_r128", "decode_r128_b64"):
-            sets = 2 if other.startswith("prefill") else (20 if other.endswith("b64") else 64)
+        for other in ("prefill_swa", "prefill_r4", "decode_r128", "decode_r128_b64", "decode_r4"):
+            sets = 2 if other.startswith("prefill") else (64 if other == "decode_r128" else 20)
             steps = 20 if other.startswith("prefill") else 200
             r, s, k = run_workload(other, steps, 3, sets, 20 if other.startswith("prefill") else 100)
             cc = counts(r.w)

@@ -149,6 +149,26 @@ def decode_ratio128(seed: int = 103, batch: int = 1, context: int = 32768) -> Wo
                     r1=r1, notes={"n_comp": n_comp.tolist()})
 
 
+def decode_ratio4(seed: int = 106, batch: int = 64, context: int = 8192,
+                  topk: int = TOPK) -> Workload:
+    """Decode on a ratio-4 indexed layer: per sequence a full 128-row raw ring plus
+    context/4 compressed rows pooling positions [0, context), of which the token
+    attends a sorted, unique, uniform top-``topk`` index list."""
+    g = torch.Generator().manual_seed(seed)
+    n1 = context // 4
+    q = _normal(g, (batch, 1, N_HEAD, HEAD_DIM), torch.float16)
+    k0 = _normal(g, (batch, WINDOW, HEAD_DIM), torch.float16)
+    v0 = _normal(g, (batch, WINDOW, HEAD_DIM), torch.float16)
+    k1 = _normal(g, (batch, n1, HEAD_DIM), torch.float16)
+    v1 = _normal(g, (batch, n1, HEAD_DIM), torch.float16)
+    off = torch.randint(0, WINDOW, (batch,), generator=g)
+    keys = torch.rand(batch, n1, generator=g)
+    idx = keys.argsort(dim=1)[:, :topk].sort(dim=1).values.to(torch.int32)
+    r0 = RegionInputs(_ring_physical(k0, off), _ring_physical(v0, off), WINDOW, ring_offset=off)
+    return Workload(f"decode_ratio4_b{batch}_n128+{topk}of{n1}", seed, q, scale_for(HEAD_DIM), r0,
+                    r1=RegionInputs(k1, v1, n1), r1_index=idx.view(batch, 1, topk))
+
+
 def prefill_raw_swa(seed: int = 104, tokens: int = PREFILL_CHUNK) -> Workload:
     """Prefill chunk on a raw layer: causal + 128-token sliding window over the chunk."""
     g = torch.Generator().manual_seed(seed)
@@ -185,12 +205,14 @@ def prefill_ratio4(seed: int = 105, tokens: int = PREFILL_CHUNK, start: int = 30
 
 
 def named(name: str) -> Workload:
-    """The five reference workloads plus the batched ratio-128 decode variant."""
+    """The five reference workloads, the batched ratio-128 decode variant and the
+    ratio-4 indexed decode."""
     table = {
         "tiny": tiny_mqa,
         "decode_swa": decode_raw_swa,
         "decode_r128": decode_ratio128,
         "decode_r128_b64": lambda: decode_ratio128(batch=64),
+        "decode_r4": decode_ratio4,
         "prefill_swa": prefill_raw_swa,
         "prefill_r4": prefill_ratio4,
     }

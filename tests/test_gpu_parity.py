@@ -105,7 +105,8 @@ def _map_check(w, bq):
 
 
 @pytest.mark.parametrize("name,bq", [("tiny", 1), ("decode_swa", 1), ("decode_r128", 1),
-                                     ("decode_r128_b64", 1), ("prefill_swa", 1), ("prefill_swa", 16),
+                                     ("decode_r128_b64", 1), ("decode_r4", 1), ("prefill_swa", 1),
+                                     ("prefill_swa", 16),
                                      ("prefill_r4", 1), ("prefill_r4", 16), ("prefill_r4", 2048)])
 def test_blockmap_bits_on_workloads(name, bq):
     got = _map_check(wl.named(name), bq)
@@ -156,6 +157,17 @@ def test_attention_workload_full(name, entry, bq):
     out = _run(w, entry, bq).double().numpy()
     want = ref.attention(ref.from_workload(w))
     _compare(out, want, f"{name}/{entry}")
+
+
+def test_attention_decode_ratio4_sampled():
+    """The indexed ratio-4 decode batch at full size (64 sequences, 128 ring rows +
+    top-512 of 2048 compressed rows each); the oracle computes a sample of the
+    sequences."""
+    w = wl.named("decode_r4")
+    out = _run(w, "decode", 1).double().numpy()
+    seqs = [0, 1, 17, 31, 32, 50, 62, 63]
+    want = ref.attention(ref.from_workload(w), tokens=[(b, 0) for b in seqs])
+    _compare(out[seqs, 0], want, "decode_r4 sampled")
 
 
 def test_attention_prefill_ratio4_sampled():
