@@ -380,8 +380,8 @@ __global__ __launch_bounds__(256, MODE == kSplitHeads ? 2 : 1) void attn_staged_
     float mx = sv[0];
 #pragma unroll
     for (int i2 = 1; i2 < 8; ++i2) mx = fmaxf(mx, sv[i2]);
-    mx = fmaxf(mx, __shfl_xor(mx, 16));
-    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    mx = xor_max(mx, 16);
+    mx = xor_max(mx, 32);
     const bool grow = mx > m + kRescaleSlack;
     const float mref = grow ? mx : m;
     const float msafe = (mref == -INFINITY) ? 0.f : mref;
@@ -453,8 +453,8 @@ __global__ __launch_bounds__(256, MODE == kSplitHeads ? 2 : 1) void attn_staged_
 
   // ---- epilogue: O = O / l, float32 stores (4 consecutive dims per lane)
   float lt = l;
-  lt += __shfl_xor(lt, 16);
-  lt += __shfl_xor(lt, 32);
+  lt = xor_sum(lt, 16);
+  lt = xor_sum(lt, 32);
   const float inv = lt > 0.f ? 1.f / lt : 0.f;
   float *ob = (float *)(p.o + b * p.o_sb + t * p.o_st + (int64_t)h * p.o_sh) + d0 + 4 * g;
 #pragma unroll

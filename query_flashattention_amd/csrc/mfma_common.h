@@ -37,6 +37,23 @@ __device__ __forceinline__ uint32_t slot_mask(uint32_t vis, int G) {
   return ((vis >> (4 * G)) & 0xfu) | (((vis >> (16 + 4 * G)) & 0xfu) << 4);
 }
 
+// Butterfly steps across the four 16-lane groups without the LDS crossbar:
+// v_permlane16_swap / v_permlane32_swap with both operands equal hand each lane
+// the pair {x[l], x[l ^ 16]} (resp. {x[l], x[l ^ 32]}) in some order, so max and
+// sum of the pair are the values of a xor-16 (xor-32) exchange on every lane.
+__device__ __forceinline__ float xor_max(float x, int d) {
+  const uint32_t u = __builtin_bit_cast(uint32_t, x);
+  const auto r = d == 16 ? __builtin_amdgcn_permlane16_swap(u, u, false, false)
+                         : __builtin_amdgcn_permlane32_swap(u, u, false, false);
+  return fmaxf(__builtin_bit_cast(float, (uint32_t)r[0]), __builtin_bit_cast(float, (uint32_t)r[1]));
+}
+__device__ __forceinline__ float xor_sum(float x, int d) {
+  const uint32_t u = __builtin_bit_cast(uint32_t, x);
+  const auto r = d == 16 ? __builtin_amdgcn_permlane16_swap(u, u, false, false)
+                         : __builtin_amdgcn_permlane32_swap(u, u, false, false);
+  return __builtin_bit_cast(float, (uint32_t)r[0]) + __builtin_bit_cast(float, (uint32_t)r[1]);
+}
+
 // The online softmax keeps a reference max m per row and rescales the output only
 // when a block's max exceeds it by more than this many binary orders of magnitude.
 // Below that, P = 2^(s - m) <= 2^8 is exact enough in float16 (11-bit mantissa at
