@@ -292,6 +292,41 @@ def traffic_from_profiles(kernel_src):
         return None
 
 
+def topk_timing(rows, n, k, n_sets=4, reps=25):
+    """Mean duration of one ds4attn_topk launch over [rows, n] float32 scores (HIP
+    events around graph replays, input sets rotated), with its algorithmic bytes
+    (scores read once, indices written once)."""
+    import torch
+    from query_flashattention_amd import ds4attn as da, workloads
+
+    sets = [workloads.indexer_scores(300 + i, rows, n).to("cuda") for i in range(n_sets)]
+    outs = [torch.empty((rows, k), dtype=torch.int32, device="cuda") for _ in range(n_sets)]
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        for s, o in zip(sets, outs):
+            da.ds4attn_topk(s, k, o)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for s, o in zip(sets, outs):
+            da.ds4attn_topk(s, k, o)
+    g.replay()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        g.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / (reps * n_sets)
+    nbytes = 4.0 * rows * n + 4.0 * rows * k
+    return {"rows": rows, "n": n, "k": k, "kernel_us_mean": round(ms * 1e3, 2),
+            "algorithmic_bytes": nbytes, "gbs_kernel": round(nbytes / (ms * 1e-3) / 1e9, 1),
+            "rows_per_s": round(rows / (ms * 1e-3), 1)}
+
+
 def run_workload(name, steps, warmup, n_sets, launches):
     r = Runner(name, n_sets)
     for k in range(warmup):
@@ -406,6 +441,10 @@ def main():
             extra[other] = entry
             del r
             torch.cuda.empty_cache()
+        # top-k index selection feeding the ratio-4 layers: the prefill chunk's 2048
+        # tokens over 7680 compressed rows, and the decode batch's 64 over 2048
+        extra["topk_prefill_r4"] = topk_timing(2048, 7680, 512)
+        extra["topk_decode_r4"] = topk_timing(64, 2048, 512)
         out["extra"] = extra
 
     if args.cpu_seconds > 0:

@@ -195,6 +195,30 @@ int ds4attn_prefill(const ds4attn_args *a, const void *q, const uint8_t *blk, in
  * bq >= 1 is accepted). */
 int32_t ds4attn_prefill_bq(void);
 
+/*
+ * ds4attn_topk -- top-k index selection from given scores: the index list of a
+ * ratio-4 layer ([P-DS4] "Architecture Deep Dive", Layer Compression: each token
+ * attends the top-512 compressed rows its indexer selects; the scoring itself is
+ * learned and not computed here).
+ *
+ *   scores  device float32, row r (0 <= r < rows) at scores + r*score_stride bytes,
+ *           n scores per row
+ *   idx     device int32 output, row r at idx + r*idx_stride bytes, k entries: the
+ *           indices of the min(k, n) largest scores of the row in ascending order,
+ *           then -1 (an unused entry) up to k.  Scores compare by the IEEE total
+ *           order of their bit patterns (-0 < +0; a NaN with the sign bit clear
+ *           ranks above +inf, one with it set below -inf); equal scores go to the
+ *           lower index, so the result is unique.
+ *   0 <= rows <= 2^24, n >= 0, 1 <= k <= 2048; pointers and strides are multiples of 4
+ *   bytes; score_stride >= 4*n and idx_stride >= 4*k when rows > 1; idx must not
+ *   overlap the scores.  The output is a valid ds4attn_args.r1_index with r1_k = k.
+ *   rows == 0 launches nothing.
+ * Returns DS4ATTN_OK, DS4ATTN_E_INVAL, DS4ATTN_E_UNSUPPORTED (rows > 2^24) or
+ * DS4ATTN_E_HIP.
+ */
+int ds4attn_topk(const float *scores, int64_t rows, int32_t n, int64_t score_stride, int32_t k,
+                 int32_t *idx, int64_t idx_stride, void *stream);
+
 /* A static, NUL-terminated description of a status code. */
 const char *ds4attn_status_string(int status);
 

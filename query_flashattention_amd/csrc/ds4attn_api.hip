@@ -224,6 +224,23 @@ int ds4attn_prefill(const ds4attn_args *a, const void *q, const uint8_t *blk, in
 
 int32_t ds4attn_prefill_bq(void) { return 16; }
 
+int ds4attn_topk(const float *scores, int64_t rows, int32_t n, int64_t score_stride, int32_t k,
+                 int32_t *idx, int64_t idx_stride, void *stream) {
+  if (rows < 0 || n < 0 || k < 1 || k > kMaxIndexK) return DS4ATTN_E_INVAL;
+  if (rows > kMaxTopkRows) return DS4ATTN_E_UNSUPPORTED;
+  if (rows == 0) return DS4ATTN_OK;
+  auto aligned4 = [](const void *ptr) { return ((uintptr_t)ptr & 3u) == 0; };
+  if (!idx || !aligned4(idx) || (idx_stride & 3) || idx_stride < 0) return DS4ATTN_E_INVAL;
+  if (n > 0 && (!scores || !aligned4(scores))) return DS4ATTN_E_INVAL;
+  if ((score_stride & 3) || score_stride < 0) return DS4ATTN_E_INVAL;
+  if (rows > 1 && (idx_stride < 4LL * k || score_stride < 4LL * n)) return DS4ATTN_E_INVAL;
+  const int64_t out_len = (rows - 1) * idx_stride + 4LL * k;
+  const int64_t in_len = (rows - 1) * score_stride + 4LL * n;
+  if (n > 0 && ranges_overlap(idx, out_len, scores, in_len)) return DS4ATTN_E_INVAL;
+  const hipError_t e = launch_topk(scores, rows, n, score_stride, k, idx, idx_stride, (hipStream_t)stream);
+  return e == hipSuccess ? DS4ATTN_OK : DS4ATTN_E_HIP;
+}
+
 const char *ds4attn_status_string(int status) {
   switch (status) {
     case DS4ATTN_OK: return "ok";

@@ -115,5 +115,9 @@ hipError_t launch_attn_generic(const AttnParams &p, int elem_bytes, hipStream_t 
 // workgroups of 16; prefill keeps 64 heads of a token in one workgroup.
 hipError_t launch_attn_decode(const AttnParams &p, hipStream_t s);
 hipError_t launch_attn_prefill(const AttnParams &p, hipStream_t s);
+// Top-k index selection, one workgroup per row of scores.
+constexpr int64_t kMaxTopkRows = 1LL << 24;   // rows of one top-k launch (one 256-lane workgroup each)
+hipError_t launch_topk(const float *scores, int64_t rows, int n, int64_t s_stride, int k, int32_t *idx,
+                       int64_t o_stride, hipStream_t s);
 
 }  // namespace ds4attn

@@ -45,7 +45,7 @@ class Args(ctypes.Structure):
 
 
 EXPORTS = ("ds4attn_pad", "ds4attn_blockmap", "ds4attn_blockmap_dims", "ds4attn_decode",
-           "ds4attn_prefill", "ds4attn_prefill_bq", "ds4attn_status_string")
+           "ds4attn_prefill", "ds4attn_prefill_bq", "ds4attn_topk", "ds4attn_status_string")
 
 _lib = None
 
@@ -65,8 +65,9 @@ def lib() -> ctypes.CDLL:
         for name in ("ds4attn_decode", "ds4attn_prefill"):
             getattr(h, name).argtypes = [ctypes.POINTER(Args), _c_void_p, _c_void_p, _i32,
                                          _c_void_p, _c_void_p]
+        h.ds4attn_topk.argtypes = [_c_void_p, _i64, _i32, _i64, _i32, _c_void_p, _i64, _c_void_p]
         for name in ("ds4attn_pad", "ds4attn_blockmap", "ds4attn_blockmap_dims", "ds4attn_decode",
-                     "ds4attn_prefill", "ds4attn_prefill_bq"):
+                     "ds4attn_prefill", "ds4attn_prefill_bq", "ds4attn_topk"):
             getattr(h, name).restype = _i32
         h.ds4attn_status_string.argtypes = [_i32]
         h.ds4attn_status_string.restype = ctypes.c_char_p
@@ -175,6 +176,24 @@ def ds4attn_prefill(a: Args, q: torch.Tensor, blk: Optional[torch.Tensor], bq: i
                     stream=None) -> None:
     _check(lib().ds4attn_prefill(ctypes.byref(a), q.data_ptr(), _ptr(blk), bq, o.data_ptr(),
                                  _stream(stream)), "ds4attn_prefill")
+
+
+def ds4attn_topk(scores: torch.Tensor, k: int, idx: torch.Tensor, stream=None) -> None:
+    """Top-k index selection: scores float32 [rows, n] (rows contiguous), idx int32 [rows, k]."""
+    if scores.dtype != torch.float32 or idx.dtype != torch.int32:
+        raise TypeError("ds4attn_topk takes float32 scores and an int32 output")
+    rows, n = scores.shape
+    if (n > 1 and scores.stride(1) != 1) or (k > 1 and idx.stride(1) != 1) or idx.shape != (rows, k):
+        raise ValueError("ds4attn_topk needs rows with unit element stride and idx of shape [rows, k]")
+    _check(lib().ds4attn_topk(scores.data_ptr() if n else None, rows, n, scores.stride(0) * 4, k,
+                              idx.data_ptr(), idx.stride(0) * 4, _stream(stream)), "ds4attn_topk")
+
+
+def topk(scores: torch.Tensor, k: int, stream=None) -> torch.Tensor:
+    """Allocate the output and run ``ds4attn_topk``."""
+    idx = torch.empty((scores.shape[0], k), dtype=torch.int32, device=scores.device)
+    ds4attn_topk(scores, k, idx, stream)
+    return idx
 
 
 def ds4attn_prefill_bq() -> int:

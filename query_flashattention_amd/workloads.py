@@ -262,3 +262,27 @@ def random_problem(seed: int, batch: int, tokens: int, heads: int, head_dim: int
     return Workload(f"random_s{seed}", seed, q, scale_for(head_dim),
                     RegionInputs(k0, v0, n0, valid=valid0), window=window, q_pos0=q_pos0,
                     k_pos0=k_pos0, r1=r1, r1_index=idx)
+
+
+def indexer_scores(seed: int, rows: int, n: int, kind: str = "normal") -> torch.Tensor:
+    """float32 [rows, n] scores for the top-k selection step (the indexer that
+    produces them is learned and not on the pages, so the values are drawn).
+
+    ``normal``: standard normal.  ``coarse``: multiples of 1/4 in [-2, 2], so that
+    most selections end inside a run of equal scores.  ``special``: normal with
+    about one entry in eight replaced by +0, -0, +inf, -inf or a NaN of either sign.
+    """
+    g = torch.Generator().manual_seed(seed)
+    if kind == "normal":
+        return torch.randn(rows, n, generator=g)
+    if kind == "coarse":
+        return torch.randint(-8, 9, (rows, n), generator=g).float() * 0.25
+    if kind == "special":
+        s = torch.randn(rows, n, generator=g)
+        pick = torch.randint(0, 8, (rows, n), generator=g) == 0
+        which = torch.randint(0, 6, (rows, n), generator=g)
+        bits = torch.tensor([0x00000000, 0x80000000 - (1 << 32), 0x7F800000, 0xFF800000 - (1 << 32),
+                             0x7FC00001, 0xFFC00001 - (1 << 32)], dtype=torch.int32)
+        special = bits[which].view(torch.float32)
+        return torch.where(pick, special, s)
+    raise ValueError(f"unknown score kind {kind!r}")

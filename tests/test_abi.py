@@ -180,6 +180,30 @@ def test_pad_with_nothing_to_write_launches_nothing():
                            None, 0, None) == da.OK
 
 
+def test_topk_rejects_bad_arguments():
+    lib = da.lib()
+    out = FAKE + (1 << 30)
+    # k outside 1..2048, negative sizes
+    assert lib.ds4attn_topk(FAKE, 4, 100, 400, 0, out, 4, None) == da.E_INVAL
+    assert lib.ds4attn_topk(FAKE, 4, 100, 400, 2049, out, 2049 * 4, None) == da.E_INVAL
+    assert lib.ds4attn_topk(FAKE, -1, 100, 400, 8, out, 32, None) == da.E_INVAL
+    assert lib.ds4attn_topk(FAKE, 4, -1, 400, 8, out, 32, None) == da.E_INVAL
+    # misaligned pointers or strides, strides shorter than a row
+    assert lib.ds4attn_topk(FAKE + 2, 4, 100, 400, 8, out, 32, None) == da.E_INVAL
+    assert lib.ds4attn_topk(FAKE, 4, 100, 400, 8, out + 1, 32, None) == da.E_INVAL
+    assert lib.ds4attn_topk(FAKE, 4, 100, 402, 8, out, 32, None) == da.E_INVAL
+    assert lib.ds4attn_topk(FAKE, 4, 100, 396, 8, out, 32, None) == da.E_INVAL
+    assert lib.ds4attn_topk(FAKE, 4, 100, 400, 8, out, 28, None) == da.E_INVAL
+    # null buffers; output overlapping the scores
+    assert lib.ds4attn_topk(None, 4, 100, 400, 8, out, 32, None) == da.E_INVAL
+    assert lib.ds4attn_topk(FAKE, 4, 100, 400, 8, None, 32, None) == da.E_INVAL
+    assert lib.ds4attn_topk(FAKE, 4, 100, 400, 8, FAKE + 1200, 32, None) == da.E_INVAL
+    # more rows than one launch takes
+    assert lib.ds4attn_topk(FAKE, (1 << 24) + 1, 100, 400, 8, out, 32, None) == da.E_UNSUPPORTED
+    # no rows: nothing to launch
+    assert lib.ds4attn_topk(FAKE, 0, 100, 400, 8, out, 32, None) == da.OK
+
+
 def test_status_strings_and_tile():
     assert da.status_string(da.OK) == "ok"
     assert "invalid" in da.status_string(da.E_INVAL)
