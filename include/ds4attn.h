@@ -209,11 +209,11 @@ int32_t ds4attn_prefill_bq(void);
  *           order of their bit patterns (-0 < +0; a NaN with the sign bit clear
  *           ranks above +inf, one with it set below -inf); equal scores go to the
  *           lower index, so the result is unique.
- *   0 <= rows <= 2^24, n >= 0, 1 <= k <= 2048; pointers and strides are multiples of 4
+ *   0 <= rows <= 2^24, 0 <= n < 2^30, 1 <= k <= 2048; pointers and strides are multiples of 4
  *   bytes; score_stride >= 4*n and idx_stride >= 4*k when rows > 1; idx must not
  *   overlap the scores.  The output is a valid ds4attn_args.r1_index with r1_k = k.
  *   rows == 0 launches nothing.
- * Returns DS4ATTN_OK, DS4ATTN_E_INVAL, DS4ATTN_E_UNSUPPORTED (rows > 2^24) or
+ * Returns DS4ATTN_OK, DS4ATTN_E_INVAL, DS4ATTN_E_UNSUPPORTED (rows > 2^24 or n >= 2^30) or
  * DS4ATTN_E_HIP.
  */
 int ds4attn_topk(const float *scores, int64_t rows, int32_t n, int64_t score_stride, int32_t k,

@@ -226,8 +226,9 @@ int32_t ds4attn_prefill_bq(void) { return 16; }
 
 int ds4attn_topk(const float *scores, int64_t rows, int32_t n, int64_t score_stride, int32_t k,
                  int32_t *idx, int64_t idx_stride, void *stream) {
-  if (rows < 0 || n < 0 || k < 1 || k > kMaxIndexK) return DS4ATTN_E_INVAL;
-  if (rows > kMaxTopkRows) return DS4ATTN_E_UNSUPPORTED;
+  static_assert(kMaxTopkK <= kMaxIndexK, "a selection must be a valid index list");
+  if (rows < 0 || n < 0 || k < 1 || k > kMaxTopkK) return DS4ATTN_E_INVAL;
+  if (rows > kMaxTopkRows || n > kMaxTopkN) return DS4ATTN_E_UNSUPPORTED;
   if (rows == 0) return DS4ATTN_OK;
   auto aligned4 = [](const void *ptr) { return ((uintptr_t)ptr & 3u) == 0; };
   if (!idx || !aligned4(idx) || (idx_stride & 3) || idx_stride < 0) return DS4ATTN_E_INVAL;

@@ -116,7 +116,9 @@ hipError_t launch_attn_generic(const AttnParams &p, int elem_bytes, hipStream_t 
 hipError_t launch_attn_decode(const AttnParams &p, hipStream_t s);
 hipError_t launch_attn_prefill(const AttnParams &p, hipStream_t s);
 // Top-k index selection, one workgroup per row of scores.
-constexpr int64_t kMaxTopkRows = 1LL << 24;   // rows of one top-k launch (one 256-lane workgroup each)
+constexpr int64_t kMaxTopkRows = 1LL << 24;   // rows of one top-k launch (one workgroup each)
+constexpr int32_t kMaxTopkN = (1 << 30) - 1;  // scores per row (row bytes fit a 32-bit buffer range)
+constexpr int kMaxTopkK = 2048;               // selected entries per row (staged in LDS)
 hipError_t launch_topk(const float *scores, int64_t rows, int n, int64_t s_stride, int k, int32_t *idx,
                        int64_t o_stride, hipStream_t s);
 

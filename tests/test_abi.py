@@ -200,6 +200,7 @@ def test_topk_rejects_bad_arguments():
     assert lib.ds4attn_topk(FAKE, 4, 100, 400, 8, FAKE + 1200, 32, None) == da.E_INVAL
     # more rows than one launch takes
     assert lib.ds4attn_topk(FAKE, (1 << 24) + 1, 100, 400, 8, out, 32, None) == da.E_UNSUPPORTED
+    assert lib.ds4attn_topk(FAKE, 1, 1 << 30, 0, 8, out, 32, None) == da.E_UNSUPPORTED
     # no rows: nothing to launch
     assert lib.ds4attn_topk(FAKE, 0, 100, 400, 8, out, 32, None) == da.OK
 
