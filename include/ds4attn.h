@@ -12,6 +12,9 @@
  *   ds4attn_decode    fused Q.K^T, online softmax and P.V (tuned for few tokens)
  *   ds4attn_prefill   the same computation, tuned for long token chunks
  *
+ * and two steps around it: ds4attn_quantize_fp8 (K/V rows into the FP8 cache
+ * format) and ds4attn_topk (an index list from given scores).
+ *
  * Pages the operations follow:
  *   [P-Metal] "How DeepSeek V4 Flash Model Inference Works on Apple Silicon with
  *             Metal Backend" (instagit.com, antirez/ds4)
@@ -51,8 +54,21 @@ enum {
   DS4ATTN_E_HIP = 4           /* the HIP runtime refused a launch */
 };
 
-/* Element types of Q, K and V (Q and K/V must match).  O is always float32. */
-enum { DS4ATTN_F16 = 0, DS4ATTN_F32 = 1 };
+/* Element types.  Q, and K/V stored plainly, are F16 or F32 (the same type);
+ * E4M3 is the element type of quantized K/V rows (OCP FP8 E4M3: bias 7, 3
+ * mantissa bits, no infinities, 0x7F/0xFF NaN, largest value 448).  O is always
+ * float32. */
+enum { DS4ATTN_F16 = 0, DS4ATTN_F32 = 1, DS4ATTN_E4M3 = 2 };
+
+/* Storage of K and V rows (ds4attn_args.kv_format).
+ *   PLAIN:     elements of ds4attn_args.dtype.
+ *   FP8_E4M3:  E4M3 codes with one float32 scale per K row and one per V row
+ *              (region.k_scale / v_scale); a row's value is decode(code) * scale.
+ *              This is the cache format ds4attn_quantize_fp8 writes ([P-DS4]
+ *              "Architecture Deep Dive", Whole-Model Graph Execution: K/V rows are
+ *              quantized to FP8 before they are stored; the element format and the
+ *              per-row scale are this library's choice, the pages give none). */
+enum { DS4ATTN_KV_PLAIN = 0, DS4ATTN_KV_FP8_E4M3 = 1 };
 
 /* Status byte values of the block map ([P-Metal] "Mask Handling and Block Skipping":
  * a single-byte status per block; fully masked blocks are skipped).  FULL marks a
@@ -73,14 +89,20 @@ enum {
  * rows [n_rows, ceil32(n_rows)) must exist (ds4attn_pad provides them).  Rows
  * that are masked are never allowed to reach the result, whatever they hold.
  * valid: device uint8 [batch][valid_stride_b bytes], nonzero = row visible, or
- * NULL = every live row visible. */
+ * NULL = every live row visible.
+ * k_scale, v_scale: FP8 rows only (kv_format DS4ATTN_KV_FP8_E4M3), else ignored:
+ * device float32, the scale of row r of sequence b at byte offset
+ * b*scale_stride_b + 4*r; only rows < n_rows are read.  The scales may alias. */
 typedef struct ds4attn_region {
   const void *k;
   const void *v;
   const uint8_t *valid;
+  const float *k_scale;
+  const float *v_scale;
   int64_t stride_b;
   int64_t stride_row;
   int64_t valid_stride_b;
+  int64_t scale_stride_b;
   int32_t n_rows;
   int32_t reserved;
 } ds4attn_region;
@@ -115,7 +137,7 @@ typedef struct ds4attn_args {
   ds4attn_region r1;    /* compressed rows; n_rows = 0 if absent */
   const int32_t *r1_index;  /* device int32 [B][T][r1_k], or NULL */
   int32_t r1_k;             /* entries per token when r1_index != NULL (1..2048) */
-  int32_t reserved;
+  int32_t kv_format;        /* DS4ATTN_KV_PLAIN (0) or DS4ATTN_KV_FP8_E4M3, both regions */
 } ds4attn_args;
 
 /*
@@ -127,6 +149,9 @@ typedef struct ds4attn_args {
  *
  *   in       region with in->n_rows live rows; in->k, in->v device [B][n_rows][head_dim]
  *            by in->stride_b / in->stride_row; in->valid optional.
+ *   dtype    element type of the rows: DS4ATTN_F16, DS4ATTN_F32 or DS4ATTN_E4M3 (FP8
+ *            codes; a zero code is +0.0; the per-row scales are not touched, the
+ *            attention never reads the scale of a padding row).
  *   k_pad, v_pad  device outputs [B][ceil32(n_rows)][head_dim] by out_stride_b /
  *            out_stride_row.  Rows < n_rows are copied bit for bit; rows
  *            [n_rows, ceil32(n_rows)) are set to +0.0 (all bits zero).  If
@@ -183,7 +208,13 @@ int ds4attn_blockmap_dims(const ds4attn_args *a, int32_t bq, int64_t *n_tiles, i
  * token in one workgroup (for 2048-token chunks,
  * [P-DS4] Whole-Model Graph Execution).  Supported: D in {64,128,256,512},
  * F16 or F32; D = 512 F16 with H % 16 == 0 runs on the matrix cores, the rest
- * on the vector-ALU kernel.
+ * on the vector-ALU kernel.  FP8 rows (a->kv_format = DS4ATTN_KV_FP8_E4M3) need
+ * the matrix-core case (F16 Q, D = 512, H % 16 == 0, no DS4ATTN_FLAG_GENERIC);
+ * the rows are 512 bytes of codes, strides multiples of 16 as above, and both
+ * regions with live rows need k_scale and v_scale (4-byte aligned,
+ * scale_stride_b a multiple of 4 and >= 4*n_rows when batch > 1); anything else
+ * with FP8 rows returns DS4ATTN_E_UNSUPPORTED (shapes) or DS4ATTN_E_INVAL
+ * (pointers, strides).
  * Returns DS4ATTN_OK, DS4ATTN_E_INVAL, DS4ATTN_E_UNSUPPORTED or DS4ATTN_E_HIP.
  */
 int ds4attn_decode(const ds4attn_args *a, const void *q, const uint8_t *blk, int32_t bq,
@@ -218,6 +249,29 @@ int32_t ds4attn_prefill_bq(void);
  */
 int ds4attn_topk(const float *scores, int64_t rows, int32_t n, int64_t score_stride, int32_t k,
                  int32_t *idx, int64_t idx_stride, void *stream);
+
+/*
+ * ds4attn_quantize_fp8 -- the FP8 KV quantize step ([P-DS4] "Architecture Deep
+ * Dive", Whole-Model Graph Execution: K/V rows are quantized to FP8 before they
+ * are stored in the cache; the format is this library's choice, see
+ * DS4ATTN_KV_FP8_E4M3).
+ *
+ *   x       device rows [batch][n_rows][head_dim] of dtype (DS4ATTN_F16 or DS4ATTN_F32),
+ *           row r of sequence b at x + b*x_stride_b + r*x_stride_row; finite values
+ *   codes   device uint8 output, same indexing by code_stride_b / code_stride_row
+ *   scales  device float32 output, row r of sequence b at byte b*scale_stride_b + 4*r
+ * Per row, in float32: amax = max |x|, scale = amax / 448; each code is the E4M3
+ * value nearest to x / scale clamped to [-448, 448], ties to even mantissa, with
+ * the sign bit of x / scale; a row with scale 0 gets zero codes.
+ * head_dim in {64, 128, 256, 512}; x, codes and their strides 16-byte aligned;
+ * scales 4-byte aligned with scale_stride_b a multiple of 4 and >= 4*n_rows when
+ * batch > 1; outputs must not overlap x or each other.
+ * Returns DS4ATTN_OK, DS4ATTN_E_INVAL, DS4ATTN_E_UNSUPPORTED or DS4ATTN_E_HIP.
+ */
+int ds4attn_quantize_fp8(const void *x, int32_t dtype, int32_t batch, int32_t n_rows, int32_t head_dim,
+                         int64_t x_stride_b, int64_t x_stride_row, uint8_t *codes,
+                         int64_t code_stride_b, int64_t code_stride_row, float *scales,
+                         int64_t scale_stride_b, void *stream);
 
 /* A static, NUL-terminated description of a status code. */
 const char *ds4attn_status_string(int status);

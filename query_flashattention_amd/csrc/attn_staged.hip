@@ -41,7 +41,12 @@ namespace ds4attn {
 
 enum : int { kSplitHeads = 0, kSplitDims = 1 };
 
-template <int MODE, bool INDEXED>
+// FP8 rows (E4M3 codes, a float32 scale per row): the rows travel to LDS as codes
+// (half the bytes), two rows per transfer, and are converted where the operands
+// are read: K codes to float16 (exact), with the row's scale applied to the fp32
+// scores; V codes through an 8-bit transpose read to float16 (exact), times the
+// rows' scales in float16.  P and the accumulators are as for float16 rows.
+template <int MODE, bool INDEXED, bool FP8>
 __global__ __launch_bounds__(256, MODE == kSplitHeads ? 2 : 1) void attn_staged_kernel(const AttnParams p) {
   constexpr int HG = MODE == kSplitHeads ? 64 : 16;   // heads per workgroup
   constexpr int NKS = MODE == kSplitHeads ? 16 : 4;    // 32-dim k-steps of S per wave
@@ -69,9 +74,12 @@ __global__ __launch_bounds__(256, MODE == kSplitHeads ? 2 : 1) void attn_staged_
   const int h = hg * HG + (MODE == kSplitHeads ? 16 * w : 0) + c16;
   const int d0 = MODE == kSplitHeads ? 0 : 128 * w;
 
-  // Two tile buffers as separate LDS objects.
-  __shared__ __attribute__((aligned(16))) char kt0[kKTile], kt1[NBUF == 2 ? kKTile : 16];
-  __shared__ __attribute__((aligned(16))) char vt0[kVTile], vt1[NBUF == 2 ? kVTile : 16];
+  // Two tile buffers as separate LDS objects (FP8: codes, plus the blocks' row scales).
+  constexpr int KT = FP8 ? kF8Tile : kKTile, VT = FP8 ? kF8Tile : kVTile;
+  __shared__ __attribute__((aligned(16))) char kt0[KT], kt1[NBUF == 2 ? KT : 16];
+  __shared__ __attribute__((aligned(16))) char vt0[VT], vt1[NBUF == 2 ? VT : 16];
+  // scales of block rows 8w'..8w'+7: K at [16w' + q], V at [16w' + 8 + q]
+  __shared__ __attribute__((aligned(16))) float sc0[FP8 ? 64 : 4], sc1[FP8 && NBUF == 2 ? 64 : 4];
   __shared__ floatx4 xs[MODE == kSplitDims ? 4 * 2 * 64 : 1];   // partial S^T exchange
   __shared__ uint16_t blist[kListCap];
   __shared__ int cnt[4];
@@ -83,6 +91,7 @@ __global__ __launch_bounds__(256, MODE == kSplitHeads ? 2 : 1) void attn_staged_
   // transfers into one pair from the reads of the other.
   auto ktile = [&](auto buf) -> char * { return decltype(buf)::value ? kt1 : kt0; };
   auto vtile = [&](auto buf) -> char * { return decltype(buf)::value ? vt1 : vt0; };
+  auto stile = [&](auto buf) -> float * { return decltype(buf)::value ? sc1 : sc0; };
 
   // Start the transfers of key block j (uniform) into buffer pair `buf`: wave w
   // moves rows 8w..8w+7 of K and of V, one 1 KiB row per instruction, kStageOps
@@ -91,43 +100,87 @@ __global__ __launch_bounds__(256, MODE == kSplitHeads ? 2 : 1) void attn_staged_
   // entries that are unused read row 0) and hidden rows are cleared afterwards.
   auto stage_rows = [&](int j, uint32_t vm, auto buf) __attribute__((always_inline)) {
     const uint32_t kbase = lds_addr(ktile(buf)), vbase = lds_addr(vtile(buf));
-    const char *kb, *vb;
+    const char *kb, *vb, *ksb = nullptr, *vsb = nullptr;
     int64_t sr;
-    int base;
+    int base, nlive;
     if (j < p.nb0) {
       kb = p.k0 + b * p.kv0_sb;
       vb = p.v0 + b * p.kv0_sb;
       sr = p.kv0_sr;
       base = j * kRowsPerBlock;
+      nlive = p.n0;
+      if (FP8) {
+        ksb = p.ks0 + b * p.s0_sb;
+        vsb = p.vs0 + b * p.s0_sb;
+      }
     } else {
       kb = p.k1 + b * p.kv1_sb;
       vb = p.v1 + b * p.kv1_sb;
       sr = p.kv1_sr;
       base = (j - p.nb0) * kRowsPerBlock;
+      nlive = p.n1;
+      if (FP8) {
+        ksb = p.ks1 + b * p.s1_sb;
+        vsb = p.vs1 + b * p.s1_sb;
+      }
     }
-    int rows[8];
-    if (INDEXED && j >= p.nb0) {
-      // the wave's eight list entries in two 16-byte LDS reads (entries past r1_k
-      // hold -1); unused entries read row 0, they are masked
-      const int4 *src = (const int4 *)&idx_s[base + 8 * w];
-      const int4 c0 = src[0], c1 = src[1];
-      const int cs[8] = {c0.x, c0.y, c0.z, c0.w, c1.x, c1.y, c1.z, c1.w};
+    if constexpr (FP8) {
+      // pair pp = rows 2pp, 2pp+1 of the wave's eight: lane i moves 16 bytes of
+      // row (i & 1) from byte 16 * (i >> 1).  Each lane resolves its own row (a
+      // gathered entry is read from the list; unused entries read row 0, masked).
+      const int hsel = lane & 1;
+      const int64_t chunk = 16 * (lane >> 1);
+      auto lane_row = [&](int q) -> int {
+        int row = base + 8 * w + q;
+        if (INDEXED && j >= p.nb0) {
+          const int c = idx_s[row];
+          row = (c >= 0 && c < p.n1) ? c : 0;
+        }
+        return row;
+      };
 #pragma unroll
-      for (int q = 0; q < 8; ++q) {
-        const int c = __builtin_amdgcn_readfirstlane(cs[q]);
-        rows[q] = (c >= 0 && c < p.n1) ? c : 0;
+      for (int pp = 0; pp < 4; ++pp) {
+        const int q = 2 * pp + hsel;
+        const int row = lane_row(q);
+        const bool shown = (vm >> (8 * w + q)) & 1u;
+        const uint32_t off = (uint32_t)f8_pair_off(4 * w + pp);
+        dma16_lanes(shown ? kb + row * sr + chunk : kZeroRow + chunk, kbase + off);
+        dma16_lanes(shown ? vb + row * sr + chunk : kZeroRow + chunk, vbase + off);
+      }
+      // lanes 0-7: K scales of the eight rows, lanes 8-15: V scales (rows past the
+      // region's live rows have none and read zero)
+      if (lane < 16) {
+        const int q = lane & 7;
+        const int row = lane_row(q);
+        const bool shown = ((vm >> (8 * w + q)) & 1u) && row < nlive;
+        dma4_lanes(shown ? (lane < 8 ? ksb : vsb) + 4 * (int64_t)row : kZeroRow,
+                   lds_addr(stile(buf)) + 64u * w);
       }
     } else {
+      int rows[8];
+      if (INDEXED && j >= p.nb0) {
+        // the wave's eight list entries in two 16-byte LDS reads (entries past r1_k
+        // hold -1); unused entries read row 0, they are masked
+        const int4 *src = (const int4 *)&idx_s[base + 8 * w];
+        const int4 c0 = src[0], c1 = src[1];
+        const int cs[8] = {c0.x, c0.y, c0.z, c0.w, c1.x, c1.y, c1.z, c1.w};
 #pragma unroll
-      for (int q = 0; q < 8; ++q) rows[q] = base + 8 * w + q;
-    }
+        for (int q = 0; q < 8; ++q) {
+          const int c = __builtin_amdgcn_readfirstlane(cs[q]);
+          rows[q] = (c >= 0 && c < p.n1) ? c : 0;
+        }
+      } else {
 #pragma unroll
-    for (int q = 0; q < 8; ++q) {
-      const int rr = 8 * w + q;
-      const int row = rows[q];
-      const bool shown = (vm >> rr) & 1u;
-      dma16(shown ? kb + row * sr : kZeroRow, lane16, kbase + rr * kKRow);
-      dma16(shown ? vb + row * sr : kZeroRow, lane16, vbase + rr * kVRow);
+        for (int q = 0; q < 8; ++q) rows[q] = base + 8 * w + q;
+      }
+#pragma unroll
+      for (int q = 0; q < 8; ++q) {
+        const int rr = 8 * w + q;
+        const int row = rows[q];
+        const bool shown = (vm >> rr) & 1u;
+        dma16(shown ? kb + row * sr : kZeroRow, lane16, kbase + rr * kKRow);
+        dma16(shown ? vb + row * sr : kZeroRow, lane16, vbase + rr * kVRow);
+      }
     }
   };
   using Pair0 = std::integral_constant<int, 0>;
@@ -285,7 +338,14 @@ __global__ __launch_bounds__(256, MODE == kSplitHeads ? 2 : 1) void attn_staged_
     while (hidden) {
       const int rr = 8 * w + __ffs(hidden) - 1;
       hidden &= hidden - 1;
-      *(uint4 *)(vt + rr * kVRow + 16 * lane) = make_uint4(0u, 0u, 0u, 0u);
+      if constexpr (FP8) {
+        // the row's 32 chunks of 16 bytes, and its V scale
+        if (lane < 32)
+          *(uint4 *)(vt + f8_pair_off(rr >> 1) + 16 * (rr & 1) + 32 * lane) = make_uint4(0u, 0u, 0u, 0u);
+        if (lane == 0) stile(buf)[16 * w + 8 + (rr & 7)] = 0.f;
+      } else {
+        *(uint4 *)(vt + rr * kVRow + 16 * lane) = make_uint4(0u, 0u, 0u, 0u);
+      }
     }
   };
 
@@ -333,22 +393,44 @@ __global__ __launch_bounds__(256, MODE == kSplitHeads ? 2 : 1) void attn_staged_
     // ---- S^T = K Q^T over this wave's head dims; operand reads run KPD steps ahead
     floatx4 s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
     const char *ktc = ktile(buf), *vtc = vtile(buf);
-    const char *krow0 = ktc + c16 * kKRow + 2 * (d0 + 8 * g), *krow1 = krow0 + 16 * kKRow;
-    uint4 ka[KPD], kb[KPD];
+    if constexpr (FP8) {
+      // row c16 (pair c16 / 2) and row 16 + c16, dims d0 + 32ks + 8g .. +7: 8 codes
+      const char *krow0 = ktc + f8_pair_off(c16 >> 1) + 16 * (c16 & 1) + 2 * d0 + 32 * (g >> 1) + 8 * (g & 1);
+      const char *krow1 = krow0 + (f8_pair_off(8) - f8_pair_off(0));
+      uint2 ka[KPD], kb[KPD];
 #pragma unroll
-    for (int u = 0; u < KPD; ++u) {
-      ka[u] = *(const uint4 *)(krow0 + 64 * u);
-      kb[u] = *(const uint4 *)(krow1 + 64 * u);
-    }
-#pragma unroll
-    for (int ks = 0; ks < NKS; ++ks) {
-      s0 = mfma16(*(const half8 *)&ka[ks % KPD], qf[ks], s0);
-      s1 = mfma16(*(const half8 *)&kb[ks % KPD], qf[ks], s1);
-      if (ks + KPD < NKS) {
-        ka[ks % KPD] = *(const uint4 *)(krow0 + 64 * (ks + KPD));
-        kb[ks % KPD] = *(const uint4 *)(krow1 + 64 * (ks + KPD));
+      for (int u = 0; u < KPD; ++u) {
+        ka[u] = *(const uint2 *)(krow0 + 64 * u);
+        kb[u] = *(const uint2 *)(krow1 + 64 * u);
       }
-      __builtin_amdgcn_sched_barrier(0);   // keep this order: MFMAs, then the reads they free
+#pragma unroll
+      for (int ks = 0; ks < NKS; ++ks) {
+        s0 = mfma16(e4m3x8_to_half8(ka[ks % KPD]), qf[ks], s0);
+        s1 = mfma16(e4m3x8_to_half8(kb[ks % KPD]), qf[ks], s1);
+        if (ks + KPD < NKS) {
+          ka[ks % KPD] = *(const uint2 *)(krow0 + 64 * (ks + KPD));
+          kb[ks % KPD] = *(const uint2 *)(krow1 + 64 * (ks + KPD));
+        }
+        __builtin_amdgcn_sched_barrier(0);   // keep this order: MFMAs, then the reads they free
+      }
+    } else {
+      const char *krow0 = ktc + c16 * kKRow + 2 * (d0 + 8 * g), *krow1 = krow0 + 16 * kKRow;
+      uint4 ka[KPD], kb[KPD];
+#pragma unroll
+      for (int u = 0; u < KPD; ++u) {
+        ka[u] = *(const uint4 *)(krow0 + 64 * u);
+        kb[u] = *(const uint4 *)(krow1 + 64 * u);
+      }
+#pragma unroll
+      for (int ks = 0; ks < NKS; ++ks) {
+        s0 = mfma16(*(const half8 *)&ka[ks % KPD], qf[ks], s0);
+        s1 = mfma16(*(const half8 *)&kb[ks % KPD], qf[ks], s1);
+        if (ks + KPD < NKS) {
+          ka[ks % KPD] = *(const uint4 *)(krow0 + 64 * (ks + KPD));
+          kb[ks % KPD] = *(const uint4 *)(krow1 + 64 * (ks + KPD));
+        }
+        __builtin_amdgcn_sched_barrier(0);   // keep this order: MFMAs, then the reads they free
+      }
     }
     if (MODE == kSplitDims) {
       // partial tiles meet in LDS; every wave adds them in the same order
@@ -365,10 +447,23 @@ __global__ __launch_bounds__(256, MODE == kSplitHeads ? 2 : 1) void attn_staged_
     }
     // ---- online softmax: this lane holds rows slot_row(g, 0..7) of head h
     float sv[8];
+    if constexpr (FP8) {
+      // K row scales of slot rows 4g..4g+3 and 16+4g..16+4g+3
+      const float *sc = stile(buf);
+      const float4 klo = *(const float4 *)(sc + 16 * (g >> 1) + 4 * (g & 1));
+      const float4 khi = *(const float4 *)(sc + 16 * (2 + (g >> 1)) + 4 * (g & 1));
+      const float kq[8] = {klo.x, klo.y, klo.z, klo.w, khi.x, khi.y, khi.z, khi.w};
 #pragma unroll
-    for (int i2 = 0; i2 < 4; ++i2) {
-      sv[i2] = s0[i2] * p.scale_log2;
-      sv[4 + i2] = s1[i2] * p.scale_log2;
+      for (int i2 = 0; i2 < 4; ++i2) {
+        sv[i2] = s0[i2] * (p.scale_log2 * kq[i2]);
+        sv[4 + i2] = s1[i2] * (p.scale_log2 * kq[4 + i2]);
+      }
+    } else {
+#pragma unroll
+      for (int i2 = 0; i2 < 4; ++i2) {
+        sv[i2] = s0[i2] * p.scale_log2;
+        sv[4 + i2] = s1[i2] * p.scale_log2;
+      }
     }
     const uint32_t vis = __builtin_amdgcn_readfirstlane(vmask[i & (kMaskRing - 1)]);
     if (vis != 0xffffffffu) {
@@ -402,26 +497,57 @@ __global__ __launch_bounds__(256, MODE == kSplitHeads ? 2 : 1) void attn_staged_
     }
     // ---- O^T += V^T P^T; V^T operand = two transpose reads (slots 0-3, 4-7), VPD
     // output tiles ahead
-    const lds_char *vrow0 = (const lds_char *)(__attribute__((address_space(3))) const void *)vtc +
-                            tr_r0 * kVRow + 2 * d0 + 8 * tr_a;
-    const lds_char *vrow1 = vrow0 + 16 * kVRow;
-    auto vload = [&](int dt) __attribute__((always_inline)) -> half8 {
-      const short4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-          (__attribute__((address_space(3))) short4_t *)(vrow0 + 32 * dt));
-      const short4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-          (__attribute__((address_space(3))) short4_t *)(vrow1 + 32 * dt));
-      // whole-vector casts: slots 0-3 from the first read, 4-7 from the second
-      return __builtin_shufflevector(__builtin_bit_cast(half4, lo), __builtin_bit_cast(half4, hi), 0,
-                                     1, 2, 3, 4, 5, 6, 7);
-    };
-    half8 vq[VPD];
+    if constexpr (FP8) {
+      // 8-bit transpose read (lane 16G + 8H + B receives byte B of lanes 16G + H + 2k,
+      // k = 0..7, measured on the device): this lane supplies row slot_row(g, k),
+      // k = (lane & 15) >> 1, dims 16dt + 8(lane & 1) .. +7, so lane 16g + c
+      // receives dim 16dt + c of its group's eight slot rows
+      const int trk = (lane & 15) >> 1;
+      const int trow = trk < 4 ? 4 * g + trk : 16 + 4 * g + (trk - 4);
+      const lds_char *vsrc = (const lds_char *)(__attribute__((address_space(3))) const void *)vtc +
+                             f8_pair_off(trow >> 1) + 16 * (trow & 1) + 2 * d0 + 8 * (lane & 1);
+      // V row scales of the slot rows, in float16
+      const float *sc = stile(buf);
+      const float4 vlo = *(const float4 *)(sc + 16 * (g >> 1) + 8 + 4 * (g & 1));
+      const float4 vhi = *(const float4 *)(sc + 16 * (2 + (g >> 1)) + 8 + 4 * (g & 1));
+      const half8 vsc = {(_Float16)vlo.x, (_Float16)vlo.y, (_Float16)vlo.z, (_Float16)vlo.w,
+                         (_Float16)vhi.x, (_Float16)vhi.y, (_Float16)vhi.z, (_Float16)vhi.w};
+      auto vload = [&](int dt) __attribute__((always_inline)) -> uint2 {
+        const int2v r = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
+            (__attribute__((address_space(3))) int2v *)(vsrc + 32 * dt));
+        return make_uint2((uint32_t)r.x, (uint32_t)r.y);
+      };
+      uint2 vq[VPD];
 #pragma unroll
-    for (int u = 0; u < VPD; ++u) vq[u] = vload(u);
+      for (int u = 0; u < VPD; ++u) vq[u] = vload(u);
 #pragma unroll
-    for (int dt = 0; dt < NDT; ++dt) {
-      o[dt] = mfma16(vq[dt % VPD], pf, o[dt]);
-      if (dt + VPD < NDT) vq[dt % VPD] = vload(dt + VPD);
-      __builtin_amdgcn_sched_barrier(0);   // keep this order: MFMA, then the reads it frees
+      for (int dt = 0; dt < NDT; ++dt) {
+        o[dt] = mfma16(e4m3x8_to_half8(vq[dt % VPD]) * vsc, pf, o[dt]);
+        if (dt + VPD < NDT) vq[dt % VPD] = vload(dt + VPD);
+        __builtin_amdgcn_sched_barrier(0);   // keep this order: MFMA, then the reads it frees
+      }
+    } else {
+      const lds_char *vrow0 = (const lds_char *)(__attribute__((address_space(3))) const void *)vtc +
+                              tr_r0 * kVRow + 2 * d0 + 8 * tr_a;
+      const lds_char *vrow1 = vrow0 + 16 * kVRow;
+      auto vload = [&](int dt) __attribute__((always_inline)) -> half8 {
+        const short4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (__attribute__((address_space(3))) short4_t *)(vrow0 + 32 * dt));
+        const short4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (__attribute__((address_space(3))) short4_t *)(vrow1 + 32 * dt));
+        // whole-vector casts: slots 0-3 from the first read, 4-7 from the second
+        return __builtin_shufflevector(__builtin_bit_cast(half4, lo), __builtin_bit_cast(half4, hi), 0,
+                                       1, 2, 3, 4, 5, 6, 7);
+      };
+      half8 vq[VPD];
+#pragma unroll
+      for (int u = 0; u < VPD; ++u) vq[u] = vload(u);
+#pragma unroll
+      for (int dt = 0; dt < NDT; ++dt) {
+        o[dt] = mfma16(vq[dt % VPD], pf, o[dt]);
+        if (dt + VPD < NDT) vq[dt % VPD] = vload(dt + VPD);
+        __builtin_amdgcn_sched_barrier(0);   // keep this order: MFMA, then the reads it frees
+      }
     }
 
     lds_barrier();   // every wave is done with buffer B
@@ -434,7 +560,7 @@ __global__ __launch_bounds__(256, MODE == kSplitHeads ? 2 : 1) void attn_staged_
         lds_barrier();
       }
       stage(nx, buf, Masked{});
-      if constexpr (NBUF == 2) wait_vmcnt<kStageOps>();   // block i+1 (staged earlier) landed
+      if constexpr (NBUF == 2) wait_vmcnt<FP8 ? kF8StageOps : kStageOps>();   // block i+1 (staged earlier) landed
       else wait_vmcnt<0>();
     } else {
       wait_vmcnt<0>();
@@ -467,8 +593,13 @@ static hipError_t launch_staged(const AttnParams &p, hipStream_t s) {
   const int64_t n = (int64_t)p.B * p.T * (p.H / HG);
   if (n == 0) return hipSuccess;
   const dim3 grid((unsigned)n), block(256);
-  if (p.indexed) hipLaunchKernelGGL((attn_staged_kernel<MODE, true>), grid, block, 0, s, p);
-  else hipLaunchKernelGGL((attn_staged_kernel<MODE, false>), grid, block, 0, s, p);
+  if (p.fp8) {
+    if (p.indexed) hipLaunchKernelGGL((attn_staged_kernel<MODE, true, true>), grid, block, 0, s, p);
+    else hipLaunchKernelGGL((attn_staged_kernel<MODE, false, true>), grid, block, 0, s, p);
+  } else {
+    if (p.indexed) hipLaunchKernelGGL((attn_staged_kernel<MODE, true, false>), grid, block, 0, s, p);
+    else hipLaunchKernelGGL((attn_staged_kernel<MODE, false, false>), grid, block, 0, s, p);
+  }
   return hipGetLastError();
 }
 

@@ -15,7 +15,17 @@ constexpr int kMaxIndexK = kIdxCap;
 inline int64_t ceil32(int64_t n) { return (n + 31) / 32 * 32; }
 inline bool aligned16(const void *ptr) { return ((uintptr_t)ptr & 15u) == 0; }
 inline bool stride16(int64_t s) { return s >= 0 && (s & 15) == 0; }
-inline int elem_bytes(int32_t dtype) { return dtype == DS4ATTN_F16 ? 2 : 4; }
+inline int elem_bytes(int32_t dtype) { return dtype == DS4ATTN_F16 ? 2 : (dtype == DS4ATTN_E4M3 ? 1 : 4); }
+inline bool aligned4(const void *ptr) { return ((uintptr_t)ptr & 3u) == 0; }
+
+// FP8 regions with live rows need both scale arrays, holding n_rows floats per sequence.
+int check_scales(const ds4attn_region &r, int32_t batch) {
+  if (r.n_rows == 0 || batch == 0) return DS4ATTN_OK;
+  if (!r.k_scale || !r.v_scale || !aligned4(r.k_scale) || !aligned4(r.v_scale)) return DS4ATTN_E_INVAL;
+  if (r.scale_stride_b < 0 || (r.scale_stride_b & 3)) return DS4ATTN_E_INVAL;
+  if (batch > 1 && r.scale_stride_b < 4LL * r.n_rows) return DS4ATTN_E_INVAL;
+  return DS4ATTN_OK;
+}
 inline bool head_dim_ok(int32_t d) { return d == 64 || d == 128 || d == 256 || d == 512; }
 
 // A region with n_rows > 0 needs K, V and strides that hold whole padded rows.
@@ -79,11 +89,24 @@ int run_attention(const ds4attn_args *a, const void *q, const uint8_t *blk, int3
   if (a->head_dim <= 0) return DS4ATTN_E_INVAL;
   if (!head_dim_ok(a->head_dim)) return DS4ATTN_E_UNSUPPORTED;
   if (!std::isfinite(a->scale)) return DS4ATTN_E_INVAL;
+  if (a->kv_format != DS4ATTN_KV_PLAIN && a->kv_format != DS4ATTN_KV_FP8_E4M3) return DS4ATTN_E_INVAL;
+  const bool fp8 = a->kv_format == DS4ATTN_KV_FP8_E4M3;
   const int eb = elem_bytes(a->dtype);
-  const int row_bytes = a->head_dim * eb;
+  const int row_bytes = a->head_dim * eb;                       // Q rows
+  const int kv_row_bytes = fp8 ? a->head_dim : row_bytes;       // K/V rows
   AttnParams P;
-  int st = resolve_mask(a, row_bytes, true, P);
+  int st = resolve_mask(a, kv_row_bytes, true, P);
   if (st) return st;
+  if (fp8) {
+    if ((st = check_scales(a->r0, a->batch)) || (st = check_scales(a->r1, a->batch))) return st;
+    P.fp8 = 1;
+    P.ks0 = (const char *)a->r0.k_scale;
+    P.vs0 = (const char *)a->r0.v_scale;
+    P.s0_sb = a->r0.scale_stride_b;
+    P.ks1 = (const char *)a->r1.k_scale;
+    P.vs1 = (const char *)a->r1.v_scale;
+    P.s1_sb = a->r1.scale_stride_b;
+  }
   const int64_t work = (int64_t)a->batch * a->n_tok;
   if (work == 0) return DS4ATTN_OK;
   if (!q || !o || !aligned16(q) || !aligned16(o)) return DS4ATTN_E_INVAL;
@@ -116,6 +139,8 @@ int run_attention(const ds4attn_args *a, const void *q, const uint8_t *blk, int3
   const bool fits32 = (int64_t)P.nb0 * 32 * P.kv0_sr < 0x80000000LL && rows1 * P.kv1_sr < 0x80000000LL;
   const bool mfma = a->dtype == DS4ATTN_F16 && a->head_dim == 512 && a->n_head % 16 == 0 &&
                     !(a->flags & DS4ATTN_FLAG_GENERIC) && P.nbd <= kListCap && fits32;
+  // FP8 rows are dequantized inside the matrix-core kernels only
+  if (fp8 && !mfma) return DS4ATTN_E_UNSUPPORTED;
   if (mfma && prefill && a->n_head % 64 == 0) e = launch_attn_prefill(P, s);
   else if (mfma) e = launch_attn_decode(P, s);
   else e = launch_attn_generic(P, eb, s);
@@ -135,7 +160,7 @@ int ds4attn_pad(const ds4attn_region *in, int32_t batch, int32_t head_dim, int32
                 void *k_pad, void *v_pad, int64_t out_stride_b, int64_t out_stride_row,
                 uint8_t *valid_pad, int64_t valid_pad_stride_b, void *stream) {
   if (!in || batch < 0 || in->n_rows < 0) return DS4ATTN_E_INVAL;
-  if (dtype != DS4ATTN_F16 && dtype != DS4ATTN_F32) return DS4ATTN_E_INVAL;
+  if (dtype != DS4ATTN_F16 && dtype != DS4ATTN_F32 && dtype != DS4ATTN_E4M3) return DS4ATTN_E_INVAL;
   if (head_dim <= 0 || (head_dim * elem_bytes(dtype)) % 16) return DS4ATTN_E_INVAL;
   const int row_bytes = head_dim * elem_bytes(dtype);
   const int64_t n = in->n_rows, npad = ceil32(n);
@@ -239,6 +264,39 @@ int ds4attn_topk(const float *scores, int64_t rows, int32_t n, int64_t score_str
   const int64_t in_len = (rows - 1) * score_stride + 4LL * n;
   if (n > 0 && ranges_overlap(idx, out_len, scores, in_len)) return DS4ATTN_E_INVAL;
   const hipError_t e = launch_topk(scores, rows, n, score_stride, k, idx, idx_stride, (hipStream_t)stream);
+  return e == hipSuccess ? DS4ATTN_OK : DS4ATTN_E_HIP;
+}
+
+int ds4attn_quantize_fp8(const void *x, int32_t dtype, int32_t batch, int32_t n_rows, int32_t head_dim,
+                         int64_t x_stride_b, int64_t x_stride_row, uint8_t *codes,
+                         int64_t code_stride_b, int64_t code_stride_row, float *scales,
+                         int64_t scale_stride_b, void *stream) {
+  if (dtype != DS4ATTN_F16 && dtype != DS4ATTN_F32) return DS4ATTN_E_INVAL;
+  if (batch < 0 || n_rows < 0 || head_dim <= 0) return DS4ATTN_E_INVAL;
+  if (!head_dim_ok(head_dim)) return DS4ATTN_E_UNSUPPORTED;
+  if ((int64_t)batch * n_rows == 0) return DS4ATTN_OK;
+  if ((int64_t)batch * n_rows > 0x7fffffffLL) return DS4ATTN_E_UNSUPPORTED;
+  const int eb = elem_bytes(dtype);
+  const int64_t row_bytes = (int64_t)head_dim * eb;
+  if (!x || !codes || !scales || !aligned16(x) || !aligned16(codes) || !aligned4(scales))
+    return DS4ATTN_E_INVAL;
+  if (!stride16(x_stride_row) || !stride16(x_stride_b) || !stride16(code_stride_row) ||
+      !stride16(code_stride_b) || scale_stride_b < 0 || (scale_stride_b & 3))
+    return DS4ATTN_E_INVAL;
+  if (n_rows > 1 && (x_stride_row < row_bytes || code_stride_row < head_dim)) return DS4ATTN_E_INVAL;
+  if (batch > 1 && (x_stride_b < (n_rows - 1) * x_stride_row + row_bytes ||
+                    code_stride_b < (n_rows - 1) * code_stride_row + head_dim ||
+                    scale_stride_b < 4LL * n_rows))
+    return DS4ATTN_E_INVAL;
+  const int64_t x_len = (batch - 1) * x_stride_b + (n_rows - 1) * x_stride_row + row_bytes;
+  const int64_t c_len = (batch - 1) * code_stride_b + (n_rows - 1) * code_stride_row + head_dim;
+  const int64_t s_len = (batch - 1) * scale_stride_b + 4LL * n_rows;
+  if (ranges_overlap(codes, c_len, x, x_len) || ranges_overlap(scales, s_len, x, x_len) ||
+      ranges_overlap(scales, s_len, codes, c_len))
+    return DS4ATTN_E_INVAL;
+  const hipError_t e = launch_quant_fp8(x, eb, batch, n_rows, head_dim, x_stride_b, x_stride_row, codes,
+                                        code_stride_b, code_stride_row, scales, scale_stride_b,
+                                        (hipStream_t)stream);
   return e == hipSuccess ? DS4ATTN_OK : DS4ATTN_E_HIP;
 }
 

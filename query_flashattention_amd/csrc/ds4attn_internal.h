@@ -42,6 +42,10 @@ struct AttnParams {
   const int32_t *idx;      // [B][T][r1_k] or null
   int r1_k;
   int indexed;
+  // FP8 rows: E4M3 codes, one float32 scale per K row and per V row
+  int fp8;
+  const char *ks0, *vs0, *ks1, *vs1;   // scales of row r of sequence b at b * s*_sb + 4r
+  int64_t s0_sb, s1_sb;
   // block map
   const uint8_t *blk;      // [B][ntiles][nbd] or null (every block treated as PARTIAL)
   int bq;
@@ -115,6 +119,10 @@ hipError_t launch_attn_generic(const AttnParams &p, int elem_bytes, hipStream_t 
 // workgroups of 16; prefill keeps 64 heads of a token in one workgroup.
 hipError_t launch_attn_decode(const AttnParams &p, hipStream_t s);
 hipError_t launch_attn_prefill(const AttnParams &p, hipStream_t s);
+// FP8 quantize step: one wave per row of head_dim elements (elem_bytes 2 or 4).
+hipError_t launch_quant_fp8(const void *x, int elem_bytes, int B, int n, int D, int64_t x_sb, int64_t x_sr,
+                            uint8_t *codes, int64_t c_sb, int64_t c_sr, float *scales, int64_t s_sb,
+                            hipStream_t s);
 // Top-k index selection, one workgroup per row of scores.
 constexpr int64_t kMaxTopkRows = 1LL << 24;   // rows of one top-k launch (one workgroup each)
 constexpr int32_t kMaxTopkN = (1 << 30) - 1;  // scores per row (row bytes fit a 32-bit buffer range)

@@ -1,0 +1,126 @@
+// FP8 KV quantize step: each K or V row becomes E4M3 codes plus one float32
+// scale before it is stored in the cache ([P-DS4] "Architecture Deep Dive",
+// Whole-Model Graph Execution, where an FP8 KV quantize step precedes the raw KV
+// store; the element format and the per-row scale are this library's reading).
+//
+// One wave per row, E = D/64 consecutive elements per lane.  In float32: amax by a
+// wave reduction, scale = amax / 448, each element x / scale clamped to +-448 and
+// rounded to the nearest E4M3 value, ties to even.  The rounding is done on the
+// float32 bits (below 2^-6 the values are multiples of 2^-9, so a scaled
+// round-to-nearest-even gives the code directly; above, the top three mantissa
+// bits are kept with a round-to-nearest-even carry into the exponent), so both
+// the codes and the scale are exactly determined by float32 arithmetic.  Each
+// row is read once and written once: 2D or 4D bytes in, D + 4 bytes out.
+//
+// [P-DS4] = "DwarfStar 4 (DS4) -- DeepSeek V4 Flash Inference Engine".
+#include "ds4attn_internal.h"
+
+namespace ds4attn {
+
+namespace {
+
+constexpr float kE4M3Max = 448.0f;
+
+// E4M3 code of a float32 value with |y| <= 448.
+__device__ __forceinline__ uint32_t e4m3_code(float y) {
+  const uint32_t u = __float_as_uint(y);
+  const uint32_t sign = (u >> 24) & 0x80u;
+  const uint32_t a = u & 0x7fffffffu;
+  uint32_t mag;
+  if (a < 0x3c800000u) {
+    // below 2^-6: steps of 2^-9; the product is exact, the rounding is to even
+    mag = (uint32_t)__builtin_rintf(__uint_as_float(a) * 512.0f);
+  } else {
+    // keep 3 mantissa bits, round to nearest even (the carry may reach the
+    // exponent), then move the exponent bias from 127 to 7
+    mag = ((a + 0x7ffffu + ((a >> 20) & 1u)) >> 20) - (120u << 3);
+  }
+  return sign | mag;
+}
+
+template <int E, bool F32>
+__global__ __launch_bounds__(256) void quant_fp8_kernel(const char *__restrict__ x, int n, int64_t x_sb,
+                                                        int64_t x_sr, char *__restrict__ codes, int64_t c_sb,
+                                                        int64_t c_sr, char *__restrict__ scales,
+                                                        int64_t s_sb, int rows) {
+  const int lane = threadIdx.x & 63;
+  const int64_t r = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (r >= rows) return;
+  const int b = (int)(r / n), row = (int)(r % n);
+  const char *src = x + b * x_sb + row * x_sr + (int64_t)lane * E * (F32 ? 4 : 2);
+  // the lane's E elements are contiguous and aligned to their size (row starts and
+  // strides are multiples of 16 bytes)
+  float v[E];
+  if constexpr (F32) {
+    float t[E];
+    __builtin_memcpy(t, __builtin_assume_aligned(src, 4 * E < 16 ? 4 * E : 16), 4 * E);
+#pragma unroll
+    for (int i = 0; i < E; ++i) v[i] = t[i];
+  } else {
+    _Float16 t[E];
+    __builtin_memcpy(t, __builtin_assume_aligned(src, 2 * E < 16 ? 2 * E : 16), 2 * E);
+#pragma unroll
+    for (int i = 0; i < E; ++i) v[i] = (float)t[i];
+  }
+  float amax = 0.f;
+#pragma unroll
+  for (int i = 0; i < E; ++i) amax = fmaxf(amax, fabsf(v[i]));
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) amax = fmaxf(amax, __shfl_xor(amax, off));
+  const float scale = amax / kE4M3Max;
+  uint8_t c[E];
+#pragma unroll
+  for (int i = 0; i < E; ++i) {
+    uint32_t code = 0;
+    if (scale != 0.f) {
+      const float y = fminf(fmaxf(v[i] / scale, -kE4M3Max), kE4M3Max);   // keeps the sign of zero
+      code = e4m3_code(y);
+    }
+    c[i] = (uint8_t)code;
+  }
+  char *dst = codes + b * c_sb + row * c_sr + (int64_t)lane * E;
+  if constexpr (E == 8) {
+    uint2 w;
+    w.x = c[0] | (c[1] << 8) | (c[2] << 16) | ((uint32_t)c[3] << 24);
+    w.y = c[4] | (c[5] << 8) | (c[6] << 16) | ((uint32_t)c[7] << 24);
+    *(uint2 *)dst = w;
+  } else if constexpr (E == 4) {
+    *(uint32_t *)dst = c[0] | (c[1] << 8) | (c[2] << 16) | ((uint32_t)c[3] << 24);
+  } else if constexpr (E == 2) {
+    *(uint16_t *)dst = (uint16_t)(c[0] | (c[1] << 8));
+  } else {
+    *(uint8_t *)dst = c[0];
+  }
+  if (lane == 0) *(float *)(scales + b * s_sb + 4LL * row) = scale;
+}
+
+template <int E>
+hipError_t launch_e(bool f32, const void *x, int B, int n, int64_t x_sb, int64_t x_sr, uint8_t *codes,
+                    int64_t c_sb, int64_t c_sr, float *scales, int64_t s_sb, hipStream_t s) {
+  const int rows = B * n;
+  const dim3 grid((unsigned)((rows + 3) / 4)), block(256);
+  if (f32)
+    hipLaunchKernelGGL((quant_fp8_kernel<E, true>), grid, block, 0, s, (const char *)x, n, x_sb, x_sr,
+                       (char *)codes, c_sb, c_sr, (char *)scales, s_sb, rows);
+  else
+    hipLaunchKernelGGL((quant_fp8_kernel<E, false>), grid, block, 0, s, (const char *)x, n, x_sb, x_sr,
+                       (char *)codes, c_sb, c_sr, (char *)scales, s_sb, rows);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_quant_fp8(const void *x, int elem_bytes, int B, int n, int D, int64_t x_sb, int64_t x_sr,
+                            uint8_t *codes, int64_t c_sb, int64_t c_sr, float *scales, int64_t s_sb,
+                            hipStream_t s) {
+  const bool f32 = elem_bytes == 4;
+  switch (D) {
+    case 64: return launch_e<1>(f32, x, B, n, x_sb, x_sr, codes, c_sb, c_sr, scales, s_sb, s);
+    case 128: return launch_e<2>(f32, x, B, n, x_sb, x_sr, codes, c_sb, c_sr, scales, s_sb, s);
+    case 256: return launch_e<4>(f32, x, B, n, x_sb, x_sr, codes, c_sb, c_sr, scales, s_sb, s);
+    case 512: return launch_e<8>(f32, x, B, n, x_sb, x_sr, codes, c_sb, c_sr, scales, s_sb, s);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+}  // namespace ds4attn

@@ -10,6 +10,20 @@ namespace ds4attn {
 typedef short short4_t __attribute__((ext_vector_type(4)));
 typedef _Float16 half4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) char lds_char;
+typedef int int2v __attribute__((ext_vector_type(2)));
+typedef _Float16 half2v __attribute__((ext_vector_type(2)));
+
+// Eight E4M3 codes (byte i = element i) to float16, exactly (every finite E4M3
+// value is a float16 value; the conversion's scale operand is 1).
+__device__ __forceinline__ half8 e4m3x8_to_half8(uint2 w) {
+  const half2v a = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8((int)w.x, 1.0f, false);
+  const half2v b = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8((int)w.x, 1.0f, true);
+  const half2v c = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8((int)w.y, 1.0f, false);
+  const half2v d = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8((int)w.y, 1.0f, true);
+  const half4 ab = __builtin_shufflevector(a, b, 0, 1, 2, 3);
+  const half4 cd = __builtin_shufflevector(c, d, 0, 1, 2, 3);
+  return __builtin_shufflevector(ab, cd, 0, 1, 2, 3, 4, 5, 6, 7);
+}
 
 // One row: 16 bytes per lane from `row` + 16 * lane (`row` uniform) into LDS at
 // `lds` + 16 * lane (`lds` uniform).  The row address travels in scalar registers
@@ -27,6 +41,20 @@ __device__ __forceinline__ void dma16(const char *row, uint32_t lane16, uint32_t
   const uint64_t ru = ((uint64_t)hi << 32) | (uint64_t)lo;
   asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1"
                :: "v"(lane16), "s"(ru), "s"(__builtin_amdgcn_readfirstlane(lds)) : "memory");
+}
+
+// The same transfer with a per-lane source address: lane i's 16 bytes come from
+// `src` (a different row for different lanes) and land at `lds` + 16 * i.  Used
+// for FP8 rows, two 512-byte rows per instruction.
+__device__ __forceinline__ void dma16_lanes(const char *src, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
+               :: "v"(src), "s"(__builtin_amdgcn_readfirstlane(lds)) : "memory");
+}
+
+// 4 bytes per active lane from a per-lane address into LDS at `lds` + 4 * lane.
+__device__ __forceinline__ void dma4_lanes(const char *src, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dword %0, off"
+               :: "v"(src), "s"(__builtin_amdgcn_readfirstlane(lds)) : "memory");
 }
 
 // LDS byte address of a shared-memory pointer.
@@ -68,6 +96,17 @@ constexpr int kTable = 256 / kRowsPerBlock;   // dense blocks masked at the star
 // rows x 32 bytes of a transpose read spread over 8-byte bank groups).
 constexpr int kKRow = 1040, kVRow = 1056;
 constexpr int kKTile = 32 * kKRow, kVTile = 32 * kVRow;
+
+// FP8 tiles (512-byte rows of E4M3 codes).  One transfer moves a pair of rows,
+// interleaved in 16-byte chunks: byte 32c + 16h + e of pair p is byte 16c + e of
+// row 2p + h.  Pairs are 1056 bytes apart, pairs 8..15 shifted by 128 more, so
+// that the 8-byte operand reads of one half-wave (K: 16 rows x 2 chunks halves;
+// V transpose reads: rows 0-7 with 16-23, or 8-15 with 24-31) fall on distinct
+// banks.  A stage is 4 K pairs, 4 V pairs and one transfer of 16 scales per wave.
+constexpr int kF8Pair = 1056;
+__host__ __device__ constexpr int f8_pair_off(int p) { return p * kF8Pair + (p >= 8 ? 128 : 0); }
+constexpr int kF8Tile = 16 * kF8Pair + 128;
+constexpr int kF8StageOps = 9;
 
 
 }  // namespace ds4attn

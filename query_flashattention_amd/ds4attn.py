@@ -19,7 +19,8 @@ import torch
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libds4attn.so")
 
 OK, E_INVAL, E_UNSUPPORTED, E_HIP = 0, 1, 2, 4
-F16, F32 = 0, 1
+F16, F32, E4M3 = 0, 1, 2
+KV_PLAIN, KV_FP8_E4M3 = 0, 1
 BLK_SKIP, BLK_PARTIAL, BLK_FULL = 0, 1, 2
 FLAG_GENERIC = 1
 
@@ -29,8 +30,9 @@ _i32, _i64 = ctypes.c_int32, ctypes.c_int64
 
 class Region(ctypes.Structure):
     _fields_ = [("k", _c_void_p), ("v", _c_void_p), ("valid", _c_void_p),
+                ("k_scale", _c_void_p), ("v_scale", _c_void_p),
                 ("stride_b", _i64), ("stride_row", _i64), ("valid_stride_b", _i64),
-                ("n_rows", _i32), ("reserved", _i32)]
+                ("scale_stride_b", _i64), ("n_rows", _i32), ("reserved", _i32)]
 
 
 class Args(ctypes.Structure):
@@ -41,11 +43,12 @@ class Args(ctypes.Structure):
                 ("scale", ctypes.c_float), ("window", _i32),
                 ("q_pos0", _i64), ("k_pos0", _i64),
                 ("r0", Region), ("r1", Region),
-                ("r1_index", _c_void_p), ("r1_k", _i32), ("reserved", _i32)]
+                ("r1_index", _c_void_p), ("r1_k", _i32), ("kv_format", _i32)]
 
 
 EXPORTS = ("ds4attn_pad", "ds4attn_blockmap", "ds4attn_blockmap_dims", "ds4attn_decode",
-           "ds4attn_prefill", "ds4attn_prefill_bq", "ds4attn_topk", "ds4attn_status_string")
+           "ds4attn_prefill", "ds4attn_prefill_bq", "ds4attn_topk", "ds4attn_quantize_fp8",
+           "ds4attn_status_string")
 
 _lib = None
 
@@ -66,8 +69,10 @@ def lib() -> ctypes.CDLL:
             getattr(h, name).argtypes = [ctypes.POINTER(Args), _c_void_p, _c_void_p, _i32,
                                          _c_void_p, _c_void_p]
         h.ds4attn_topk.argtypes = [_c_void_p, _i64, _i32, _i64, _i32, _c_void_p, _i64, _c_void_p]
+        h.ds4attn_quantize_fp8.argtypes = [_c_void_p, _i32, _i32, _i32, _i32, _i64, _i64, _c_void_p,
+                                           _i64, _i64, _c_void_p, _i64, _c_void_p]
         for name in ("ds4attn_pad", "ds4attn_blockmap", "ds4attn_blockmap_dims", "ds4attn_decode",
-                     "ds4attn_prefill", "ds4attn_prefill_bq", "ds4attn_topk"):
+                     "ds4attn_prefill", "ds4attn_prefill_bq", "ds4attn_topk", "ds4attn_quantize_fp8"):
             getattr(h, name).restype = _i32
         h.ds4attn_status_string.argtypes = [_i32]
         h.ds4attn_status_string.restype = ctypes.c_char_p
@@ -99,15 +104,24 @@ def _dtype_code(dt: torch.dtype) -> int:
         return F16
     if dt == torch.float32:
         return F32
+    if dt == torch.uint8:      # E4M3 codes
+        return E4M3
     raise ValueError(f"unsupported element type {dt}")
 
 
 # --------------------------------------------------------------------------- marshalling
 
 def region(k: Optional[torch.Tensor] = None, v: Optional[torch.Tensor] = None, n_rows: int = 0,
-           valid: Optional[torch.Tensor] = None) -> Region:
-    """A ``Region`` over [B, N, D] K/V tensors (rows contiguous) and optional uint8 [B, N] validity."""
+           valid: Optional[torch.Tensor] = None, k_scale: Optional[torch.Tensor] = None,
+           v_scale: Optional[torch.Tensor] = None) -> Region:
+    """A ``Region`` over [B, N, D] K/V tensors (rows contiguous) and optional uint8 [B, N]
+    validity; for FP8 rows, K/V are uint8 codes and k_scale/v_scale float32 [B, >= N]."""
     r = Region()
+    if k_scale is not None:
+        if v_scale is None or v_scale.stride(0) != k_scale.stride(0) or k_scale.dtype != torch.float32:
+            raise ValueError("FP8 regions take float32 K and V scales with one batch stride")
+        r.k_scale, r.v_scale = k_scale.data_ptr(), v_scale.data_ptr()
+        r.scale_stride_b = k_scale.stride(0) * 4
     r.n_rows = int(n_rows)
     if k is not None:
         es = k.element_size()
@@ -123,9 +137,10 @@ def region(k: Optional[torch.Tensor] = None, v: Optional[torch.Tensor] = None, n
 
 def args(q: torch.Tensor, o: Optional[torch.Tensor], r0: Region, r1: Optional[Region] = None,
          r1_index: Optional[torch.Tensor] = None, scale: float = None, window: int = 0,
-         q_pos0: int = 0, k_pos0: int = 0, flags: int = 0) -> Args:
+         q_pos0: int = 0, k_pos0: int = 0, flags: int = 0, kv_format: int = KV_PLAIN) -> Args:
     """``Args`` for q [B, T, H, D] and float32 o [B, T, H, D] (o may be None for a map)."""
     a = Args()
+    a.kv_format = kv_format
     b, t, h, d = q.shape
     a.batch, a.n_tok, a.n_head, a.head_dim = b, t, h, d
     a.dtype = _dtype_code(q.dtype)
@@ -194,6 +209,32 @@ def topk(scores: torch.Tensor, k: int, stream=None) -> torch.Tensor:
     idx = torch.empty((scores.shape[0], k), dtype=torch.int32, device=scores.device)
     ds4attn_topk(scores, k, idx, stream)
     return idx
+
+
+def ds4attn_quantize_fp8(x: torch.Tensor, codes: torch.Tensor, scales: torch.Tensor, n_rows: int = None,
+                         stream=None) -> None:
+    """FP8 quantize step: x [B, N, D] float16/float32 rows -> uint8 codes [B, N, D] and
+    float32 scales [B, N] (rows contiguous along D)."""
+    b, n, d = x.shape
+    n = n if n_rows is None else int(n_rows)
+    if codes.dtype != torch.uint8 or scales.dtype != torch.float32:
+        raise TypeError("ds4attn_quantize_fp8 writes uint8 codes and float32 scales")
+    if x.stride(2) != 1 or codes.stride(2) != 1 or (n > 1 and scales.stride(1) != 1):
+        raise ValueError("rows must be contiguous along the head dimension")
+    es = x.element_size()
+    _check(lib().ds4attn_quantize_fp8(x.data_ptr(), _dtype_code(x.dtype), b, n, d, x.stride(0) * es,
+                                      x.stride(1) * es, codes.data_ptr(), codes.stride(0),
+                                      codes.stride(1), scales.data_ptr(), scales.stride(0) * 4,
+                                      _stream(stream)), "ds4attn_quantize_fp8")
+
+
+def quantize_fp8(x: torch.Tensor, stream=None):
+    """Allocate (codes, scales) and run ``ds4attn_quantize_fp8``."""
+    b, n, d = x.shape
+    codes = torch.empty((b, n, d), dtype=torch.uint8, device=x.device)
+    scales = torch.empty((b, n), dtype=torch.float32, device=x.device)
+    ds4attn_quantize_fp8(x, codes, scales, stream=stream)
+    return codes, scales
 
 
 def ds4attn_prefill_bq() -> int:

@@ -32,9 +32,11 @@ class DeviceRegion:
     n_rows: int
     valid: Optional[torch.Tensor]      # [B, ceil32(n)] uint8 storage: the caller's bytes in
                                        # [0, n), the tail uninitialised until padded; or None
+    k_scale: Optional[torch.Tensor] = None   # FP8 rows: float32 [B, n] row scales
+    v_scale: Optional[torch.Tensor] = None
 
     def region(self) -> da.Region:
-        return da.region(self.k, self.v, self.n_rows, self.valid)
+        return da.region(self.k, self.v, self.n_rows, self.valid, self.k_scale, self.v_scale)
 
     def pad_in_place(self, stream=None):
         """Stage 1 in place: zero the tail rows and tail validity bytes (nothing is
@@ -58,8 +60,9 @@ class DeviceProblem:
     flags: int = 0
 
     def args(self) -> da.Args:
+        fmt = da.KV_FP8_E4M3 if self.r0.k.dtype == torch.uint8 else da.KV_PLAIN
         return da.args(self.q, self.o, self.r0.region(), None if self.r1 is None else self.r1.region(),
-                       self.idx, self.scale, self.window, self.q_pos0, self.k_pos0, self.flags)
+                       self.idx, self.scale, self.window, self.q_pos0, self.k_pos0, self.flags, fmt)
 
 
 def _region_to_device(r, device) -> Optional[DeviceRegion]:
@@ -75,7 +78,11 @@ def _region_to_device(r, device) -> Optional[DeviceRegion]:
     if r.valid is not None:
         valid = torch.empty((b, cap), dtype=torch.uint8, device=device)
         valid[:, :r.n_rows].copy_(r.valid[:, :r.n_rows])
-    return DeviceRegion(k, v, r.n_rows, valid)
+    ks = vs = None
+    if getattr(r, "k_scale", None) is not None:
+        ks = r.k_scale[:, :r.n_rows].contiguous().to(device)
+        vs = r.v_scale[:, :r.n_rows].contiguous().to(device)
+    return DeviceRegion(k, v, r.n_rows, valid, ks, vs)
 
 
 def to_device(w, device="cuda") -> DeviceProblem:

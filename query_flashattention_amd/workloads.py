@@ -52,19 +52,31 @@ class RegionInputs:
     n_rows: int
     valid: Optional[torch.Tensor] = None
     ring_offset: Optional[torch.Tensor] = None
+    k_scale: Optional[torch.Tensor] = None   # FP8 rows: k/v are uint8 E4M3 codes and these
+    v_scale: Optional[torch.Tensor] = None   # are float32 [B, N] row scales
+
+    def _ring_index(self):
+        n = self.k.shape[1]
+        j = torch.arange(n)
+        return (self.ring_offset.view(-1, 1) + j.view(1, -1)) % n       # [B, N]
 
     def logical(self):
         """(k, v, valid) in logical ring order (identity when not a ring)."""
         if self.ring_offset is None:
             return self.k, self.v, self.valid
-        n = self.k.shape[1]
-        j = torch.arange(n)
-        idx = (self.ring_offset.view(-1, 1) + j.view(1, -1)) % n       # [B, N]
+        idx = self._ring_index()
         gather = idx.unsqueeze(-1).expand(-1, -1, self.k.shape[2])
         k = torch.gather(self.k, 1, gather)
         v = torch.gather(self.v, 1, gather)
         valid = None if self.valid is None else torch.gather(self.valid, 1, idx)
         return k, v, valid
+
+    def logical_scales(self):
+        """(k_scale, v_scale) in logical ring order (FP8 rows)."""
+        if self.ring_offset is None or self.k_scale is None:
+            return self.k_scale, self.v_scale
+        idx = self._ring_index()
+        return torch.gather(self.k_scale, 1, idx), torch.gather(self.v_scale, 1, idx)
 
 
 @dataclass
@@ -204,6 +216,34 @@ def prefill_ratio4(seed: int = 105, tokens: int = PREFILL_CHUNK, start: int = 30
                     r1_index=idx.view(1, tokens, topk))
 
 
+def _fp8_rows(g, shape):
+    """E4M3 codes (uint8, sign and magnitude code drawn uniformly over the finite
+    codes up to 224, subnormals included) and float32 row scales near 2^-7."""
+    mag = torch.randint(0, 0x77, shape, generator=g, dtype=torch.int32)
+    sign = torch.randint(0, 2, shape, generator=g, dtype=torch.int32) * 0x80
+    codes = (mag + sign).to(torch.uint8)
+    scales = torch.exp2(torch.rand(shape[:-1], generator=g) - 7.5).to(torch.float32)
+    return codes, scales
+
+
+def fp8_variant(w: Workload, seed: int) -> Workload:
+    """The same workload (Q, structure, validity, rings, index lists) with its K/V
+    rows drawn as FP8 codes and per-row scales from generator ``seed`` (in the
+    order K0, V0, K1, V1)."""
+    g = torch.Generator().manual_seed(seed)
+
+    def conv(r):
+        if r is None:
+            return None
+        kc, ks = _fp8_rows(g, tuple(r.k.shape))
+        vc, vs = _fp8_rows(g, tuple(r.v.shape))
+        return RegionInputs(kc, vc, r.n_rows, r.valid, r.ring_offset, ks, vs)
+
+    r0, r1 = conv(w.r0), conv(w.r1)
+    return Workload(w.name + "_fp8", seed, w.q, w.scale, r0, window=w.window, q_pos0=w.q_pos0,
+                    k_pos0=w.k_pos0, r1=r1, r1_index=w.r1_index, notes=dict(w.notes, kv="fp8_e4m3"))
+
+
 def named(name: str) -> Workload:
     """The five reference workloads, the batched ratio-128 decode variant and the
     ratio-4 indexed decode."""
@@ -215,6 +255,11 @@ def named(name: str) -> Workload:
         "decode_r4": decode_ratio4,
         "prefill_swa": prefill_raw_swa,
         "prefill_r4": prefill_ratio4,
+        # FP8 rows (E4M3 codes, per-row scales) on the same structures
+        "decode_swa_fp8": lambda: fp8_variant(decode_raw_swa(), 107),
+        "decode_r4_fp8": lambda: fp8_variant(decode_ratio4(), 108),
+        "decode_r128_fp8": lambda: fp8_variant(decode_ratio128(batch=64), 109),
+        "prefill_r4_fp8": lambda: fp8_variant(prefill_ratio4(), 110),
     }
     return table[name]()
 

@@ -205,6 +205,84 @@ def test_topk_rejects_bad_arguments():
     assert lib.ds4attn_topk(FAKE, 0, 100, 400, 8, out, 32, None) == da.OK
 
 
+def _fp8_args(**kw):
+    a = _good_args(**kw)
+    a.kv_format = da.KV_FP8_E4M3
+    a.r0.stride_row = 512
+    a.r0.stride_b = 128 * 512
+    a.r0.k_scale = a.r0.v_scale = FAKE + (1 << 24)
+    a.r0.scale_stride_b = 4 * 128
+    return a
+
+
+@pytest.mark.parametrize("mutate,expect", [
+    (lambda a: setattr(a, "kv_format", 5), da.E_INVAL),
+    (lambda a: setattr(a.r0, "k_scale", None), da.E_INVAL),
+    (lambda a: setattr(a.r0, "v_scale", FAKE + 2), da.E_INVAL),          # misaligned
+    (lambda a: setattr(a.r0, "scale_stride_b", 6), da.E_INVAL),
+    (lambda a: (setattr(a, "batch", 2), setattr(a.r0, "scale_stride_b", 4 * 127)), da.E_INVAL),
+    (lambda a: setattr(a.r0, "stride_row", 496), da.E_INVAL),            # shorter than a row
+    (lambda a: setattr(a, "n_head", 8), da.E_UNSUPPORTED),               # no matrix-core kernel
+    (lambda a: setattr(a, "flags", da.FLAG_GENERIC), da.E_UNSUPPORTED),
+])
+def test_fp8_attention_rejects_bad_arguments(mutate, expect):
+    a = _fp8_args()
+    mutate(a)
+    assert _decode(a) == expect
+
+
+def test_fp8_attention_needs_float16_queries():
+    assert _decode(_fp8_args(dtype=da.F32)) == da.E_UNSUPPORTED
+
+
+def test_fp8_attention_with_empty_regions_needs_no_scales():
+    a = _fp8_args()
+    a.batch = 0
+    a.r0.k_scale = None
+    assert _decode(a, q=None, o=None) == da.OK
+
+
+def test_quantize_rejects_bad_arguments():
+    lib = da.lib()
+    x, c, s = FAKE, FAKE + (1 << 26), FAKE + (1 << 27)
+
+    def q(**kw):
+        p = dict(x=x, dtype=da.F16, batch=2, n=10, d=512, xsb=10 * 1024, xsr=1024, c=c, csb=10 * 512,
+                 csr=512, s=s, ssb=40)
+        p.update(kw)
+        return lib.ds4attn_quantize_fp8(p["x"], p["dtype"], p["batch"], p["n"], p["d"], p["xsb"],
+                                        p["xsr"], p["c"], p["csb"], p["csr"], p["s"], p["ssb"], None)
+
+    assert q(dtype=da.E4M3) == da.E_INVAL
+    assert q(d=96) == da.E_UNSUPPORTED
+    assert q(d=-1) == da.E_INVAL
+    assert q(batch=-1) == da.E_INVAL
+    assert q(x=FAKE + 8) == da.E_INVAL
+    assert q(s=s + 2) == da.E_INVAL
+    assert q(xsr=1000) == da.E_INVAL
+    assert q(xsr=512) == da.E_INVAL                  # rows overlap
+    assert q(csr=496) == da.E_INVAL
+    assert q(ssb=36) == da.E_INVAL                   # fewer scales than rows
+    assert q(c=x + 4096) == da.E_INVAL               # codes overlap the input
+    assert q(s=c + 64) == da.E_INVAL                 # scales overlap the codes
+    assert q(x=None) == da.E_INVAL
+    assert q(n=0) == da.OK                           # nothing to do, nothing launched
+    assert q(batch=0, x=None, c=None, s=None) == da.OK
+
+
+def test_pad_accepts_fp8_rows():
+    """E4M3 rows are 1-byte elements: a 512-dim row is 512 bytes; a region that
+    fills whole blocks in place launches nothing."""
+    lib = da.lib()
+    r = da.Region()
+    r.k, r.v = FAKE, FAKE + (1 << 24)
+    r.n_rows, r.stride_row, r.stride_b = 64, 512, 64 * 512
+    assert lib.ds4attn_pad(ctypes.byref(r), 2, 512, da.E4M3, r.k, r.v, r.stride_b, r.stride_row,
+                           None, 0, None) == da.OK
+    assert lib.ds4attn_pad(ctypes.byref(r), 2, 512, 3, r.k, r.v, r.stride_b, r.stride_row,
+                           None, 0, None) == da.E_INVAL
+
+
 def test_status_strings_and_tile():
     assert da.status_string(da.OK) == "ok"
     assert "invalid" in da.status_string(da.E_INVAL)

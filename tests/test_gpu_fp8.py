@@ -1,0 +1,210 @@
+"""GPU parity of the FP8 KV rows: the quantize step (``ds4attn_quantize_fp8``)
+bit-exact against ``oracle.fp8.quantize_rows``, and the attention on E4M3 rows
+with per-row scales against the float64 oracle run on the dequantized rows
+(``oracle.fp8.dequantize_rows``), within the attention tolerance (max-abs 1e-2,
+mean-abs 1e-3).
+
+Covered: the quantizer on float16 and float32 rows of every supported head dim,
+rows of zeros, negative zeros, tiny and huge magnitudes, constant rows, strided
+rows; attention on the decode workloads with FP8 rows at full size (ring
+window, ratio-128 with a partly valid tail, ratio-4 indexed), the ratio-4
+prefill chunk on sampled tokens, general ragged cases through both kernels
+(validity masks whose hidden rows hold NaN codes and NaN scales, windows, index
+lists with unused entries, two regions), and the chain quantize -> attention.
+"""
+
+import dataclasses
+import zlib
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import fp8 as ofp8
+from oracle import reference as ref
+from query_flashattention_amd import ds4attn as da
+from query_flashattention_amd import pipeline, workloads as wl
+
+pytestmark = pytest.mark.gpu
+
+MAX_ABS, MEAN_ABS = 1e-2, 1e-3
+DEV = "cuda:0"
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _need_gpu():
+    if not torch.cuda.is_available():
+        pytest.fail("GPU tests need an MI355X; none is visible")
+    da.lib()  # fail loudly if the HIP library is missing
+
+
+def _compare(out, want, label):
+    err = np.abs(np.asarray(out, dtype=np.float64) - want)
+    mx, mean = float(err.max()) if err.size else 0.0, float(err.mean()) if err.size else 0.0
+    print(f"{label}: max abs {mx:.3e} mean abs {mean:.3e} over {err.size} values")
+    assert np.isfinite(out).all(), label
+    assert mx <= MAX_ABS and mean <= MEAN_ABS, (label, mx, mean)
+
+
+def _oracle_problem(w) -> ref.Problem:
+    """The oracle's view of an FP8 workload: rows dequantized in float64 (logical ring order)."""
+
+    def region(r):
+        if r is None:
+            return None
+        k, v, valid = r.logical()
+        ks, vs = r.logical_scales()
+        return ref.Region(ofp8.dequantize_rows(k.numpy(), ks.numpy()),
+                          ofp8.dequantize_rows(v.numpy(), vs.numpy()), int(r.n_rows),
+                          None if valid is None else valid.numpy())
+
+    idx = None if w.r1_index is None else w.r1_index.numpy()
+    return ref.Problem(q=w.q.numpy(), scale=float(w.scale), r0=region(w.r0), window=int(w.window),
+                       q_pos0=int(w.q_pos0), k_pos0=int(w.k_pos0), r1=region(w.r1), r1_index=idx)
+
+
+def _run(w, entry, bq):
+    dp = pipeline.to_device(w, DEV)
+    out = pipeline.step(dp, entry, bq)
+    torch.cuda.synchronize()
+    return out.cpu().double().numpy()
+
+
+# --------------------------------------------------------------------------- quantize
+
+def _quant_rows(seed, b, n, d, dtype):
+    g = torch.Generator().manual_seed(seed)
+    x = torch.randn(b, n, d, generator=g) * torch.exp2(torch.randint(-12, 12, (b, n, 1), generator=g).float())
+    x[0, 0] = 0.0
+    if n > 1:
+        x[0, 1] = -0.0
+    if n > 2:
+        x[0, 2] = 3.0                                  # constant row
+    if n > 3:
+        x[0, 3] *= 1e-6                                # tiny
+    if n > 4 and dtype == torch.float32:
+        x[0, 4] *= 1e25                                # huge (float32 only)
+    if n > 5:
+        x[0, 5, ::3] = -0.0                            # signed zeros inside a row
+    return x.to(dtype)
+
+
+@pytest.mark.parametrize("dtype", [torch.float16, torch.float32], ids=["f16", "f32"])
+@pytest.mark.parametrize("d", [64, 128, 256, 512])
+def test_quantize_matches_oracle(dtype, d):
+    x = _quant_rows(300 + d, 3, 77, d, dtype)
+    codes, scales = da.quantize_fp8(x.to(DEV))
+    torch.cuda.synchronize()
+    want_c, want_s = ofp8.quantize_rows(x.numpy())
+    assert np.array_equal(scales.cpu().numpy().view(np.uint32), want_s.view(np.uint32))
+    got_c = codes.cpu().numpy()
+    bad = np.argwhere(got_c != want_c)
+    assert bad.size == 0, (bad[:5].tolist(), got_c[tuple(bad[0])], want_c[tuple(bad[0])])
+
+
+def test_quantize_strided_rows():
+    """Rows inside wider buffers; the bytes around the outputs stay untouched."""
+    x = _quant_rows(310, 2, 33, 512, torch.float16)
+    wide = torch.zeros(2, 40, 640, dtype=torch.float16)
+    wide[:, 3:36, 64:576] = x
+    xd = wide.to(DEV)[:, 3:36, 64:576]
+    codes = torch.full((2, 50, 544), 0xAB, dtype=torch.uint8, device=DEV)
+    scales = torch.full((2, 64), 7.0, dtype=torch.float32, device=DEV)
+    da.ds4attn_quantize_fp8(xd, codes[:, 5:38, 16:528], scales[:, 10:43])
+    torch.cuda.synchronize()
+    want_c, want_s = ofp8.quantize_rows(x.numpy())
+    c, s = codes.cpu().numpy(), scales.cpu().numpy()
+    assert np.array_equal(c[:, 5:38, 16:528], want_c)
+    assert np.array_equal(s[:, 10:43], want_s)
+    c[:, 5:38, 16:528] = 0xAB
+    s[:, 10:43] = 7.0
+    assert (c == 0xAB).all() and (s == 7.0).all()
+
+
+# --------------------------------------------------------------------------- attention on FP8 rows
+
+@pytest.mark.parametrize("name", ["decode_swa_fp8", "decode_r128_fp8"])
+def test_attention_fp8_decode_full(name):
+    w = wl.named(name)
+    out = _run(w, "decode", 1)
+    _compare(out, ref.attention(_oracle_problem(w)), name)
+
+
+def test_attention_fp8_decode_ratio4_sampled():
+    w = wl.named("decode_r4_fp8")
+    out = _run(w, "decode", 1)
+    seqs = [0, 1, 17, 31, 32, 50, 62, 63]
+    want = ref.attention(_oracle_problem(w), tokens=[(b, 0) for b in seqs])
+    _compare(out[seqs, 0], want, "decode_r4_fp8 sampled")
+
+
+def test_attention_fp8_prefill_ratio4_sampled():
+    w = wl.named("prefill_r4_fp8")
+    out = _run(w, "prefill", da.ds4attn_prefill_bq())
+    toks = [0, 1, 31, 32, 127, 128, 129, 700, 1023, 1024, 1500, 2046, 2047]
+    want = ref.attention(_oracle_problem(w), tokens=[(0, t) for t in toks])
+    _compare(out[0, toks], want, "prefill_r4_fp8 sampled")
+
+
+FP8_CASES = [
+    ("f8_h16_ragged", dict(batch=3, tokens=2, heads=16, head_dim=512, n0=77), "decode", 1),
+    ("f8_h32_window", dict(batch=1, tokens=40, heads=32, head_dim=512, n0=100, window=24,
+                           q_pos0=60, k_pos0=0), "prefill", 16),
+    ("f8_h48_valid", dict(batch=2, tokens=3, heads=48, head_dim=512, n0=90, valid0_frac=0.5),
+     "prefill", 1),
+    ("f8_h64_two_regions", dict(batch=2, tokens=2, heads=64, head_dim=512, n0=128, n1=150,
+                                r1_mode="all", valid1_frac=0.8), "decode", 1),
+    ("f8_h64_index", dict(batch=1, tokens=6, heads=64, head_dim=512, n0=70, window=32, q_pos0=60,
+                          k_pos0=0, n1=300, r1_mode="index", r1_k=100, idx_invalid_frac=0.1),
+     "prefill", 16),
+    ("f8_h64_decode_index_valid", dict(batch=2, tokens=1, heads=64, head_dim=512, n0=33, n1=64,
+                                       r1_mode="index", r1_k=64, valid1_frac=0.6), "decode", 1),
+    ("f8_masked_tokens", dict(batch=1, tokens=5, heads=16, head_dim=512, n0=40, window=4, q_pos0=0,
+                              k_pos0=3), "prefill", 2),
+]
+
+
+def _poison_hidden_rows(w):
+    """Rows a validity mask hides hold NaN codes and NaN scales: they must not reach O."""
+    for r in (w.r0, w.r1):
+        if r is None or r.valid is None:
+            continue
+        hidden = r.valid == 0
+        r.k[hidden] = 0x7F
+        r.v[hidden] = 0xFF
+        r.k_scale[hidden] = float("nan")
+        r.v_scale[hidden] = float("nan")
+
+
+@pytest.mark.parametrize("label,kw,entry,bq", FP8_CASES, ids=[c[0] for c in FP8_CASES])
+def test_attention_fp8_random(label, kw, entry, bq):
+    seed = zlib.crc32(label.encode()) % 1000
+    w = wl.fp8_variant(wl.random_problem(seed, **kw), seed + 1)
+    want = ref.attention(_oracle_problem(w))
+    _poison_hidden_rows(w)
+    out = _run(w, entry, bq)
+    _compare(out, want, label)
+    if label == "f8_masked_tokens":
+        assert (out[0, :3] == 0).all()   # tokens 0..2 see no row: exact zeros
+
+
+def test_quantize_then_attend():
+    """float16 K/V -> ds4attn_quantize_fp8 -> decode on the FP8 rows, against the
+    oracle's quantization fed to the oracle's attention."""
+    w = wl.named("decode_swa")
+    dp = pipeline.to_device(w, DEV)
+    r = dp.r0
+    kc, ks = da.quantize_fp8(r.k[:, :r.n_rows])
+    vc, vs = da.quantize_fp8(r.v[:, :r.n_rows])
+    torch.cuda.synchronize()
+    wk, wks = ofp8.quantize_rows(w.r0.k.numpy())
+    wv, wvs = ofp8.quantize_rows(w.r0.v.numpy())
+    assert np.array_equal(kc.cpu().numpy(), wk) and np.array_equal(vc.cpu().numpy(), wv)
+    assert np.array_equal(ks.cpu().numpy(), wks) and np.array_equal(vs.cpu().numpy(), wvs)
+    dp.r0 = pipeline.DeviceRegion(kc, vc, r.n_rows, None, ks, vs)
+    out = pipeline.step(dp, "decode", 1)
+    torch.cuda.synchronize()
+    w8 = dataclasses.replace(w, r0=wl.RegionInputs(torch.from_numpy(wk), torch.from_numpy(wv), w.r0.n_rows,
+                                                   None, w.r0.ring_offset, torch.from_numpy(wks),
+                                                   torch.from_numpy(wvs)))
+    _compare(out.cpu().double().numpy(), ref.attention(_oracle_problem(w8)), "quantize -> decode")
