@@ -49,6 +49,10 @@ DESCRIPTIONS = {
     "prefill_swa": "prefill chunk, raw layer: 2048 tokens x 64 q-heads x d512, causal + 128 window",
     "prefill_r4": "prefill chunk, ratio-4 layer at position 30720: 2048 tokens x 64 q-heads x d512, "
                   "2175 raw rows (causal + 128 window) + top-512 of 7680 compressed rows per token",
+    "decode_swa_fp8": "decode_swa with FP8 K/V rows (E4M3 codes + one float32 scale per row)",
+    "decode_r128_fp8": "decode_r128_b64 with FP8 K/V rows",
+    "decode_r4_fp8": "decode_r4 with FP8 K/V rows",
+    "prefill_r4_fp8": "prefill_r4 with FP8 K/V rows",
 }
 
 
@@ -64,9 +68,12 @@ def counts(w):
     Visible rows per token come from the window interval and the validity
     bytes of the workload (interval arithmetic on the inputs, no attention)."""
     import numpy as np
+    import torch
 
     b, t, h, d = w.q.shape
     es = w.q.element_size()
+    # a K or V row: d elements, or d E4M3 codes plus its float32 scale
+    row_bytes = d + 4 if w.r0.k.dtype == torch.uint8 else d * es
     n0 = w.r0.n_rows
     toks = np.arange(t, dtype=np.int64)
     pairs = 0
@@ -102,11 +109,11 @@ def counts(w):
                 gathered += int(ok.sum())
                 kv_rows += int(np.unique(idx[ok]).size)
     flops = 4.0 * h * d * pairs
-    kv_bytes = 2.0 * d * es * kv_rows
+    kv_bytes = 2.0 * row_bytes * kv_rows
     q_bytes = float(b * t * h * d * es)
     o_bytes = float(b * t * h * d * 4)
     return {"flops": flops, "kv_bytes": kv_bytes, "q_bytes": q_bytes, "o_bytes": o_bytes,
-            "pairs": pairs, "gather_bytes": 2.0 * d * es * gathered}
+            "pairs": pairs, "gather_bytes": 2.0 * row_bytes * gathered}
 
 
 # --------------------------------------------------------------------------- GPU timing
@@ -327,6 +334,41 @@ def topk_timing(rows, n, k, n_sets=4, reps=25):
             "rows_per_s": round(rows / (ms * 1e-3), 1)}
 
 
+def quantize_timing(b, n, d=512, n_sets=4, reps=25):
+    """Mean duration of one ds4attn_quantize_fp8 launch over [b, n, d] float16 rows,
+    with its algorithmic bytes (rows read once; codes and scales written once)."""
+    import torch
+    from query_flashattention_amd import ds4attn as da
+
+    g = torch.Generator().manual_seed(401)
+    xs = [torch.randn(b, n, d, generator=g).half().to("cuda") for _ in range(n_sets)]
+    outs = [(torch.empty(b, n, d, dtype=torch.uint8, device="cuda"),
+             torch.empty(b, n, dtype=torch.float32, device="cuda")) for _ in range(n_sets)]
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        for x, (c, sc) in zip(xs, outs):
+            da.ds4attn_quantize_fp8(x, c, sc)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    gr = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(gr):
+        for x, (c, sc) in zip(xs, outs):
+            da.ds4attn_quantize_fp8(x, c, sc)
+    gr.replay()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        gr.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / (reps * n_sets)
+    nbytes = b * n * (2.0 * d + d + 4)
+    return {"rows": b * n, "head_dim": d, "kernel_us_mean": round(ms * 1e3, 2), "algorithmic_bytes": nbytes,
+            "gbs_kernel": round(nbytes / (ms * 1e-3) / 1e9, 1)}
+
+
 def run_workload(name, steps, warmup, n_sets, launches):
     r = Runner(name, n_sets)
     for k in range(warmup):
@@ -390,7 +432,8 @@ def main():
         roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": round(achieved / HBM_PEAK_GBS, 4),
                 "traffic": traffic_from_profiles(DECODE_KERNEL_SRC) if name == "decode_swa" else None,
-                "kernel": "attn_staged_kernel<1,false> (ds4attn_decode)",
+                "kernel": "attn_staged_kernel<1,%s,%s> (ds4attn_decode)" % (
+                    str(runner.w.r1_index is not None).lower(), str(name.endswith("_fp8")).lower()),
                 "bytes_per_launch": compulsory, "kernel_ms_mean": round(kern["mean"], 5),
                 "kernel_launches_timed": kern["launches"],
                 "single_launch_ms_median": round(kern["single_launch_median"], 5)}
@@ -400,7 +443,9 @@ def main():
         achieved = c["flops"] / kern_s / 1e12
         roof = {"bound": "mfma", "achieved": round(achieved, 2), "peak": MFMA_F16_PEAK_TFLOPS,
                 "unit": "TFLOP/s", "frac": round(achieved / MFMA_F16_PEAK_TFLOPS, 4), "traffic": None,
-                "kernel": "attn_staged_kernel<0,...> (ds4attn_prefill)", "flops_per_launch": c["flops"],
+                "kernel": "attn_staged_kernel<0,%s,%s> (ds4attn_prefill)" % (
+                    str(runner.w.r1_index is not None).lower(), str(name.endswith("_fp8")).lower()),
+                "flops_per_launch": c["flops"],
                 "kernel_ms_mean": round(kern["mean"], 5), "kernel_launches_timed": kern["launches"]}
 
     out = {
@@ -420,7 +465,8 @@ def main():
 
     if not args.no_extra and name == "decode_swa":
         extra = {}
-        for other in ("prefill_swa", "prefill_r4", "decode_r128", "decode_r128_b64", "decode_r4"):
+        for other in ("prefill_swa", "prefill_r4", "decode_r128", "decode_r128_b64", "decode_r4",
+                      "decode_swa_fp8", "decode_r128_fp8", "decode_r4_fp8", "prefill_r4_fp8"):
             sets = 2 if other.startswith("prefill") else (64 if other == "decode_r128" else 20)
             steps = 20 if other.startswith("prefill") else 200
             r, s, k = run_workload(other, steps, 3, sets, 20 if other.startswith("prefill") else 100)
@@ -445,6 +491,8 @@ def main():
         # tokens over 7680 compressed rows, and the decode batch's 64 over 2048
         extra["topk_prefill_r4"] = topk_timing(2048, 7680, 512)
         extra["topk_decode_r4"] = topk_timing(64, 2048, 512)
+        # the FP8 quantize step over a 64-sequence x 2048-row cache of float16 rows
+        extra["quantize_fp8_64x2048"] = quantize_timing(64, 2048)
         out["extra"] = extra
 
     if args.cpu_seconds > 0:

@@ -240,7 +240,10 @@ __global__ __launch_bounds__(256, MODE == kSplitHeads ? 2 : 1) void attn_staged_
   int tok = 0;
   uint32_t toff0 = kOutOfRange, toff1 = kOutOfRange;
   if (tj < p.nbd) row_rule(tj, tid & 31, tok, toff0, toff1);
-  const int tv0 = buf_load_u8(rb0, toff0), tv1 = buf_load_u8(rb1, toff1);
+  // (a region without a validity array needs no load: a load, even out of range,
+  // is a full round trip queued behind the block transfers)
+  const int tv0 = p.valid0 ? buf_load_u8(rb0, toff0) : 0;
+  const int tv1 = p.valid1 ? buf_load_u8(rb1, toff1) : 0;
 
   // Q^T operand fragments: head h, dims d0 + 32ks + 8g .. +7
   half8 qf[NKS];
@@ -303,8 +306,8 @@ __global__ __launch_bounds__(256, MODE == kSplitHeads ? 2 : 1) void attn_staged_
       }
 #pragma unroll
       for (int k = 0; k < K; ++k) {
-        vb0[k] = buf_load_u8(rb0, off0[k]);
-        vb1[k] = buf_load_u8(rb1, off1[k]);
+        vb0[k] = p.valid0 ? buf_load_u8(rb0, off0[k]) : 0;
+        vb1[k] = p.valid1 ? buf_load_u8(rb1, off1[k]) : 0;
       }
 #pragma unroll
       for (int k = 0; k < K; ++k) {
