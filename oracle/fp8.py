@@ -2,9 +2,10 @@
 
 The engine quantizes each new K/V row to FP8 before storing it in the cache, and
 the attention reads the quantized rows ([P-DS4] "Architecture Deep Dive",
-Whole-Model Graph Execution: "FP8 KV quantize -> store raw KV -> attention";
-"GPU Backend Architecture" lists DS4-specific FP8 KV quantization among the GPU
-operations).  The pages do not give the format.  Readings taken (each is listed
+Whole-Model Graph Execution, where the layer schedule puts an FP8 quantize step
+between the Q/KV projections and the raw KV store; "GPU Backend Architecture"
+counts an FP8 KV quantization among the GPU operations).  The pages do not give
+the format.  Readings taken (each is listed
 in DESIGN.md):
 
 * element format: OCP FP8 E4M3 ("e4m3fn"): 1 sign, 4 exponent bits (bias 7), 3
