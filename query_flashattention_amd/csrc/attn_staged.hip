@@ -54,7 +54,8 @@ __global__ __launch_bounds__(256, MODE == kSplitHeads ? 2 : 1) void attn_staged_
   // Tile buffers: DIMS double-buffers (block i+1 and i+2 in flight while block i
   // is consumed); HEADS keeps one block so that two workgroups share a CU and one
   // computes while the other's transfers are in flight.
-  constexpr int NBUF = MODE == kSplitHeads ? 1 : 2;
+  // (FP8 tiles are half the size: DIMS keeps four blocks in flight)
+  constexpr int NBUF = MODE == kSplitHeads ? 1 : (FP8 ? 4 : 2);
   constexpr int KPD = 2;   // K operand reads in flight (k-steps)
   constexpr int VPD = 4;   // V operand reads in flight (output tiles)
   const int tid = threadIdx.x;
@@ -76,10 +77,13 @@ __global__ __launch_bounds__(256, MODE == kSplitHeads ? 2 : 1) void attn_staged_
 
   // Two tile buffers as separate LDS objects (FP8: codes, plus the blocks' row scales).
   constexpr int KT = FP8 ? kF8Tile : kKTile, VT = FP8 ? kF8Tile : kVTile;
-  __shared__ __attribute__((aligned(16))) char kt0[KT], kt1[NBUF == 2 ? KT : 16];
-  __shared__ __attribute__((aligned(16))) char vt0[VT], vt1[NBUF == 2 ? VT : 16];
+  __shared__ __attribute__((aligned(16))) char kt0[KT], kt1[NBUF >= 2 ? KT : 16];
+  __shared__ __attribute__((aligned(16))) char kt2[NBUF >= 4 ? KT : 16], kt3[NBUF >= 4 ? KT : 16];
+  __shared__ __attribute__((aligned(16))) char vt0[VT], vt1[NBUF >= 2 ? VT : 16];
+  __shared__ __attribute__((aligned(16))) char vt2[NBUF >= 4 ? VT : 16], vt3[NBUF >= 4 ? VT : 16];
   // scales of block rows 8w'..8w'+7: K at [16w' + q], V at [16w' + 8 + q]
-  __shared__ __attribute__((aligned(16))) float sc0[FP8 ? 64 : 4], sc1[FP8 && NBUF == 2 ? 64 : 4];
+  __shared__ __attribute__((aligned(16))) float sc0[FP8 ? 64 : 4], sc1[FP8 && NBUF >= 2 ? 64 : 4];
+  __shared__ __attribute__((aligned(16))) float sc2[FP8 && NBUF >= 4 ? 64 : 4], sc3[FP8 && NBUF >= 4 ? 64 : 4];
   __shared__ floatx4 xs[MODE == kSplitDims ? 4 * 2 * 64 : 1];   // partial S^T exchange
   __shared__ uint16_t blist[kListCap];
   __shared__ int cnt[4];
@@ -89,9 +93,27 @@ __global__ __launch_bounds__(256, MODE == kSplitHeads ? 2 : 1) void attn_staged_
 
   // Tile buffer pair 0 or 1, chosen at compile time so the compiler can tell the
   // transfers into one pair from the reads of the other.
-  auto ktile = [&](auto buf) -> char * { return decltype(buf)::value ? kt1 : kt0; };
-  auto vtile = [&](auto buf) -> char * { return decltype(buf)::value ? vt1 : vt0; };
-  auto stile = [&](auto buf) -> float * { return decltype(buf)::value ? sc1 : sc0; };
+  auto ktile = [&](auto buf) -> char * {
+    constexpr int B = decltype(buf)::value;
+    return B == 0 ? kt0 : (B == 1 ? kt1 : (B == 2 ? kt2 : kt3));
+  };
+  auto vtile = [&](auto buf) -> char * {
+    constexpr int B = decltype(buf)::value;
+    return B == 0 ? vt0 : (B == 1 ? vt1 : (B == 2 ? vt2 : vt3));
+  };
+  auto stile = [&](auto buf) -> float * {
+    constexpr int B = decltype(buf)::value;
+    return B == 0 ? sc0 : (B == 1 ? sc1 : (B == 2 ? sc2 : sc3));
+  };
+  // f(Buf<0>), ..., f(Buf<NBUF-1>) with compile-time buffer indices
+  auto for_bufs = [&](auto f) __attribute__((always_inline)) {
+    f(std::integral_constant<int, 0>{});
+    if constexpr (NBUF >= 2) f(std::integral_constant<int, 1>{});
+    if constexpr (NBUF >= 4) {
+      f(std::integral_constant<int, 2>{});
+      f(std::integral_constant<int, 3>{});
+    }
+  };
 
   // Start the transfers of key block j (uniform) into buffer pair `buf`: wave w
   // moves rows 8w..8w+7 of K and of V, one 1 KiB row per instruction, kStageOps
@@ -125,34 +147,37 @@ __global__ __launch_bounds__(256, MODE == kSplitHeads ? 2 : 1) void attn_staged_
       }
     }
     if constexpr (FP8) {
-      // pair pp = rows 2pp, 2pp+1 of the wave's eight: lane i moves 16 bytes of
-      // row (i & 1) from byte 16 * (i >> 1).  Each lane resolves its own row (a
-      // gathered entry is read from the list; unused entries read row 0, masked).
-      const int hsel = lane & 1;
-      const int64_t chunk = 16 * (lane >> 1);
-      auto lane_row = [&](int q) -> int {
-        int row = base + 8 * w + q;
+      // wave w moves pairs 4w..4w+3: lanes 0-31 the pair's first row, lanes 32-63
+      // its second, 16 bytes each.  Each lane resolves its own row (a gathered entry
+      // is read from the list; unused entries read row 0, masked).
+      auto lane_row = [&](int rr) -> int {
+        int row = base + rr;
         if (INDEXED && j >= p.nb0) {
           const int c = idx_s[row];
           row = (c >= 0 && c < p.n1) ? c : 0;
         }
         return row;
       };
+      const int half = lane >> 5;
+      const int64_t chunk = 16 * (lane & 31);
 #pragma unroll
       for (int pp = 0; pp < 4; ++pp) {
-        const int q = 2 * pp + hsel;
-        const int row = lane_row(q);
-        const bool shown = (vm >> (8 * w + q)) & 1u;
-        const uint32_t off = (uint32_t)f8_pair_off(4 * w + pp);
+        const int pr = 4 * w + pp;
+        const int rr = half ? f8_second_row(pr) : pr;
+        const int row = lane_row(rr);
+        const bool shown = (vm >> rr) & 1u;
+        const uint32_t off = (uint32_t)(pr * kF8Pair);
         dma16_lanes(shown ? kb + row * sr + chunk : kZeroRow + chunk, kbase + off);
         dma16_lanes(shown ? vb + row * sr + chunk : kZeroRow + chunk, vbase + off);
       }
-      // lanes 0-7: K scales of the eight rows, lanes 8-15: V scales (rows past the
-      // region's live rows have none and read zero)
+      // the eight rows' scales: lanes 0-3 K of the pairs' first rows, 4-7 K of their
+      // second rows, 8-11 and 12-15 the same for V (rows past the region's live
+      // rows have none and read zero)
       if (lane < 16) {
-        const int q = lane & 7;
-        const int row = lane_row(q);
-        const bool shown = ((vm >> (8 * w + q)) & 1u) && row < nlive;
+        const int pr = 4 * w + (lane & 3);
+        const int rr = (lane & 4) ? f8_second_row(pr) : pr;
+        const int row = lane_row(rr);
+        const bool shown = ((vm >> rr) & 1u) && row < nlive;
         dma4_lanes(shown ? (lane < 8 ? ksb : vsb) + 4 * (int64_t)row : kZeroRow,
                    lds_addr(stile(buf)) + 64u * w);
       }
@@ -183,28 +208,21 @@ __global__ __launch_bounds__(256, MODE == kSplitHeads ? 2 : 1) void attn_staged_
       }
     }
   };
-  using Pair0 = std::integral_constant<int, 0>;
-  using Pair1 = std::integral_constant<int, 1>;
   using Masked = std::integral_constant<bool, true>;
   using Unmasked = std::integral_constant<bool, false>;
 
-  // The first two list entries are guessed before the map row arrives, and their
+  // The first NBUF list entries are guessed before the map row arrives, and their
   // transfers start at once: without a map (or for the token's own tile) the list
   // starts at the first block the window reaches.  A wrong guess is redone below.
-  int spec0 = -1, spec1 = -1;
-  {
-    int jlo = 0;
-    if (p.blk && p.window > 0) {
-      const int64_t lo = p.qk_delta + (int64_t)(t / p.bq) * p.bq - p.window + 1;   // tile's first row
-      jlo = lo <= 0 ? 0 : (int)(lo / kRowsPerBlock < p.nb0 ? lo / kRowsPerBlock : p.nb0);
-    }
-    if (jlo < p.nbd) spec0 = jlo;
-    if (NBUF == 2 && jlo + 1 < p.nbd) spec1 = jlo + 1;
+  int jlo = 0;
+  if (p.blk && p.window > 0) {
+    const int64_t lo = p.qk_delta + (int64_t)(t / p.bq) * p.bq - p.window + 1;   // tile's first row
+    jlo = lo <= 0 ? 0 : (int)(lo / kRowsPerBlock < p.nb0 ? lo / kRowsPerBlock : p.nb0);
   }
-  if (spec0 >= 0) stage_rows(spec0, 0xffffffffu, Pair0{});
-  if constexpr (NBUF == 2) {
-    if (spec1 >= 0) stage_rows(spec1, 0xffffffffu, Pair1{});
-  }
+  auto spec = [&](int e) -> int { return jlo + e < p.nbd ? jlo + e : -1; };   // guess for entry e
+  for_bufs([&](auto E) {
+    if (spec(E) >= 0) stage_rows(spec(E), 0xffffffffu, E);
+  });
 
   // validity arrays of this sequence (size 0 when absent: every load out of range)
   const rsrc_t rb0 = make_rsrc(p.valid0 + (int64_t)b * p.valid0_sb, p.valid0 ? (uint32_t)p.n0 : 0u);
@@ -336,17 +354,26 @@ __global__ __launch_bounds__(256, MODE == kSplitHeads ? 2 : 1) void attn_staged_
   // 8w..8w+7 (its own completed transfers wrote them).
   auto clear_masked = [&](int i, auto buf) __attribute__((always_inline)) {
     if (i >= nlist) return;
-    uint32_t hidden = (~vmask[i & (kMaskRing - 1)] >> (8 * w)) & 0xffu;
+    const uint32_t vmi = vmask[i & (kMaskRing - 1)];
     char *vt = vtile(buf);
-    while (hidden) {
-      const int rr = 8 * w + __ffs(hidden) - 1;
-      hidden &= hidden - 1;
-      if constexpr (FP8) {
-        // the row's 32 chunks of 16 bytes, and its V scale
-        if (lane < 32)
-          *(uint4 *)(vt + f8_pair_off(rr >> 1) + 16 * (rr & 1) + 32 * lane) = make_uint4(0u, 0u, 0u, 0u);
-        if (lane == 0) stile(buf)[16 * w + 8 + (rr & 7)] = 0.f;
-      } else {
+    if constexpr (FP8) {
+      // this wave's rows are the rows of its pairs 4w..4w+3: slot q < 4 the first
+      // row of pair 4w + q, slot q >= 4 the second row of pair 4w + q - 4
+#pragma unroll
+      for (int q = 0; q < 8; ++q) {
+        const int pr = 4 * w + (q & 3);
+        const int rr = q < 4 ? pr : f8_second_row(pr);
+        if (!((vmi >> rr) & 1u)) {
+          // the row's 512 bytes, and its V scale
+          if (lane < 32) *(uint4 *)(vt + f8_row_off(rr) + 16 * lane) = make_uint4(0u, 0u, 0u, 0u);
+          if (lane == 0) stile(buf)[16 * w + 8 + q] = 0.f;
+        }
+      }
+    } else {
+      uint32_t hidden = (~vmi >> (8 * w)) & 0xffu;
+      while (hidden) {
+        const int rr = 8 * w + __ffs(hidden) - 1;
+        hidden &= hidden - 1;
         *(uint4 *)(vt + rr * kVRow + 16 * lane) = make_uint4(0u, 0u, 0u, 0u);
       }
     }
@@ -363,32 +390,33 @@ __global__ __launch_bounds__(256, MODE == kSplitHeads ? 2 : 1) void attn_staged_
   const int tr_e = (lane >> 2) & 3, tr_a = lane & 3;
   const int tr_r0 = 4 * g + tr_e;   // slot rows 0-3 of group g; rows 16 + ... for slots 4-7
 
-  // Pipeline: blocks i+1 and i+2 are in flight while block i is consumed.
-  //   prologue: entries 0 -> pair 0 and 1 -> pair 1 unmasked (already in flight
-  //             when guessed right), meanwhile compute the masks of the first
-  //             entries; clear the hidden rows of 0 and 1
-  //   block i (pair B): consume from B; barrier (B free); stage i+2 -> B masked;
-  //                     wait for this wave's transfers of i+1; barrier (publishes i+1)
+  // Pipeline: blocks i+1 .. i+NBUF are in flight while block i is consumed.
+  //   prologue: entry e -> buffer e unmasked for e < NBUF (already in flight when
+  //             guessed right), meanwhile compute the masks of the first entries;
+  //             clear the hidden rows of those entries
+  //   block i (buffer B = i mod NBUF): consume from B; barrier (B free); stage
+  //             i+NBUF -> B masked; wait for this wave's transfers of i+1; barrier
+  //             (publishes i+1)
   {
-    int j0 = -1, j1 = -1, st;
-    if (nlist > 0) entry_at(0, j0, st);
-    if (nlist > 1) entry_at(1, j1, st);
-    j0 = __builtin_amdgcn_readfirstlane(j0);
-    j1 = __builtin_amdgcn_readfirstlane(j1);
-    const bool hit0 = nlist < 1 || j0 == spec0, hit1 = NBUF == 1 || nlist < 2 || j1 == spec1;
-    if (!(hit0 && hit1)) {
+    bool hit[NBUF], all = true;
+    for_bufs([&](auto E) {
+      int j = -1, st;
+      if (nlist > E) entry_at(E, j, st);
+      j = __builtin_amdgcn_readfirstlane(j);
+      hit[E] = nlist <= E || j == spec(E);
+      all = all && hit[E];
+    });
+    if (!all) {
       wait_vmcnt<0>();   // the guessed transfers land before their buffers are refilled
-      if (!hit0) stage(0, Pair0{}, Unmasked{});
-      if constexpr (NBUF == 2) {
-        if (!hit1) stage(1, Pair1{}, Unmasked{});
-      }
+      for_bufs([&](auto E) {
+        if (!hit[E]) stage(E, E, Unmasked{});
+      });
     }
   }
   build_masks(0, nlist < kMaskChunk ? nlist : kMaskChunk, std::integral_constant<int, 8>{});
   wait_vmcnt<0>();
   lds_barrier();   // masks visible
-  clear_masked(0, Pair0{});
-  if constexpr (NBUF == 2) clear_masked(1, Pair1{});
+  for_bufs([&](auto E) { clear_masked(E, E); });
   lds_barrier();   // blocks 0 and 1 ready
 
   auto iteration = [&](int i, auto buf) __attribute__((always_inline)) {
@@ -397,22 +425,22 @@ __global__ __launch_bounds__(256, MODE == kSplitHeads ? 2 : 1) void attn_staged_
     floatx4 s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
     const char *ktc = ktile(buf), *vtc = vtile(buf);
     if constexpr (FP8) {
-      // row c16 (pair c16 / 2) and row 16 + c16, dims d0 + 32ks + 8g .. +7: 8 codes
-      const char *krow0 = ktc + f8_pair_off(c16 >> 1) + 16 * (c16 & 1) + 2 * d0 + 32 * (g >> 1) + 8 * (g & 1);
-      const char *krow1 = krow0 + (f8_pair_off(8) - f8_pair_off(0));
+      // rows c16 and 16 + c16, dims d0 + 32ks + 8g .. +7: 8 codes
+      const char *krow0 = ktc + f8_row_off(c16) + d0 + 8 * g;
+      const char *krow1 = ktc + f8_row_off(16 + c16) + d0 + 8 * g;
       uint2 ka[KPD], kb[KPD];
 #pragma unroll
       for (int u = 0; u < KPD; ++u) {
-        ka[u] = *(const uint2 *)(krow0 + 64 * u);
-        kb[u] = *(const uint2 *)(krow1 + 64 * u);
+        ka[u] = *(const uint2 *)(krow0 + 32 * u);
+        kb[u] = *(const uint2 *)(krow1 + 32 * u);
       }
 #pragma unroll
       for (int ks = 0; ks < NKS; ++ks) {
         s0 = mfma16(e4m3x8_to_half8(ka[ks % KPD]), qf[ks], s0);
         s1 = mfma16(e4m3x8_to_half8(kb[ks % KPD]), qf[ks], s1);
         if (ks + KPD < NKS) {
-          ka[ks % KPD] = *(const uint2 *)(krow0 + 64 * (ks + KPD));
-          kb[ks % KPD] = *(const uint2 *)(krow1 + 64 * (ks + KPD));
+          ka[ks % KPD] = *(const uint2 *)(krow0 + 32 * (ks + KPD));
+          kb[ks % KPD] = *(const uint2 *)(krow1 + 32 * (ks + KPD));
         }
         __builtin_amdgcn_sched_barrier(0);   // keep this order: MFMAs, then the reads they free
       }
@@ -451,10 +479,11 @@ __global__ __launch_bounds__(256, MODE == kSplitHeads ? 2 : 1) void attn_staged_
     // ---- online softmax: this lane holds rows slot_row(g, 0..7) of head h
     float sv[8];
     if constexpr (FP8) {
-      // K row scales of slot rows 4g..4g+3 and 16+4g..16+4g+3
+      // K row scales of slot rows 4g..4g+3 (first rows of wave g's pairs) and
+      // 16+4g..16+4g+3 (second rows of wave (g ^ 2)'s pairs)
       const float *sc = stile(buf);
-      const float4 klo = *(const float4 *)(sc + 16 * (g >> 1) + 4 * (g & 1));
-      const float4 khi = *(const float4 *)(sc + 16 * (2 + (g >> 1)) + 4 * (g & 1));
+      const float4 klo = *(const float4 *)(sc + 16 * g);
+      const float4 khi = *(const float4 *)(sc + 16 * (g ^ 2) + 4);
       const float kq[8] = {klo.x, klo.y, klo.z, klo.w, khi.x, khi.y, khi.z, khi.w};
 #pragma unroll
       for (int i2 = 0; i2 < 4; ++i2) {
@@ -508,16 +537,16 @@ __global__ __launch_bounds__(256, MODE == kSplitHeads ? 2 : 1) void attn_staged_
       const int trk = (lane & 15) >> 1;
       const int trow = trk < 4 ? 4 * g + trk : 16 + 4 * g + (trk - 4);
       const lds_char *vsrc = (const lds_char *)(__attribute__((address_space(3))) const void *)vtc +
-                             f8_pair_off(trow >> 1) + 16 * (trow & 1) + 2 * d0 + 8 * (lane & 1);
+                             f8_row_off(trow) + d0 + 8 * (lane & 1);
       // V row scales of the slot rows, in float16
       const float *sc = stile(buf);
-      const float4 vlo = *(const float4 *)(sc + 16 * (g >> 1) + 8 + 4 * (g & 1));
-      const float4 vhi = *(const float4 *)(sc + 16 * (2 + (g >> 1)) + 8 + 4 * (g & 1));
+      const float4 vlo = *(const float4 *)(sc + 16 * g + 8);
+      const float4 vhi = *(const float4 *)(sc + 16 * (g ^ 2) + 12);
       const half8 vsc = {(_Float16)vlo.x, (_Float16)vlo.y, (_Float16)vlo.z, (_Float16)vlo.w,
                          (_Float16)vhi.x, (_Float16)vhi.y, (_Float16)vhi.z, (_Float16)vhi.w};
       auto vload = [&](int dt) __attribute__((always_inline)) -> uint2 {
         const int2v r = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
-            (__attribute__((address_space(3))) int2v *)(vsrc + 32 * dt));
+            (__attribute__((address_space(3))) int2v *)(vsrc + 16 * dt));
         return make_uint2((uint32_t)r.x, (uint32_t)r.y);
       };
       uint2 vq[VPD];
@@ -563,7 +592,8 @@ __global__ __launch_bounds__(256, MODE == kSplitHeads ? 2 : 1) void attn_staged_
         lds_barrier();
       }
       stage(nx, buf, Masked{});
-      if constexpr (NBUF == 2) wait_vmcnt<FP8 ? kF8StageOps : kStageOps>();   // block i+1 (staged earlier) landed
+      // block i+1 (staged earlier) landed: only the NBUF - 1 newer stages may be in flight
+      if constexpr (NBUF >= 2) wait_vmcnt<(NBUF - 1) * (FP8 ? kF8StageOps : kStageOps)>();
       else wait_vmcnt<0>();
     } else {
       wait_vmcnt<0>();
@@ -571,13 +601,10 @@ __global__ __launch_bounds__(256, MODE == kSplitHeads ? 2 : 1) void attn_staged_
     lds_barrier();   // publishes block i+1
   };
 
-  if constexpr (NBUF == 2) {
-    for (int i = 0; i < nlist; i += 2) {
-      iteration(i, std::integral_constant<int, 0>{});
-      if (i + 1 < nlist) iteration(i + 1, std::integral_constant<int, 1>{});
-    }
-  } else {
-    for (int i = 0; i < nlist; ++i) iteration(i, std::integral_constant<int, 0>{});
+  for (int i = 0; i < nlist; i += NBUF) {
+    for_bufs([&](auto E) {
+      if (i + E < nlist) iteration(i + E, E);
+    });
   }
 
   // ---- epilogue: O = O / l, float32 stores (4 consecutive dims per lane)

@@ -98,14 +98,17 @@ constexpr int kKRow = 1040, kVRow = 1056;
 constexpr int kKTile = 32 * kKRow, kVTile = 32 * kVRow;
 
 // FP8 tiles (512-byte rows of E4M3 codes).  One transfer moves a pair of rows,
-// interleaved in 16-byte chunks: byte 32c + 16h + e of pair p is byte 16c + e of
-// row 2p + h.  Pairs are 1056 bytes apart, pairs 8..15 shifted by 128 more, so
-// that the 8-byte operand reads of one half-wave (K: 16 rows x 2 chunks halves;
-// V transpose reads: rows 0-7 with 16-23, or 8-15 with 24-31) fall on distinct
-// banks.  A stage is 4 K pairs, 4 V pairs and one transfer of 16 scales per wave.
-constexpr int kF8Pair = 1056;
-__host__ __device__ constexpr int f8_pair_off(int p) { return p * kF8Pair + (p >= 8 ? 128 : 0); }
-constexpr int kF8Tile = 16 * kF8Pair + 128;
+// each contiguous (lanes 0-31 the first, 32-63 the second: two contiguous halves
+// cost the transfer path about a third less than rows interleaved in 16-byte
+// chunks).  Pair p holds row p, then row p + 24 (p < 8) or p + 8 (p >= 8); pairs
+// are 1040 bytes apart.  So the 8-byte operand reads of a half-wave touch every
+// pair once and fall on distinct banks: K reads rows 0-15 (or 16-31), the 8-bit
+// transpose reads rows 0-7 with 16-23 (or 8-15 with 24-31).  A stage is 4 pairs
+// of K rows, 4 of V rows and one transfer of 16 scales per wave.
+constexpr int kF8Pair = 1040;
+__host__ __device__ constexpr int f8_second_row(int p) { return p < 8 ? p + 24 : p + 8; }
+__host__ __device__ constexpr int f8_row_off(int r) { return r < 16 ? r * kF8Pair : ((r - 16) ^ 8) * kF8Pair + 512; }
+constexpr int kF8Tile = 16 * kF8Pair;
 constexpr int kF8StageOps = 9;
 
 
