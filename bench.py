@@ -121,7 +121,7 @@ def counts(w):
 class Runner:
     """Resident input sets, graphs of whole steps and timing helpers for one workload."""
 
-    def __init__(self, name, n_sets, device="cuda:0"):
+    def __init__(self, name, n_sets, device="cuda:0", splits=1):
         import torch
         from query_flashattention_amd import ds4attn as da, pipeline, workloads
 
@@ -135,15 +135,24 @@ class Runner:
         for dp in self.sets:
             nt, nb = da.ds4attn_blockmap_dims(dp.args(), self.bq)
             self.blks.append(torch.empty((dp.q.shape[0], nt, nb), dtype=torch.uint8, device=device))
+        # split decode: each token's blocks over `splits` workgroups, partials in a workspace
+        self.splits = splits
+        self.ws = [torch.empty(max(1, da.ds4attn_decode_workspace_bytes(dp.args(), splits)), dtype=torch.uint8,
+                               device=device) for dp in self.sets]
         torch.cuda.synchronize()
 
     def step(self, i):
-        self.pipeline.step(self.sets[i], self.kind, self.bq, self.blks[i])
+        self.pipeline.step(self.sets[i], self.kind, self.bq, self.blks[i], splits=self.splits,
+                           workspace=self.ws[i])
 
     def attention_only(self, i):
         dp = self.sets[i]
-        fn = self.da.ds4attn_decode if self.kind == "decode" else self.da.ds4attn_prefill
         blk = self.blks[i]
+        if self.splits > 1:
+            self.da.ds4attn_decode_split(dp.args(), dp.q, blk if blk.numel() else None, self.bq, dp.o,
+                                         self.splits, self.ws[i])
+            return
+        fn = self.da.ds4attn_decode if self.kind == "decode" else self.da.ds4attn_prefill
         fn(dp.args(), dp.q, blk if blk.numel() else None, self.bq, dp.o)
 
     def capture(self):
@@ -369,8 +378,8 @@ def quantize_timing(b, n, d=512, n_sets=4, reps=25):
             "gbs_kernel": round(nbytes / (ms * 1e-3) / 1e9, 1)}
 
 
-def run_workload(name, steps, warmup, n_sets, launches):
-    r = Runner(name, n_sets)
+def run_workload(name, steps, warmup, n_sets, launches, splits=1):
+    r = Runner(name, n_sets, splits=splits)
     for k in range(warmup):
         r.step(k % n_sets)
     r.capture()
@@ -487,6 +496,16 @@ def main():
             extra[other] = entry
             del r
             torch.cuda.empty_cache()
+        # one sequence of the ratio-128 layer (12 key blocks): each token's blocks over
+        # 4 workgroups per head group, then the combine pass
+        r, s_, k = run_workload("decode_r128", 200, 3, 64, 100, splits=4)
+        extra["decode_r128_split4"] = {"ms_per_step": round(s_ * 1e3 / 200, 5),
+                                        "kernel_ms_mean": round(k["mean"], 5),
+                                        "single_launch_ms_median": round(k["single_launch_median"], 5),
+                                        "kernel_us_mean": round(k["mean"] * 1e3, 2),
+                                        "note": "partial pass + combine pass, both in the timed launches"}
+        del r
+        torch.cuda.empty_cache()
         # top-k index selection feeding the ratio-4 layers: the prefill chunk's 2048
         # tokens over 7680 compressed rows, and the decode batch's 64 over 2048
         extra["topk_prefill_r4"] = topk_timing(2048, 7680, 512)

@@ -227,6 +227,32 @@ int ds4attn_prefill(const ds4attn_args *a, const void *q, const uint8_t *blk, in
 int32_t ds4attn_prefill_bq(void);
 
 /*
+ * ds4attn_decode_split -- ds4attn_decode with each token's key blocks divided over
+ * `splits` workgroups per group of 16 heads, for batches too small to fill the
+ * chip (one sequence of a long-context layer: [P-DS4] "Architecture Deep Dive",
+ * 32K-1M contexts; the fused step of [P-Metal] "FlashAttention Kernel
+ * Architecture" run on parts of the block list).  Each part keeps its own running
+ * maximum, sum and unnormalised output in `workspace`; a second kernel combines
+ * them: O = sum_s 2^(m_s - M) O_s / sum_s 2^(m_s - M) l_s with M = max_s m_s (the
+ * online-softmax rescale, applied once across parts).  The result equals
+ * ds4attn_decode's up to rounding.
+ *   splits     1..64; 1 is ds4attn_decode (no workspace needed)
+ *   workspace  device, 16-byte aligned, at least ds4attn_decode_workspace_bytes
+ *              bytes, not overlapping o; its contents on entry do not matter
+ * Needs the matrix-core case (F16 Q, D = 512, H % 16 == 0, no DS4ATTN_FLAG_GENERIC;
+ * either KV format), else DS4ATTN_E_UNSUPPORTED.
+ * Returns DS4ATTN_OK, DS4ATTN_E_INVAL, DS4ATTN_E_UNSUPPORTED or DS4ATTN_E_HIP.
+ */
+int ds4attn_decode_split(const ds4attn_args *a, const void *q, const uint8_t *blk, int32_t bq,
+                         float *o, int32_t splits, void *workspace, int64_t workspace_bytes,
+                         void *stream);
+
+/* Workspace bytes ds4attn_decode_split needs for *a and `splits` (0 for splits = 1):
+ * B * T * (H / 16) * splits records of 16 * 512 * 4 + 128 bytes.  Host only;
+ * returns DS4ATTN_OK, DS4ATTN_E_INVAL or DS4ATTN_E_UNSUPPORTED (H % 16 != 0). */
+int ds4attn_decode_workspace_bytes(const ds4attn_args *a, int32_t splits, int64_t *bytes);
+
+/*
  * ds4attn_topk -- top-k index selection from given scores: the index list of a
  * ratio-4 layer ([P-DS4] "Architecture Deep Dive", Layer Compression: each token
  * attends the top-512 compressed rows its indexer selects; the scoring itself is

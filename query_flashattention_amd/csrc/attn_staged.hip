@@ -66,7 +66,12 @@ __global__ __launch_bounds__(256, MODE == kSplitHeads ? 2 : 1) void attn_staged_
   const uint32_t lane16 = 16u * lane;   // this lane's byte offset in a transferred row
 
   const int ngroups = p.H / HG;
-  const int64_t L = xcd_remap(blockIdx.x, gridDim.x);
+  // split decode: consecutive workgroups share (token, head group) and take
+  // consecutive parts of its block list
+  const int nsplit = MODE == kSplitDims ? p.nsplit : 1;
+  const int64_t L0 = xcd_remap(blockIdx.x, gridDim.x);
+  const int split = (int)(L0 % nsplit);
+  const int64_t L = L0 / nsplit;
   const int hg = (int)(L % ngroups);
   const int64_t bt = L / ngroups;
   const int t = (int)(bt % p.T);
@@ -219,7 +224,13 @@ __global__ __launch_bounds__(256, MODE == kSplitHeads ? 2 : 1) void attn_staged_
     const int64_t lo = p.qk_delta + (int64_t)(t / p.bq) * p.bq - p.window + 1;   // tile's first row
     jlo = lo <= 0 ? 0 : (int)(lo / kRowsPerBlock < p.nb0 ? lo / kRowsPerBlock : p.nb0);
   }
-  auto spec = [&](int e) -> int { return jlo + e < p.nbd ? jlo + e : -1; };   // guess for entry e
+  // a split's list part starts at its share of the dense blocks from jlo on
+  const int64_t ndguess = p.nbd > jlo ? p.nbd - jlo : 0;
+  const int e0_guess = (int)(ndguess * split / nsplit);
+  const int n_guess = (int)(ndguess * (split + 1) / nsplit) - e0_guess;   // the part's length
+  auto spec = [&](int e) -> int {   // guess for the part's entry e
+    return e < n_guess && jlo + e0_guess + e < p.nbd ? jlo + e0_guess + e : -1;
+  };
   for_bufs([&](auto E) {
     if (spec(E) >= 0) stage_rows(spec(E), 0xffffffffu, E);
   });
@@ -278,6 +289,8 @@ __global__ __launch_bounds__(256, MODE == kSplitHeads ? 2 : 1) void attn_staged_
   const uint8_t *blkrow = p.blk ? p.blk + ((int64_t)b * p.ntiles + t / p.bq) * p.nbd : nullptr;
   const int ndense = build_block_list<256>(blkrow, p.nbd, blist, cnt);   // ends with a barrier
   const int nlist = ndense + (INDEXED ? p.nb1 : 0);
+  // this workgroup's part of the list: entries [e0, e1)
+  const int e0 = (int)((int64_t)nlist * split / nsplit), e1 = (int)((int64_t)nlist * (split + 1) / nsplit);
   {
     const bool vis = tok && (toff0 == kOutOfRange || tv0 != 0) && (toff1 == kOutOfRange || tv1 != 0);
     const uint64_t bal = __ballot(vis);
@@ -353,7 +366,7 @@ __global__ __launch_bounds__(256, MODE == kSplitHeads ? 2 : 1) void attn_staged_
   // Clear the V rows of entry i that its mask hides, among this wave's own rows
   // 8w..8w+7 (its own completed transfers wrote them).
   auto clear_masked = [&](int i, auto buf) __attribute__((always_inline)) {
-    if (i >= nlist) return;
+    if (i >= e1) return;
     const uint32_t vmi = vmask[i & (kMaskRing - 1)];
     char *vt = vtile(buf);
     if constexpr (FP8) {
@@ -401,22 +414,22 @@ __global__ __launch_bounds__(256, MODE == kSplitHeads ? 2 : 1) void attn_staged_
     bool hit[NBUF], all = true;
     for_bufs([&](auto E) {
       int j = -1, st;
-      if (nlist > E) entry_at(E, j, st);
+      if (e1 > e0 + E) entry_at(e0 + E, j, st);
       j = __builtin_amdgcn_readfirstlane(j);
-      hit[E] = nlist <= E || j == spec(E);
+      hit[E] = e1 <= e0 + E || j == spec(E);
       all = all && hit[E];
     });
     if (!all) {
       wait_vmcnt<0>();   // the guessed transfers land before their buffers are refilled
       for_bufs([&](auto E) {
-        if (!hit[E]) stage(E, E, Unmasked{});
+        if (!hit[E]) stage(e0 + E, E, Unmasked{});
       });
     }
   }
-  build_masks(0, nlist < kMaskChunk ? nlist : kMaskChunk, std::integral_constant<int, 8>{});
+  build_masks(e0, e1 - e0 < kMaskChunk ? e1 - e0 : kMaskChunk, std::integral_constant<int, 8>{});
   wait_vmcnt<0>();
   lds_barrier();   // masks visible
-  for_bufs([&](auto E) { clear_masked(E, E); });
+  for_bufs([&](auto E) { clear_masked(e0 + E, E); });
   lds_barrier();   // blocks 0 and 1 ready
 
   auto iteration = [&](int i, auto buf) __attribute__((always_inline)) {
@@ -584,10 +597,10 @@ __global__ __launch_bounds__(256, MODE == kSplitHeads ? 2 : 1) void attn_staged_
 
     lds_barrier();   // every wave is done with buffer B
     const int nx = i + NBUF;   // the entry buffer B takes next
-    if (nx < nlist) {
+    if (nx < e1) {
       if ((nx & (kMaskChunk - 1)) == 0) {
         // next chunk of masks (one batch of loads per 8 entries; drains the transfers)
-        const int n = nlist - nx;
+        const int n = e1 - nx;
         build_masks(nx, n < kMaskChunk ? n : kMaskChunk, std::integral_constant<int, 1>{});
         lds_barrier();
       }
@@ -601,9 +614,9 @@ __global__ __launch_bounds__(256, MODE == kSplitHeads ? 2 : 1) void attn_staged_
     lds_barrier();   // publishes block i+1
   };
 
-  for (int i = 0; i < nlist; i += NBUF) {
+  for (int i = e0; i < e1; i += NBUF) {
     for_bufs([&](auto E) {
-      if (i + E < nlist) iteration(i + E, E);
+      if (i + E < e1) iteration(i + E, E);
     });
   }
 
@@ -611,6 +624,18 @@ __global__ __launch_bounds__(256, MODE == kSplitHeads ? 2 : 1) void attn_staged_
   float lt = l;
   lt = xor_sum(lt, 16);
   lt = xor_sum(lt, 32);
+  if (MODE == kSplitDims && nsplit > 1) {
+    // partial record of this split: unnormalised O, then the maxima and the sums
+    char *rec = p.ws + (L * nsplit + split) * kSplitRecord;
+    float *ob = (float *)rec + c16 * 512 + d0 + 4 * g;
+#pragma unroll
+    for (int dt = 0; dt < NDT; ++dt) *(floatx4 *)(ob + 16 * dt) = o[dt];
+    if (w == 0 && g == 0) {
+      ((float *)(rec + 16 * 512 * 4))[c16] = m;
+      ((float *)(rec + 16 * 512 * 4))[16 + c16] = lt;
+    }
+    return;
+  }
   const float inv = lt > 0.f ? 1.f / lt : 0.f;
   float *ob = (float *)(p.o + b * p.o_sb + t * p.o_st + (int64_t)h * p.o_sh) + d0 + 4 * g;
 #pragma unroll
@@ -620,7 +645,7 @@ __global__ __launch_bounds__(256, MODE == kSplitHeads ? 2 : 1) void attn_staged_
 template <int MODE>
 static hipError_t launch_staged(const AttnParams &p, hipStream_t s) {
   constexpr int HG = MODE == kSplitHeads ? 64 : 16;
-  const int64_t n = (int64_t)p.B * p.T * (p.H / HG);
+  const int64_t n = (int64_t)p.B * p.T * (p.H / HG) * (MODE == kSplitDims ? p.nsplit : 1);
   if (n == 0) return hipSuccess;
   const dim3 grid((unsigned)n), block(256);
   if (p.fp8) {
@@ -636,6 +661,70 @@ static hipError_t launch_staged(const AttnParams &p, hipStream_t s) {
 hipError_t launch_attn_decode(const AttnParams &p, hipStream_t s) {
   return launch_staged<kSplitDims>(p, s);
 }
+// Combine the split partials of one (token, head group): 16 heads x 512 dims over
+// 1024 threads, thread = (head, 8 consecutive dims).  The partials were accumulated
+// against their own running maxima m_s (base 2); with M = max m_s the result is
+// sum_s 2^(m_s - M) O_s / sum_s 2^(m_s - M) l_s, zero when no split saw a row.  The
+// maxima and sums of all parts are staged in LDS first (one load per thread), and
+// the parts' outputs are read eight parts at a time, so the pass costs a few
+// memory round trips whatever the split count.
+__global__ __launch_bounds__(1024) void split_combine_kernel(const AttnParams p) {
+  __shared__ float ml[2][16][kMaxSplits];   // [m | l][head][part]
+  const int ngroups = p.H / 16;
+  const int64_t L = blockIdx.x;
+  const int hg = (int)(L % ngroups);
+  const int64_t bt = L / ngroups;
+  const int t = (int)(bt % p.T), b = (int)(bt / p.T);
+  const int tid = threadIdx.x, hh = tid >> 6, dq = (tid & 63) * 8;
+  const int ns = p.nsplit;
+  const char *rec0 = p.ws + L * ns * kSplitRecord;
+  for (int e = tid; e < 32 * ns; e += 1024) {   // e = part * 32 + (0..15 maxima, 16..31 sums)
+    const int sp = e >> 5, k = e & 31;
+    ml[k >> 4][k & 15][sp] = ((const float *)(rec0 + sp * kSplitRecord + 16 * 512 * 4))[k];
+  }
+  __syncthreads();
+  float mmax = -INFINITY;
+  for (int sp = 0; sp < ns; ++sp) mmax = fmaxf(mmax, ml[0][hh][sp]);
+  floatx4 acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f};
+  float lsum = 0.f;
+  if (mmax != -INFINITY) {
+    for (int s0 = 0; s0 < ns; s0 += 8) {
+      floatx4 v0[8], v1[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        if (s0 + u < ns) {
+          const floatx4 *src = (const floatx4 *)((const float *)(rec0 + (s0 + u) * kSplitRecord) + hh * 512 + dq);
+          v0[u] = src[0];
+          v1[u] = src[1];
+        }
+      }
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        if (s0 + u < ns) {
+          const float ms = ml[0][hh][s0 + u];
+          const float wgt = ms == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(ms - mmax);
+          lsum += wgt * ml[1][hh][s0 + u];
+          acc0 += wgt * v0[u];
+          acc1 += wgt * v1[u];
+        }
+      }
+    }
+  }
+  const float inv = lsum > 0.f ? 1.f / lsum : 0.f;
+  float *ob = (float *)(p.o + b * p.o_sb + t * p.o_st + (int64_t)(hg * 16 + hh) * p.o_sh) + dq;
+  *(floatx4 *)ob = acc0 * inv;
+  *(floatx4 *)(ob + 4) = acc1 * inv;
+}
+
+hipError_t launch_attn_decode_split(const AttnParams &p, hipStream_t s) {
+  hipError_t e = launch_staged<kSplitDims>(p, s);
+  if (e != hipSuccess) return e;
+  const int64_t n = (int64_t)p.B * p.T * (p.H / 16);
+  if (n == 0) return hipSuccess;
+  hipLaunchKernelGGL(split_combine_kernel, dim3((unsigned)n), dim3(1024), 0, s, p);
+  return hipGetLastError();
+}
+
 hipError_t launch_attn_prefill(const AttnParams &p, hipStream_t s) {
   return launch_staged<kSplitHeads>(p, s);
 }

@@ -79,11 +79,21 @@ int resolve_mask(const ds4attn_args *a, int row_bytes, bool need_kv, AttnParams 
   if (P.n1 == 0) P.nb1 = 0;
   else P.nb1 = P.indexed ? (P.r1_k + 31) / 32 : (int)(ceil32(P.n1) / 32);
   P.nbd = P.nb0 + (P.indexed ? 0 : P.nb1);
+  P.nsplit = 1;
   return DS4ATTN_OK;
 }
 
+bool ranges_overlap(const void *a, int64_t alen, const void *b, int64_t blen) {
+  const uintptr_t a0 = (uintptr_t)a, b0 = (uintptr_t)b;
+  return a0 < b0 + (uintptr_t)blen && b0 < a0 + (uintptr_t)alen;
+}
+
+int64_t split_workspace_bytes(const ds4attn_args *a, int32_t splits) {
+  return splits > 1 ? (int64_t)a->batch * a->n_tok * (a->n_head / 16) * splits * kSplitRecord : 0;
+}
+
 int run_attention(const ds4attn_args *a, const void *q, const uint8_t *blk, int32_t bq, float *o,
-                  void *stream, bool prefill) {
+                  void *stream, bool prefill, int32_t splits = 1, void *ws = nullptr, int64_t ws_bytes = 0) {
   if (!a) return DS4ATTN_E_INVAL;
   if (a->dtype != DS4ATTN_F16 && a->dtype != DS4ATTN_F32) return DS4ATTN_E_INVAL;
   if (a->head_dim <= 0) return DS4ATTN_E_INVAL;
@@ -141,16 +151,26 @@ int run_attention(const ds4attn_args *a, const void *q, const uint8_t *blk, int3
                     !(a->flags & DS4ATTN_FLAG_GENERIC) && P.nbd <= kListCap && fits32;
   // FP8 rows are dequantized inside the matrix-core kernels only
   if (fp8 && !mfma) return DS4ATTN_E_UNSUPPORTED;
+  if (splits > 1) {
+    // split decode runs on the matrix-core decode kernel only
+    if (!mfma || prefill) return DS4ATTN_E_UNSUPPORTED;
+    if (work * (a->n_head / 16) * splits > 0x7fffffffLL) return DS4ATTN_E_UNSUPPORTED;
+    const int64_t need = split_workspace_bytes(a, splits);
+    if (!ws || !aligned16(ws) || ws_bytes < need) return DS4ATTN_E_INVAL;
+    const int64_t o_len = (a->batch - 1) * a->o_stride_b + (a->n_tok - 1) * a->o_stride_t +
+                          (a->n_head - 1) * a->o_stride_h + 4LL * a->head_dim;
+    if (ranges_overlap(ws, need, o, o_len)) return DS4ATTN_E_INVAL;
+    P.nsplit = splits;
+    P.ws = (char *)ws;
+    e = launch_attn_decode_split(P, s);
+    return e == hipSuccess ? DS4ATTN_OK : DS4ATTN_E_HIP;
+  }
   if (mfma && prefill && a->n_head % 64 == 0) e = launch_attn_prefill(P, s);
   else if (mfma) e = launch_attn_decode(P, s);
   else e = launch_attn_generic(P, eb, s);
   return e == hipSuccess ? DS4ATTN_OK : DS4ATTN_E_HIP;
 }
 
-bool ranges_overlap(const void *a, int64_t alen, const void *b, int64_t blen) {
-  const uintptr_t a0 = (uintptr_t)a, b0 = (uintptr_t)b;
-  return a0 < b0 + (uintptr_t)blen && b0 < a0 + (uintptr_t)alen;
-}
 
 }  // namespace
 
@@ -245,6 +265,20 @@ int ds4attn_decode(const ds4attn_args *a, const void *q, const uint8_t *blk, int
 int ds4attn_prefill(const ds4attn_args *a, const void *q, const uint8_t *blk, int32_t bq, float *o,
                     void *stream) {
   return run_attention(a, q, blk, bq, o, stream, true);
+}
+
+int ds4attn_decode_workspace_bytes(const ds4attn_args *a, int32_t splits, int64_t *bytes) {
+  if (!a || !bytes || splits < 1 || splits > kMaxSplits) return DS4ATTN_E_INVAL;
+  if (a->batch < 0 || a->n_tok < 0 || a->n_head < 1) return DS4ATTN_E_INVAL;
+  if (splits > 1 && a->n_head % 16) return DS4ATTN_E_UNSUPPORTED;
+  *bytes = split_workspace_bytes(a, splits);
+  return DS4ATTN_OK;
+}
+
+int ds4attn_decode_split(const ds4attn_args *a, const void *q, const uint8_t *blk, int32_t bq, float *o,
+                         int32_t splits, void *workspace, int64_t workspace_bytes, void *stream) {
+  if (splits < 1 || splits > kMaxSplits || workspace_bytes < 0) return DS4ATTN_E_INVAL;
+  return run_attention(a, q, blk, bq, o, stream, false, splits, workspace, workspace_bytes);
 }
 
 int32_t ds4attn_prefill_bq(void) { return 16; }

@@ -46,6 +46,10 @@ struct AttnParams {
   int fp8;
   const char *ks0, *vs0, *ks1, *vs1;   // scales of row r of sequence b at b * s*_sb + 4r
   int64_t s0_sb, s1_sb;
+  // split decode: each token's block list divided over nsplit workgroups per head
+  // group, partial results in ws (one kSplitRecord per (b, t, head group, split))
+  int nsplit;              // 1 = no split
+  char *ws;
   // block map
   const uint8_t *blk;      // [B][ntiles][nbd] or null (every block treated as PARTIAL)
   int bq;
@@ -118,6 +122,12 @@ hipError_t launch_attn_generic(const AttnParams &p, int elem_bytes, hipStream_t 
 // Matrix-core kernels (head dim 512, float16): decode splits a token's heads over
 // workgroups of 16; prefill keeps 64 heads of a token in one workgroup.
 hipError_t launch_attn_decode(const AttnParams &p, hipStream_t s);
+// Split decode: the partial pass (p.nsplit > 1, p.ws set) then the combine pass.
+// A partial record: unnormalised O of 16 heads x 512 dims (float32, head-major),
+// then the 16 running maxima (base-2 scores) and the 16 sums.
+constexpr int kMaxSplits = 64;
+constexpr int64_t kSplitRecord = 16 * 512 * 4 + 16 * 4 * 2;
+hipError_t launch_attn_decode_split(const AttnParams &p, hipStream_t s);
 hipError_t launch_attn_prefill(const AttnParams &p, hipStream_t s);
 // FP8 quantize step: one wave per row of head_dim elements (elem_bytes 2 or 4).
 hipError_t launch_quant_fp8(const void *x, int elem_bytes, int B, int n, int D, int64_t x_sb, int64_t x_sr,

@@ -283,6 +283,37 @@ def test_pad_accepts_fp8_rows():
                            None, 0, None) == da.E_INVAL
 
 
+def test_split_decode_rejects_bad_arguments():
+    lib = da.lib()
+    a = _good_args()
+    need = da.ds4attn_decode_workspace_bytes(a, 4)
+    assert need == 1 * 1 * 4 * 4 * (16 * 512 * 4 + 128)
+    assert da.ds4attn_decode_workspace_bytes(a, 1) == 0
+    ws = FAKE + (1 << 32)
+
+    def split(aa, splits, w=ws, nbytes=need, q=FAKE, o=FAKE):
+        return lib.ds4attn_decode_split(ctypes.byref(aa), q, None, 1, o, splits, w, nbytes, None)
+
+    assert split(a, 0) == da.E_INVAL
+    assert split(a, 65) == da.E_INVAL
+    assert split(a, 4, w=None) == da.E_INVAL
+    assert split(a, 4, nbytes=need - 1) == da.E_INVAL
+    assert split(a, 4, w=ws + 8) == da.E_INVAL                   # misaligned
+    assert split(a, 4, w=FAKE) == da.E_INVAL                     # overlaps o
+    g = _good_args(heads=8)                                      # no matrix-core kernel
+    assert split(g, 4) == da.E_UNSUPPORTED
+    b = _good_args()
+    b.flags = da.FLAG_GENERIC
+    assert split(b, 4) == da.E_UNSUPPORTED
+    e = _good_args()
+    e.batch = 0
+    assert split(e, 4, w=None, nbytes=0, q=None, o=None) == da.OK   # nothing to do
+    n = ctypes.c_int64()
+    assert lib.ds4attn_decode_workspace_bytes(ctypes.byref(_good_args(heads=8)), 2, ctypes.byref(n)) == \
+        da.E_UNSUPPORTED
+    assert lib.ds4attn_decode_workspace_bytes(ctypes.byref(a), 0, ctypes.byref(n)) == da.E_INVAL
+
+
 def test_status_strings_and_tile():
     assert da.status_string(da.OK) == "ok"
     assert "invalid" in da.status_string(da.E_INVAL)

@@ -244,3 +244,66 @@ def test_decode_and_prefill_agree():
     a = _run(w, "decode", 1).double().numpy()
     b = _run(w, "prefill", 1).double().numpy()
     _compare(a, b, "decode vs prefill")
+
+
+# --------------------------------------------------------------------------- split decode
+
+def _run_split(w, splits, use_map=True):
+    dp = pipeline.to_device(w, DEV)
+    if use_map:
+        out = pipeline.step(dp, "decode", 1, splits=splits)
+    else:
+        dp.r0.pad_in_place()
+        if dp.r1 is not None:
+            dp.r1.pad_in_place()
+        a = dp.args()
+        ws = torch.empty(da.ds4attn_decode_workspace_bytes(a, splits), dtype=torch.uint8, device=DEV)
+        da.ds4attn_decode_split(a, dp.q, None, 1, dp.o, splits, ws)
+        out = dp.o
+    torch.cuda.synchronize()
+    return out.cpu()
+
+
+@pytest.mark.parametrize("splits", [2, 3, 12, 64])
+def test_split_decode_ratio128_single_sequence(splits):
+    """The ratio-128 layer at 32K for one sequence (12 key blocks) with its blocks
+    divided over 2, 3, 12 and 64 workgroups per head group (64: most parts empty)."""
+    w = wl.named("decode_r128")
+    out = _run_split(w, splits).double().numpy()
+    _compare(out, ref.attention(ref.from_workload(w)), f"decode_r128 split {splits}")
+
+
+@pytest.mark.parametrize("name,splits", [("decode_swa", 2), ("decode_r4", 5), ("decode_r4_fp8", 3),
+                                          ("decode_r128_fp8", 4)])
+def test_split_decode_batches(name, splits):
+    w = wl.named(name)
+    out = _run_split(w, splits).double().numpy()
+    if name.endswith("_fp8"):
+        plain = _run(w, "decode", 1).double().numpy()
+        _compare(out, plain, f"{name} split {splits} vs unsplit")
+        return
+    seqs = [0, 1, 31, 63]
+    want = ref.attention(ref.from_workload(w), tokens=[(b, 0) for b in seqs])
+    _compare(out[seqs, 0], want, f"{name} split {splits}")
+
+
+SPLIT_CASES = [
+    ("split_ragged_valid", dict(batch=2, tokens=3, heads=16, head_dim=512, n0=150, valid0_frac=0.5), 4),
+    ("split_window_index", dict(batch=1, tokens=4, heads=64, head_dim=512, n0=70, window=32, q_pos0=60,
+                                k_pos0=0, n1=300, r1_mode="index", r1_k=100, idx_invalid_frac=0.1), 6),
+    ("split_masked_tokens", dict(batch=1, tokens=5, heads=16, head_dim=512, n0=40, window=4, q_pos0=0,
+                                 k_pos0=3), 3),
+]
+
+
+@pytest.mark.parametrize("label,kw,splits", SPLIT_CASES, ids=[c[0] for c in SPLIT_CASES])
+def test_split_decode_random(label, kw, splits):
+    w = wl.random_problem(zlib.crc32(label.encode()) % 1000, **kw)
+    want = ref.attention(ref.from_workload(w))
+    with_map = _run_split(w, splits)
+    _compare(with_map.double().numpy(), want, label)
+    # without a map every block is a list entry, so the parts differ: same result up to rounding
+    no_map = _run_split(w, splits, use_map=False)
+    _compare(no_map.double().numpy(), want, label + " no map")
+    if label == "split_masked_tokens":
+        assert (with_map[0, :3] == 0).all()   # tokens 0..2 see no row in any part: exact zeros
