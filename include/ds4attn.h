@@ -80,7 +80,18 @@ enum {
   /* Run the generic vector-ALU kernel even where the matrix-core kernel applies
    * ([P-Metal] "Vector vs Non-Vector Execution Paths": a path that handles any
    * head size).  Results agree within rounding; it exists for cross-checks. */
-  DS4ATTN_FLAG_GENERIC = 1
+  DS4ATTN_FLAG_GENERIC = 1,
+  /* Decode on the matrix-core kernel only, with a chosen split of the work over a
+   * workgroup's four waves (by default the library picks one from the length a
+   * token's block list can reach).  DIMS: the waves share each key block and split
+   * the head dimension.  KEYS: the waves take different 16-row halves of the key
+   * blocks and merge their partial results at the end; float16 rows only
+   * (DS4ATTN_E_UNSUPPORTED for FP8 rows).  Setting both is DS4ATTN_E_INVAL; with
+   * DS4ATTN_FLAG_GENERIC, or where the matrix-core kernel does not apply, either
+   * is DS4ATTN_E_UNSUPPORTED.  Results agree within rounding; they exist for
+   * cross-checks and measurement. */
+  DS4ATTN_FLAG_DECODE_DIMS = 2,
+  DS4ATTN_FLAG_DECODE_KEYS = 4
 };
 
 /* One KV region.  Row r of sequence b starts at  k + b*stride_b + r*stride_row

@@ -33,13 +33,22 @@
 //         16 heads; the four partial score tiles meet in LDS and every wave sums
 //         them in the same order; 4 workgroups per 64-head token fill the chip
 //         for small decode batches.
+//   KEYS  (HG = 16, decode, float16 rows): the waves take different key rows.
+//         Wave w consumes half-blocks (16 rows) w, w+4, w+8, ... of the list for
+//         all 16 heads over the full head dimension, with its own running max,
+//         sum and output; the four partial results are merged in LDS at the end
+//         (the log-sum-exp rule).  Its rows travel global -> registers (one
+//         contiguous 1 KiB row per load, the next half-block's while the current
+//         one is consumed) -> the wave's own K and V tiles, so no wave waits for
+//         another inside the key loop and the vector-memory path stays busy.
 #include "staging.h"
 
+#include <algorithm>
 #include <type_traits>
 
 namespace ds4attn {
 
-enum : int { kSplitHeads = 0, kSplitDims = 1 };
+enum : int { kSplitHeads = 0, kSplitDims = 1, kSplitKeys = 2 };
 
 // FP8 rows (E4M3 codes, a float32 scale per row): the rows travel to LDS as codes
 // (half the bytes), two rows per transfer, and are converted where the operands
@@ -48,16 +57,18 @@ enum : int { kSplitHeads = 0, kSplitDims = 1 };
 // rows' scales in float16.  P and the accumulators are as for float16 rows.
 template <int MODE, bool INDEXED, bool FP8>
 __global__ __launch_bounds__(256, MODE == kSplitHeads ? 2 : 1) void attn_staged_kernel(const AttnParams p) {
+  constexpr bool KEYS = MODE == kSplitKeys;
+  static_assert(!(KEYS && FP8), "the KEYS split takes float16 rows");
   constexpr int HG = MODE == kSplitHeads ? 64 : 16;   // heads per workgroup
-  constexpr int NKS = MODE == kSplitHeads ? 16 : 4;    // 32-dim k-steps of S per wave
-  constexpr int NDT = MODE == kSplitHeads ? 32 : 8;    // 16-dim output tiles per wave
+  constexpr int NKS = MODE == kSplitDims ? 4 : 16;    // 32-dim k-steps of S per wave
+  constexpr int NDT = MODE == kSplitDims ? 8 : 32;    // 16-dim output tiles per wave
   // Tile buffers: DIMS double-buffers (block i+1 and i+2 in flight while block i
   // is consumed); HEADS keeps one block so that two workgroups share a CU and one
   // computes while the other's transfers are in flight.
   // (FP8 tiles are half the size: DIMS keeps four blocks in flight)
   constexpr int NBUF = MODE == kSplitHeads ? 1 : (FP8 ? 4 : 2);
-  constexpr int KPD = 2;   // K operand reads in flight (k-steps)
-  constexpr int VPD = 4;   // V operand reads in flight (output tiles)
+  constexpr int KPD = KEYS ? 4 : 2;   // K operand reads in flight (k-steps)
+  constexpr int VPD = KEYS ? 8 : 4;   // V operand reads in flight (output tiles)
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave index (uniform)
@@ -68,7 +79,7 @@ __global__ __launch_bounds__(256, MODE == kSplitHeads ? 2 : 1) void attn_staged_
   const int ngroups = p.H / HG;
   // split decode: consecutive workgroups share (token, head group) and take
   // consecutive parts of its block list
-  const int nsplit = MODE == kSplitDims ? p.nsplit : 1;
+  const int nsplit = MODE == kSplitHeads ? 1 : p.nsplit;
   const int64_t L0 = xcd_remap(blockIdx.x, gridDim.x);
   const int split = (int)(L0 % nsplit);
   const int64_t L = L0 / nsplit;
@@ -78,10 +89,16 @@ __global__ __launch_bounds__(256, MODE == kSplitHeads ? 2 : 1) void attn_staged_
   const int b = (int)(bt / p.T);
   // this lane's head and the first head dim of this wave's operands
   const int h = hg * HG + (MODE == kSplitHeads ? 16 * w : 0) + c16;
-  const int d0 = MODE == kSplitHeads ? 0 : 128 * w;
+  const int d0 = MODE == kSplitDims ? 128 * w : 0;
 
   // Two tile buffers as separate LDS objects (FP8: codes, plus the blocks' row scales).
-  constexpr int KT = FP8 ? kF8Tile : kKTile, VT = FP8 ? kF8Tile : kVTile;
+  constexpr int KT = KEYS ? 16 : (FP8 ? kF8Tile : kKTile), VT = KEYS ? 16 : (FP8 ? kF8Tile : kVTile);
+  // KEYS: each wave's K tile (16 rows) and V tile (16 rows); at the end the same
+  // memory holds the waves' partial outputs, and mlw their maxima and sums
+  constexpr int kWaveTile = 16 * kKRow + 16 * kVRow;
+  static_assert(4 * kWaveTile >= 4 * 32 * 64 * 16, "the partial outputs fit in the tiles");
+  __shared__ __attribute__((aligned(16))) char wt[KEYS ? 4 * kWaveTile : 16];
+  __shared__ float mlw[KEYS ? 2 * 4 * 16 : 1];
   __shared__ __attribute__((aligned(16))) char kt0[KT], kt1[NBUF >= 2 ? KT : 16];
   __shared__ __attribute__((aligned(16))) char kt2[NBUF >= 4 ? KT : 16], kt3[NBUF >= 4 ? KT : 16];
   __shared__ __attribute__((aligned(16))) char vt0[VT], vt1[NBUF >= 2 ? VT : 16];
@@ -216,6 +233,92 @@ __global__ __launch_bounds__(256, MODE == kSplitHeads ? 2 : 1) void attn_staged_
   using Masked = std::integral_constant<bool, true>;
   using Unmasked = std::integral_constant<bool, false>;
 
+  // KEYS: a half-block's rows travel global -> this wave's staging registers, one
+  // contiguous 1 KiB row per load (K rows then, later, V rows).  `rows_of`
+  // resolves the 16 rows of half-block `hf` of key block j (uniform): region base
+  // offset and row numbers (gathered entries that are unused read row 0; every row
+  // is read, and the rows a mask hides are dealt with where they are used).
+  typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+  // (two staging sets: a wave's half-blocks alternate between them, so its rows
+  // are requested two rounds before they are used)
+  u32x4 stk0[KEYS ? 16 : 1], stv0[KEYS ? 16 : 1], stk1[KEYS ? 16 : 1], stv1[KEYS ? 16 : 1];
+  struct HalfRows {
+    rsrc_t k, v;      // the region's K and V rows of this sequence
+    int32_t off[16];  // byte offsets of the 16 rows in them
+  };
+  auto rows_of = [&](int j, int hf) __attribute__((always_inline)) -> HalfRows {
+    HalfRows hr;
+    if constexpr (KEYS) {
+      int rb;
+      bool gath = false;
+      const char *kb, *vb;
+      int64_t sr, span;
+      if (j < p.nb0) {
+        kb = p.k0 + b * p.kv0_sb;
+        vb = p.v0 + b * p.kv0_sb;
+        sr = p.kv0_sr;
+        span = (int64_t)p.nb0 * kRowsPerBlock * sr;
+        rb = j * kRowsPerBlock + 16 * hf;
+      } else {
+        kb = p.k1 + b * p.kv1_sb;
+        vb = p.v1 + b * p.kv1_sb;
+        sr = p.kv1_sr;
+        // (gathered rows are any of the region's n1 rows; dense ones fill whole blocks)
+        span = (INDEXED ? (int64_t)p.n1 : (int64_t)p.nb1 * kRowsPerBlock) * sr;
+        rb = (j - p.nb0) * kRowsPerBlock + 16 * hf;
+        gath = INDEXED;
+      }
+      // (a sequence's rows span less than 2^31 bytes; loads past the span read 0)
+      const uint32_t bytes = (uint32_t)(span < 0x7fffffff ? span : 0x7fffffff);
+      hr.k = make_rsrc(kb, bytes);
+      hr.v = make_rsrc(vb, bytes);
+      const int32_t sr32 = (int32_t)sr;
+      if (gath) {
+        const int4 *src = (const int4 *)&idx_s[rb];
+#pragma unroll
+        for (int q4 = 0; q4 < 4; ++q4) {
+          const int4 c4 = src[q4];
+          const int cs[4] = {c4.x, c4.y, c4.z, c4.w};
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const int c = __builtin_amdgcn_readfirstlane(cs[q]);
+            hr.off[4 * q4 + q] = ((c >= 0 && c < p.n1) ? c : 0) * sr32;
+          }
+        }
+      } else {
+#pragma unroll
+        for (int q = 0; q < 16; ++q) hr.off[q] = (rb + q) * sr32;
+      }
+    }
+    return hr;
+  };
+  // nothing to read: loads through it return zeros without touching memory
+  auto no_rows = [&]() __attribute__((always_inline)) -> HalfRows {
+    HalfRows hr;
+    hr.k = hr.v = make_rsrc(p.k0, 0u);
+#pragma unroll
+    for (int q = 0; q < 16; ++q) hr.off[q] = 0;
+    return hr;
+  };
+  auto load_k = [&](const HalfRows &hr, auto set) __attribute__((always_inline)) {
+    if constexpr (KEYS) {
+      u32x4 *dst = decltype(set)::value ? stk1 : stk0;
+#pragma unroll
+      for (int q = 0; q < 16; ++q)
+        dst[q] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(hr.k, lane16, hr.off[q], 0));
+    }
+  };
+  auto load_v = [&](const HalfRows &hr, auto set) __attribute__((always_inline)) {
+    if constexpr (KEYS) {
+      u32x4 *dst = decltype(set)::value ? stv1 : stv0;
+#pragma unroll
+      for (int q = 0; q < 16; ++q)
+        dst[q] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(hr.v, lane16, hr.off[q], 0));
+    }
+  };
+  using Set0 = std::integral_constant<int, 0>;
+  using Set1 = std::integral_constant<int, 1>;
+
   // The first NBUF list entries are guessed before the map row arrives, and their
   // transfers start at once: without a map (or for the token's own tile) the list
   // starts at the first block the window reaches.  A wrong guess is redone below.
@@ -231,9 +334,22 @@ __global__ __launch_bounds__(256, MODE == kSplitHeads ? 2 : 1) void attn_staged_
   auto spec = [&](int e) -> int {   // guess for the part's entry e
     return e < n_guess && jlo + e0_guess + e < p.nbd ? jlo + e0_guess + e : -1;
   };
-  for_bufs([&](auto E) {
-    if (spec(E) >= 0) stage_rows(spec(E), 0xffffffffu, E);
-  });
+  // KEYS issues its map row load first, so that waiting for it does not wait for
+  // the rows loaded behind it (vector loads complete in order).  Its loads are
+  // issued unconditionally where it matters (through buffer descriptors of size 0
+  // when there is nothing to read): the compiler's wait counts assume the fewest
+  // loads any path issues, so a load skipped on some path makes the common path
+  // wait for everything in flight.
+  const uint8_t *blkrow = p.blk ? p.blk + ((int64_t)b * p.ntiles + t / p.bq) * p.nbd : nullptr;
+  int s_first = -1;
+  if constexpr (KEYS) {
+    const int sraw = buf_load_u8(make_rsrc(blkrow, blkrow ? (uint32_t)p.nbd : 0u), (uint32_t)tid);
+    s_first = tid < p.nbd ? (blkrow ? sraw : kPartial) : 0;
+  } else {
+    for_bufs([&](auto E) {
+      if (spec(E) >= 0) stage_rows(spec(E), 0xffffffffu, E);
+    });
+  }
 
   // validity arrays of this sequence (size 0 when absent: every load out of range)
   const rsrc_t rb0 = make_rsrc(p.valid0 + (int64_t)b * p.valid0_sb, p.valid0 ? (uint32_t)p.n0 : 0u);
@@ -271,23 +387,58 @@ __global__ __launch_bounds__(256, MODE == kSplitHeads ? 2 : 1) void attn_staged_
   if (tj < p.nbd) row_rule(tj, tid & 31, tok, toff0, toff1);
   // (a region without a validity array needs no load: a load, even out of range,
   // is a full round trip queued behind the block transfers)
-  const int tv0 = p.valid0 ? buf_load_u8(rb0, toff0) : 0;
-  const int tv1 = p.valid1 ? buf_load_u8(rb1, toff1) : 0;
+  // (KEYS loads both unconditionally: the loads go out before the rows, and a
+  // conditional load makes the compiler wait for everything in flight)
+  const int tv0 = (KEYS || p.valid0) ? buf_load_u8(rb0, toff0) : 0;
+  const int tv1 = (KEYS || p.valid1) ? buf_load_u8(rb1, toff1) : 0;
+  // KEYS: the first 512 index entries into registers before the rows are loaded
+  int ia = -1, ib = -1;
+  if (KEYS && INDEXED) {
+    const rsrc_t ri = make_rsrc(p.idx + ((int64_t)b * p.T + t) * p.r1_k, 4u * (uint32_t)p.r1_k);
+    const int va = (int)__builtin_amdgcn_raw_buffer_load_b32(ri, 4u * tid, 0, 0);
+    const int vb = (int)__builtin_amdgcn_raw_buffer_load_b32(ri, 4u * (tid + 256), 0, 0);
+    ia = tid < p.r1_k ? va : -1;
+    ib = tid + 256 < p.r1_k ? vb : -1;
+  }
 
   // Q^T operand fragments: head h, dims d0 + 32ks + 8g .. +7
   half8 qf[NKS];
-  const char *qrow = p.q + b * p.q_sb + t * p.q_st + (int64_t)h * p.q_sh;
+  u32x4 qst[KEYS ? 4 : 1];
+  if constexpr (KEYS) {
+    // Q rows of heads 16hg + 4w .. +3, one contiguous 1 KiB row per load (they reach
+    // the operand registers through LDS: operand-shaped loads touch 16 rows each)
 #pragma unroll
-  for (int ks = 0; ks < NKS; ++ks) qf[ks] = *(const half8 *)(qrow + 2 * (d0 + 32 * ks + 8 * g));
+    for (int q = 0; q < 4; ++q)
+      qst[q] = *(__attribute__((address_space(1))) const u32x4 *)(
+          uniform_ptr(p.q + b * p.q_sb + t * p.q_st + (int64_t)(hg * HG + 4 * w + q) * p.q_sh) + lane16);
+    // each wave's first half-block (u = w: entry w >> 1, half w & 1) as guessed
+    {
+      const HalfRows hr = spec(w >> 1) >= 0 ? rows_of(spec(w >> 1), w & 1) : no_rows();
+      load_k(hr, Set0{});
+      load_v(hr, Set0{});
+    }
+    // Q rows into the first wave tile (free until the key loop starts)
+#pragma unroll
+    for (int q = 0; q < 4; ++q) *(u32x4 *)(wt + (4 * w + q) * kKRow + lane16) = qst[q];
+  } else {
+    const char *qrow = p.q + b * p.q_sb + t * p.q_st + (int64_t)h * p.q_sh;
+#pragma unroll
+    for (int ks = 0; ks < NKS; ++ks) qf[ks] = *(const half8 *)(qrow + 2 * (d0 + 32 * ks + 8 * g));
+  }
   if (INDEXED) {
     // the token's index list; entries up to the end of its last 32-entry block
     // that lie past r1_k read as unused (-1)
     const int32_t *src = p.idx + ((int64_t)b * p.T + t) * p.r1_k;
     const int padded = p.nb1 * kRowsPerBlock;
-    for (int e = tid; e < padded; e += 256) idx_s[e] = e < p.r1_k ? src[e] : -1;
+    if constexpr (KEYS) {
+      if (tid < padded) idx_s[tid] = ia;
+      if (tid + 256 < padded) idx_s[tid + 256] = ib;
+      for (int e = tid + 512; e < padded; e += 256) idx_s[e] = e < p.r1_k ? src[e] : -1;
+    } else {
+      for (int e = tid; e < padded; e += 256) idx_s[e] = e < p.r1_k ? src[e] : -1;
+    }
   }
-  const uint8_t *blkrow = p.blk ? p.blk + ((int64_t)b * p.ntiles + t / p.bq) * p.nbd : nullptr;
-  const int ndense = build_block_list<256>(blkrow, p.nbd, blist, cnt);   // ends with a barrier
+  const int ndense = build_block_list<256>(blkrow, p.nbd, blist, cnt, s_first);   // ends with a barrier
   const int nlist = ndense + (INDEXED ? p.nb1 : 0);
   // this workgroup's part of the list: entries [e0, e1)
   const int e0 = (int)((int64_t)nlist * split / nsplit), e1 = (int)((int64_t)nlist * (split + 1) / nsplit);
@@ -337,8 +488,8 @@ __global__ __launch_bounds__(256, MODE == kSplitHeads ? 2 : 1) void attn_staged_
       }
 #pragma unroll
       for (int k = 0; k < K; ++k) {
-        vb0[k] = p.valid0 ? buf_load_u8(rb0, off0[k]) : 0;
-        vb1[k] = p.valid1 ? buf_load_u8(rb1, off1[k]) : 0;
+        vb0[k] = (KEYS || p.valid0) ? buf_load_u8(rb0, off0[k]) : 0;
+        vb1[k] = (KEYS || p.valid1) ? buf_load_u8(rb1, off1[k]) : 0;
       }
 #pragma unroll
       for (int k = 0; k < K; ++k) {
@@ -402,6 +553,218 @@ __global__ __launch_bounds__(256, MODE == kSplitHeads ? 2 : 1) void attn_staged_
   // (ds_read_b64_tr_b16 hands element b of lane 16g + 4e + a to lane 16g + 4a + b)
   const int tr_e = (lane >> 2) & 3, tr_a = lane & 3;
   const int tr_r0 = 4 * g + tr_e;   // slot rows 0-3 of group g; rows 16 + ... for slots 4-7
+
+  if constexpr (KEYS) {
+    // ---- KEYS: wave w consumes half-blocks u = w, w + 4, ... of entries [e0, e1)
+    char *ktw = wt + w * kWaveTile;   // 16 K rows, kKRow apart
+    char *vtw = ktw + 16 * kKRow;     // 16 V rows, kVRow apart
+    const int nh = 2 * (e1 - e0);
+    // the guessed first half-block is loaded again when the list says otherwise
+    if (e0 + (w >> 1) < e1) {
+      int j, st;
+      entry_at(e0 + (w >> 1), j, st);
+      j = __builtin_amdgcn_readfirstlane(j);
+      if (j != spec(w >> 1)) {
+        const HalfRows hr = rows_of(j, w & 1);
+        load_k(hr, Set0{});
+        load_v(hr, Set0{});
+      }
+    }
+    // Q^T operand fragments (head h, dims 32ks + 8g .. +7) from the Q rows in LDS
+    // (written before the list barrier; read before the barrier after the masks)
+#pragma unroll
+    for (int ks = 0; ks < NKS; ++ks) qf[ks] = *(const half8 *)(wt + c16 * kKRow + 64 * ks + 16 * g);
+    // masks of the first two chunks of entries (the whole ring); their validity
+    // loads go out before the second half-block's rows, as waiting for them waits
+    // for everything issued earlier
+    build_masks(e0, e1 - e0 < kMaskRing ? e1 - e0 : kMaskRing, std::integral_constant<int, 8>{});
+    {
+      // the second half-block (u = w + 4) starts moving
+      const bool second = e0 + 2 + (w >> 1) < e1;
+      int j = 0, st;
+      if (second) entry_at(e0 + 2 + (w >> 1), j, st);
+      const HalfRows hr = second ? rows_of(__builtin_amdgcn_readfirstlane(j), w & 1) : no_rows();
+      load_k(hr, Set1{});
+      load_v(hr, Set1{});
+    }
+    lds_barrier();   // masks visible
+    // Round r: wave w takes half-block 4r + w, i.e. entries e0 + 2r and e0 + 2r + 1.
+    // Every kMaskChunk entries all waves meet and fill the ring slots of the chunk
+    // they have left with the masks of the chunk after the next.
+    const int nrounds = (nh + 3) >> 2;
+    // Rounds in which every wave has a half-block two rounds on ("steady") issue
+    // their loads unconditionally; the last rounds test for them.
+    auto round = [&](int r, auto set, auto steady) __attribute__((always_inline)) {
+      constexpr int S = decltype(set)::value;
+      constexpr bool STEADY = decltype(steady)::value;
+      u32x4 *stk = S ? stk1 : stk0;
+      u32x4 *stv = S ? stv1 : stv0;
+      if (r > 0 && (r & (kMaskChunk / 2 - 1)) == 0) {
+        const int c0 = e0 + 2 * r + kMaskChunk;
+        lds_barrier();   // every wave is done with the entries below e0 + 2r
+        if (c0 < e1) {
+          build_masks(c0, e1 - c0 < kMaskChunk ? e1 - c0 : kMaskChunk, std::integral_constant<int, 1>{});
+          lds_barrier();
+        }
+      }
+      const int u = 4 * r + w;
+      if (!STEADY && u >= nh) return;
+      const int hf = u & 1;
+      const uint32_t vm =
+          (__builtin_amdgcn_readfirstlane(vmask[(e0 + (u >> 1)) & (kMaskRing - 1)]) >> (16 * hf)) & 0xffffu;
+      // staged K rows -> this wave's K tile; the K rows of the wave's half-block two
+      // rounds on start moving into the same staging set
+#pragma unroll
+      for (int q = 0; q < 16; ++q) *(u32x4 *)(ktw + q * kKRow + lane16) = stk[q];
+      const bool more = STEADY || u + 8 < nh;
+      HalfRows nx;
+      if (STEADY || more) {
+        int j, st;
+        entry_at(e0 + ((u + 8) >> 1), j, st);
+        nx = rows_of(__builtin_amdgcn_readfirstlane(j), (u + 8) & 1);
+        load_k(nx, set);
+      }
+      // S^T = K Q^T: 16 keys x 16 heads over the 512 dims, K reads KPD steps ahead
+      floatx4 sacc = {0.f, 0.f, 0.f, 0.f};
+      const char *krow = ktw + c16 * kKRow + 16 * g;
+      uint4 ka[KPD];
+#pragma unroll
+      for (int u2 = 0; u2 < KPD; ++u2) ka[u2] = *(const uint4 *)(krow + 64 * u2);
+#pragma unroll
+      for (int ks = 0; ks < NKS; ++ks) {
+        sacc = mfma16(*(const half8 *)&ka[ks % KPD], qf[ks], sacc);
+        if (ks + KPD < NKS) ka[ks % KPD] = *(const uint4 *)(krow + 64 * (ks + KPD));
+        __builtin_amdgcn_sched_barrier(0);   // keep this order: MFMA, then the read it frees
+      }
+      // staged V rows -> this wave's V tile, the rows the mask hides as zeros; the
+      // next half-block's V rows start moving
+#pragma unroll
+      for (int q = 0; q < 16; ++q)
+        *(u32x4 *)(vtw + q * kVRow + lane16) = ((vm >> q) & 1u) ? stv[q] : u32x4{0u, 0u, 0u, 0u};
+      if (STEADY || more) load_v(nx, set);
+      // online softmax: this lane holds keys 4g .. 4g+3 of head h
+      float sv[4];
+#pragma unroll
+      for (int i2 = 0; i2 < 4; ++i2) {
+        sv[i2] = sacc[i2] * p.scale_log2;
+        if (!((vm >> (4 * g + i2)) & 1u)) sv[i2] = -INFINITY;
+      }
+      float mx = fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3]));
+      mx = xor_max(mx, 16);
+      mx = xor_max(mx, 32);
+      const bool grow = mx > m + kRescaleSlack;
+      const float mref = grow ? mx : m;
+      const float msafe = (mref == -INFINITY) ? 0.f : mref;
+      const float alpha = __builtin_amdgcn_exp2f(m - msafe);
+      half4 pf;
+      float psum = 0.f;
+#pragma unroll
+      for (int i2 = 0; i2 < 4; ++i2) {
+        const _Float16 ph = (_Float16)__builtin_amdgcn_exp2f(sv[i2] - msafe);
+        pf[i2] = ph;
+        psum += (float)ph;
+      }
+      l = alpha * l + psum;
+      m = mref;
+      if (__ballot(grow)) {
+#pragma unroll
+        for (int dt = 0; dt < NDT; ++dt) o[dt] *= alpha;
+      }
+      // O^T += V^T P^T, 16 keys per MFMA; one transpose read per output tile hands
+      // this lane dim 16dt + (lane & 15) of rows 4g .. 4g+3
+      const lds_char *vsrc = (const lds_char *)(__attribute__((address_space(3))) const void *)vtw +
+                             (4 * g + tr_e) * kVRow + 8 * tr_a;
+      auto vload = [&](int dt) __attribute__((always_inline)) -> half4 {
+        return __builtin_bit_cast(half4, __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                                             (__attribute__((address_space(3))) short4_t *)(vsrc + 32 * dt)));
+      };
+      half4 vq[VPD];
+#pragma unroll
+      for (int u2 = 0; u2 < VPD; ++u2) vq[u2] = vload(u2);
+#pragma unroll
+      for (int dt = 0; dt < NDT; ++dt) {
+        o[dt] = mfma16k16(vq[dt % VPD], pf, o[dt]);
+        if (dt + VPD < NDT) vq[dt % VPD] = vload(dt + VPD);
+        __builtin_amdgcn_sched_barrier(0);   // keep this order: MFMA, then the read it frees
+      }
+    };
+    using Steady = std::integral_constant<bool, true>;
+    using Tail = std::integral_constant<bool, false>;
+    // steady rounds: 4r + 3 + 8 < nh; an even number of them, then the rest
+    const int rsteady = (nh > 11 ? (nh - 11 + 3) >> 2 : 0) & ~1;
+    int r = 0;
+    for (; r < rsteady; r += 2) {
+      round(r, Set0{}, Steady{});
+      round(r + 1, Set1{}, Steady{});
+    }
+    for (; r < nrounds; r += 2) {
+      round(r, Set0{}, Tail{});
+      if (r + 1 < nrounds) round(r + 1, Set1{}, Tail{});
+    }
+
+    // ---- merge the four waves: with M = max_w m_w and f_w = 2^(m_w - M), the
+    // result is sum_w f_w O_w / sum_w f_w l_w (zero when no wave saw a row)
+    float lw = l;
+    lw = xor_sum(lw, 16);
+    lw = xor_sum(lw, 32);
+    lds_barrier();   // every wave is done with its tiles
+    if (g == 0) {
+      mlw[w * 16 + c16] = m;
+      mlw[64 + w * 16 + c16] = lw;
+    }
+    lds_barrier();
+    float mall = -INFINITY;
+#pragma unroll
+    for (int ww = 0; ww < 4; ++ww) mall = fmaxf(mall, mlw[ww * 16 + c16]);
+    float lall = 0.f;
+#pragma unroll
+    for (int ww = 0; ww < 4; ++ww) {
+      const float mw = mlw[ww * 16 + c16];
+      lall += (mw == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(mw - mall)) * mlw[64 + ww * 16 + c16];
+    }
+    const float f = m == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m - mall);
+    // wave w finishes output tiles 8w .. 8w+7 (dims 128w .. 128w+127); the others
+    // hand it theirs through LDS: xo[wave][tile][lane].  Instantiated per wave
+    // index, so that the tile selection is resolved at compile time.
+    floatx4 *xo = (floatx4 *)wt;
+    floatx4 acc[8];
+    auto merge = [&](auto wc) __attribute__((always_inline)) {
+      constexpr int W = decltype(wc)::value;
+#pragma unroll
+      for (int dt = 0; dt < NDT; ++dt)
+        if ((dt >> 3) != W) xo[(W * NDT + dt) * 64 + lane] = o[dt] * f;
+      lds_barrier();
+#pragma unroll
+      for (int k = 0; k < 8; ++k) acc[k] = o[8 * W + k] * f;
+#pragma unroll
+      for (int ww = 0; ww < 4; ++ww)
+        if (ww != W) {
+#pragma unroll
+          for (int k = 0; k < 8; ++k) acc[k] += xo[(ww * NDT + 8 * W + k) * 64 + lane];
+        }
+    };
+    if (w == 0) merge(std::integral_constant<int, 0>{});
+    else if (w == 1) merge(std::integral_constant<int, 1>{});
+    else if (w == 2) merge(std::integral_constant<int, 2>{});
+    else merge(std::integral_constant<int, 3>{});
+    if (nsplit > 1) {
+      // partial record of this split: unnormalised O, then the maxima and the sums
+      char *rec = p.ws + (L * nsplit + split) * kSplitRecord;
+      float *ob = (float *)rec + c16 * 512 + 128 * w + 4 * g;
+#pragma unroll
+      for (int k = 0; k < 8; ++k) *(floatx4 *)(ob + 16 * k) = acc[k];
+      if (w == 0 && g == 0) {
+        ((float *)(rec + 16 * 512 * 4))[c16] = mall;
+        ((float *)(rec + 16 * 512 * 4))[16 + c16] = lall;
+      }
+      return;
+    }
+    const float inv = lall > 0.f ? 1.f / lall : 0.f;
+    float *ob = (float *)(p.o + b * p.o_sb + t * p.o_st + (int64_t)h * p.o_sh) + 128 * w + 4 * g;
+#pragma unroll
+    for (int k = 0; k < 8; ++k) *(floatx4 *)(ob + 16 * k) = acc[k] * inv;
+    return;
+  }
 
   // Pipeline: blocks i+1 .. i+NBUF are in flight while block i is consumed.
   //   prologue: entry e -> buffer e unmasked for e < NBUF (already in flight when
@@ -645,10 +1008,13 @@ __global__ __launch_bounds__(256, MODE == kSplitHeads ? 2 : 1) void attn_staged_
 template <int MODE>
 static hipError_t launch_staged(const AttnParams &p, hipStream_t s) {
   constexpr int HG = MODE == kSplitHeads ? 64 : 16;
-  const int64_t n = (int64_t)p.B * p.T * (p.H / HG) * (MODE == kSplitDims ? p.nsplit : 1);
+  const int64_t n = (int64_t)p.B * p.T * (p.H / HG) * (MODE == kSplitHeads ? 1 : p.nsplit);
   if (n == 0) return hipSuccess;
   const dim3 grid((unsigned)n), block(256);
-  if (p.fp8) {
+  if constexpr (MODE == kSplitKeys) {
+    if (p.indexed) hipLaunchKernelGGL((attn_staged_kernel<MODE, true, false>), grid, block, 0, s, p);
+    else hipLaunchKernelGGL((attn_staged_kernel<MODE, false, false>), grid, block, 0, s, p);
+  } else if (p.fp8) {
     if (p.indexed) hipLaunchKernelGGL((attn_staged_kernel<MODE, true, true>), grid, block, 0, s, p);
     else hipLaunchKernelGGL((attn_staged_kernel<MODE, false, true>), grid, block, 0, s, p);
   } else {
@@ -658,8 +1024,22 @@ static hipError_t launch_staged(const AttnParams &p, hipStream_t s) {
   return hipGetLastError();
 }
 
+// Decode: float16 rows whose lists can be long take the KEYS split; short lists
+// (a few blocks: each wave would see one or two half-blocks, and the merge of the
+// four partial results would cost more than the overlap gains) and FP8 rows take
+// the DIMS split.  The bound on a token's list: the dense blocks its window can
+// reach (all dense blocks without a window), plus the gathered blocks.
+constexpr int64_t kKeysMinEntries = 8;
+static bool use_keys(const AttnParams &p) {
+  if (p.decode_split) return p.decode_split == 2;
+  if (p.fp8) return false;
+  int64_t dense = p.nbd;
+  if (p.window > 0) dense = std::min<int64_t>(dense, (int64_t)p.window / kRowsPerBlock + 2);
+  const int64_t entries = dense + (p.indexed ? p.nb1 : 0);
+  return entries / (p.nsplit > 0 ? p.nsplit : 1) >= kKeysMinEntries;
+}
 hipError_t launch_attn_decode(const AttnParams &p, hipStream_t s) {
-  return launch_staged<kSplitDims>(p, s);
+  return use_keys(p) ? launch_staged<kSplitKeys>(p, s) : launch_staged<kSplitDims>(p, s);
 }
 // Combine the split partials of one (token, head group): 16 heads x 512 dims over
 // 1024 threads, thread = (head, 8 consecutive dims).  The partials were accumulated
@@ -717,7 +1097,7 @@ __global__ __launch_bounds__(1024) void split_combine_kernel(const AttnParams p)
 }
 
 hipError_t launch_attn_decode_split(const AttnParams &p, hipStream_t s) {
-  hipError_t e = launch_staged<kSplitDims>(p, s);
+  hipError_t e = use_keys(p) ? launch_staged<kSplitKeys>(p, s) : launch_staged<kSplitDims>(p, s);
   if (e != hipSuccess) return e;
   const int64_t n = (int64_t)p.B * p.T * (p.H / 16);
   if (n == 0) return hipSuccess;

@@ -80,6 +80,7 @@ int resolve_mask(const ds4attn_args *a, int row_bytes, bool need_kv, AttnParams 
   else P.nb1 = P.indexed ? (P.r1_k + 31) / 32 : (int)(ceil32(P.n1) / 32);
   P.nbd = P.nb0 + (P.indexed ? 0 : P.nb1);
   P.nsplit = 1;
+  P.decode_split = 0;
   return DS4ATTN_OK;
 }
 
@@ -151,6 +152,13 @@ int run_attention(const ds4attn_args *a, const void *q, const uint8_t *blk, int3
                     !(a->flags & DS4ATTN_FLAG_GENERIC) && P.nbd <= kListCap && fits32;
   // FP8 rows are dequantized inside the matrix-core kernels only
   if (fp8 && !mfma) return DS4ATTN_E_UNSUPPORTED;
+  const bool want_dims = a->flags & DS4ATTN_FLAG_DECODE_DIMS, want_keys = a->flags & DS4ATTN_FLAG_DECODE_KEYS;
+  if (want_dims && want_keys) return DS4ATTN_E_INVAL;
+  if (want_dims || want_keys) {
+    // a chosen decode split: the matrix-core decode kernel, float16 rows for KEYS
+    if (!mfma || (prefill && a->n_head % 64 == 0) || (want_keys && fp8)) return DS4ATTN_E_UNSUPPORTED;
+    P.decode_split = want_keys ? 2 : 1;
+  }
   if (splits > 1) {
     // split decode runs on the matrix-core decode kernel only
     if (!mfma || prefill) return DS4ATTN_E_UNSUPPORTED;

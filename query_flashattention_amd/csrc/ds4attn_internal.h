@@ -49,6 +49,7 @@ struct AttnParams {
   // split decode: each token's block list divided over nsplit workgroups per head
   // group, partial results in ws (one kSplitRecord per (b, t, head group, split))
   int nsplit;              // 1 = no split
+  int decode_split;        // decode work split: 0 = chosen by list length, 1 = DIMS, 2 = KEYS
   char *ws;
   // block map
   const uint8_t *blk;      // [B][ntiles][nbd] or null (every block treated as PARTIAL)

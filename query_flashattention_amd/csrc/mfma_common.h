@@ -26,6 +26,11 @@ __device__ __forceinline__ int buf_load_u8(rsrc_t r, uint32_t off) {
 __device__ __forceinline__ floatx4 mfma16(const half8 &a, const half8 &b, const floatx4 &c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
 }
+typedef _Float16 half4v __attribute__((ext_vector_type(4)));
+// 16 x 16 x 16: operand lane l holds row (column) l % 16, k-slots 4(l / 16) .. +3.
+__device__ __forceinline__ floatx4 mfma16k16(const half4v &a, const half4v &b, const floatx4 &c) {
+  return __builtin_amdgcn_mfma_f32_16x16x16f16(a, b, c, 0, 0, 0);
+}
 
 // Key slot k (0..31) of an MFMA operand group: slots 8G..8G+3 hold block rows
 // 4G..4G+3 and slots 8G+4..8G+7 hold rows 16+4G..16+4G+3, which is exactly the
@@ -64,16 +69,19 @@ constexpr float kRescaleSlack = 8.f;
 // The workgroup lists, in LDS, the map blocks of its query tile that are not SKIP:
 // entry = block | status << 14, in block order.  A null map lists every block as
 // PARTIAL.  All threads of the workgroup must call it; it always ends with a barrier.
-// `cnt` is LDS scratch of NT/64 ints.
+// `cnt` is LDS scratch of NT/64 ints.  `s_first` >= 0 is the status of block
+// `threadIdx.x` already loaded by the caller (0 past the end of the row).
 template <int NT>
-__device__ __forceinline__ int build_block_list(const uint8_t *row, int nbd, uint16_t *list, int *cnt) {
+__device__ __forceinline__ int build_block_list(const uint8_t *row, int nbd, uint16_t *list, int *cnt,
+                                                int s_first = -1) {
   constexpr int NW = NT / 64;
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   int total = 0;
   for (int base = 0; base < nbd; base += NT) {
     const int j = base + tid;
     int s = 0;
-    if (j < nbd) s = row ? (int)row[j] : kPartial;
+    if (base == 0 && s_first >= 0) s = s_first;
+    else if (j < nbd) s = row ? (int)row[j] : kPartial;
     const unsigned long long m = __ballot(s != 0);
     if (lane == 0) cnt[wv] = __popcll(m);
     __syncthreads();

@@ -43,6 +43,18 @@ __device__ __forceinline__ void dma16(const char *row, uint32_t lane16, uint32_t
                :: "v"(lane16), "s"(ru), "s"(__builtin_amdgcn_readfirstlane(lds)) : "memory");
 }
 
+// A wave-uniform global-memory pointer moved to scalar registers, so that loads
+// from it take the scalar-base form with one shared lane offset.  The result is
+// typed as global memory: a generic pointer would make them flat loads, which
+// also count as LDS operations, so every wait for LDS would wait for them too.
+typedef __attribute__((address_space(1))) const char gchar;
+__device__ __forceinline__ gchar *uniform_ptr(const char *row) {
+  const uint64_t r = (uint64_t)row;
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)r);
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)(r >> 32));
+  return (gchar *)(((uint64_t)hi << 32) | (uint64_t)lo);
+}
+
 // The same transfer with a per-lane source address: lane i's 16 bytes come from
 // `src` (a different row for different lanes) and land at `lds` + 16 * i.  Used
 // for FP8 rows, two 512-byte rows per instruction.

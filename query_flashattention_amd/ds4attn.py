@@ -23,6 +23,8 @@ F16, F32, E4M3 = 0, 1, 2
 KV_PLAIN, KV_FP8_E4M3 = 0, 1
 BLK_SKIP, BLK_PARTIAL, BLK_FULL = 0, 1, 2
 FLAG_GENERIC = 1
+FLAG_DECODE_DIMS = 2
+FLAG_DECODE_KEYS = 4
 
 _c_void_p = ctypes.c_void_p
 _i32, _i64 = ctypes.c_int32, ctypes.c_int64

@@ -326,3 +326,26 @@ def test_binding_fails_loudly_without_library(tmp_path, monkeypatch):
             "\ntry:\n d.lib()\nexcept RuntimeError as e:\n print('raised', e)")
     out = subprocess.run([sys.executable, "-c", code], capture_output=True, text=True, cwd=ROOT)
     assert "raised" in out.stdout
+
+
+def _prefill(a, q=FAKE, o=FAKE, blk=None, bq=1):
+    return da.lib().ds4attn_prefill(ctypes.byref(a), q, blk, bq, o, None)
+
+
+@pytest.mark.parametrize("flags,fp8,entry,expect", [
+    (da.FLAG_DECODE_DIMS | da.FLAG_DECODE_KEYS, False, "decode", da.E_INVAL),
+    (da.FLAG_DECODE_KEYS, True, "decode", da.E_UNSUPPORTED),             # KEYS takes float16 rows
+    (da.FLAG_DECODE_KEYS | da.FLAG_GENERIC, False, "decode", da.E_UNSUPPORTED),
+    (da.FLAG_DECODE_DIMS | da.FLAG_GENERIC, False, "decode", da.E_UNSUPPORTED),
+    (da.FLAG_DECODE_DIMS, False, "prefill", da.E_UNSUPPORTED),           # 64-head prefill kernel
+])
+def test_decode_split_flags_rejected(flags, fp8, entry, expect):
+    a = _fp8_args() if fp8 else _good_args()
+    a.flags = flags
+    assert (_decode(a) if entry == "decode" else _prefill(a)) == expect
+
+
+def test_decode_split_flags_need_the_matrix_core_kernel():
+    a = _good_args(head_dim=128)
+    a.flags = da.FLAG_DECODE_KEYS
+    assert _decode(a) == da.E_UNSUPPORTED
