@@ -80,13 +80,15 @@ __global__ __launch_bounds__(256, MODE == kSplitHeads ? 2 : 1) void attn_staged_
   // split decode: consecutive workgroups share (token, head group) and take
   // consecutive parts of its block list
   const int nsplit = MODE == kSplitHeads ? 1 : p.nsplit;
-  const int64_t L0 = xcd_remap(blockIdx.x, gridDim.x);
-  const int split = (int)(L0 % nsplit);
-  const int64_t L = L0 / nsplit;
-  const int hg = (int)(L % ngroups);
-  const int64_t bt = L / ngroups;
-  const int t = (int)(bt % p.T);
-  const int b = (int)(bt / p.T);
+  // (32-bit unsigned arithmetic: the grid is below 2^31 workgroups, and 64-bit
+  // divisions by values known only at run time cost hundreds of instructions)
+  const uint32_t L0 = xcd_remap32(blockIdx.x, gridDim.x);
+  const int split = (int)(L0 % (uint32_t)nsplit);
+  const uint32_t L = L0 / (uint32_t)nsplit;
+  const int hg = (int)(L % (uint32_t)ngroups);
+  const uint32_t bt = L / (uint32_t)ngroups;
+  const int t = (int)(bt % (uint32_t)p.T);
+  const int b = (int)(bt / (uint32_t)p.T);
   // this lane's head and the first head dim of this wave's operands
   const int h = hg * HG + (MODE == kSplitHeads ? 16 * w : 0) + c16;
   const int d0 = MODE == kSplitDims ? 128 * w : 0;
@@ -328,9 +330,9 @@ __global__ __launch_bounds__(256, MODE == kSplitHeads ? 2 : 1) void attn_staged_
     jlo = lo <= 0 ? 0 : (int)(lo / kRowsPerBlock < p.nb0 ? lo / kRowsPerBlock : p.nb0);
   }
   // a split's list part starts at its share of the dense blocks from jlo on
-  const int64_t ndguess = p.nbd > jlo ? p.nbd - jlo : 0;
-  const int e0_guess = (int)(ndguess * split / nsplit);
-  const int n_guess = (int)(ndguess * (split + 1) / nsplit) - e0_guess;   // the part's length
+  const int ndguess = p.nbd > jlo ? p.nbd - jlo : 0;
+  const int e0_guess = (int)((uint32_t)(ndguess * split) / (uint32_t)nsplit);
+  const int n_guess = (int)((uint32_t)(ndguess * (split + 1)) / (uint32_t)nsplit) - e0_guess;   // the part's length
   auto spec = [&](int e) -> int {   // guess for the part's entry e
     return e < n_guess && jlo + e0_guess + e < p.nbd ? jlo + e0_guess + e : -1;
   };
@@ -411,7 +413,8 @@ __global__ __launch_bounds__(256, MODE == kSplitHeads ? 2 : 1) void attn_staged_
     for (int q = 0; q < 4; ++q)
       qst[q] = *(__attribute__((address_space(1))) const u32x4 *)(
           uniform_ptr(p.q + b * p.q_sb + t * p.q_st + (int64_t)(hg * HG + 4 * w + q) * p.q_sh) + lane16);
-    // each wave's first half-block (u = w: entry w >> 1, half w & 1) as guessed
+    // each wave's first two half-blocks (u = w and w + 4: entries w >> 1 and
+    // 2 + (w >> 1), half w & 1) as guessed
     {
       const HalfRows hr = spec(w >> 1) >= 0 ? rows_of(spec(w >> 1), w & 1) : no_rows();
       load_k(hr, Set0{});
@@ -420,6 +423,11 @@ __global__ __launch_bounds__(256, MODE == kSplitHeads ? 2 : 1) void attn_staged_
     // Q rows into the first wave tile (free until the key loop starts)
 #pragma unroll
     for (int q = 0; q < 4; ++q) *(u32x4 *)(wt + (4 * w + q) * kKRow + lane16) = qst[q];
+    {
+      const HalfRows hr = spec(2 + (w >> 1)) >= 0 ? rows_of(spec(2 + (w >> 1)), w & 1) : no_rows();
+      load_k(hr, Set1{});
+      load_v(hr, Set1{});
+    }
   } else {
     const char *qrow = p.q + b * p.q_sb + t * p.q_st + (int64_t)h * p.q_sh;
 #pragma unroll
@@ -441,7 +449,9 @@ __global__ __launch_bounds__(256, MODE == kSplitHeads ? 2 : 1) void attn_staged_
   const int ndense = build_block_list<256>(blkrow, p.nbd, blist, cnt, s_first);   // ends with a barrier
   const int nlist = ndense + (INDEXED ? p.nb1 : 0);
   // this workgroup's part of the list: entries [e0, e1)
-  const int e0 = (int)((int64_t)nlist * split / nsplit), e1 = (int)((int64_t)nlist * (split + 1) / nsplit);
+  // (nlist <= kListCap + kIdxCap / 32 and split < kMaxSplits: 32-bit products)
+  const int e0 = (int)((uint32_t)(nlist * split) / (uint32_t)nsplit);
+  const int e1 = (int)((uint32_t)(nlist * (split + 1)) / (uint32_t)nsplit);
   {
     const bool vis = tok && (toff0 == kOutOfRange || tv0 != 0) && (toff1 == kOutOfRange || tv1 != 0);
     const uint64_t bal = __ballot(vis);
@@ -469,7 +479,7 @@ __global__ __launch_bounds__(256, MODE == kSplitHeads ? 2 : 1) void attn_staged_
     constexpr int K = decltype(rounds)::value;
     const int r = lane & 31, half = lane >> 5;
     for (int e0 = 0; e0 < n; e0 += 8 * K) {
-      int ok[K], full[K], tab[K], vb0[K], vb1[K];
+      int ok[K], full[K], tab[K];
       uint32_t off0[K], off1[K];
 #pragma unroll
       for (int k = 0; k < K; ++k) {
@@ -486,16 +496,30 @@ __global__ __launch_bounds__(256, MODE == kSplitHeads ? 2 : 1) void attn_staged_
           else if (!full[k]) row_rule(j, r, ok[k], off0[k], off1[k]);
         }
       }
+      // the validity bytes: loaded and used inside the branch of a region that has
+      // them, so that the wait for them is there too (a wait after the branch
+      // would also wait for every row transfer in flight when there is none)
+      bool okv[K];
 #pragma unroll
-      for (int k = 0; k < K; ++k) {
-        vb0[k] = (KEYS || p.valid0) ? buf_load_u8(rb0, off0[k]) : 0;
-        vb1[k] = (KEYS || p.valid1) ? buf_load_u8(rb1, off1[k]) : 0;
+      for (int k = 0; k < K; ++k) okv[k] = ok[k];
+      if (p.valid0) {
+        int vb[K];
+#pragma unroll
+        for (int k = 0; k < K; ++k) vb[k] = buf_load_u8(rb0, off0[k]);
+#pragma unroll
+        for (int k = 0; k < K; ++k) okv[k] = okv[k] && (off0[k] == kOutOfRange || vb[k] != 0);
+      }
+      if (p.valid1) {
+        int vb[K];
+#pragma unroll
+        for (int k = 0; k < K; ++k) vb[k] = buf_load_u8(rb1, off1[k]);
+#pragma unroll
+        for (int k = 0; k < K; ++k) okv[k] = okv[k] && (off1[k] == kOutOfRange || vb[k] != 0);
       }
 #pragma unroll
       for (int k = 0; k < K; ++k) {
         const int el = e0 + 8 * k + 2 * w + half;
-        const bool vis = ok[k] && (off0[k] == kOutOfRange || vb0[k] != 0) &&
-                         (off1[k] == kOutOfRange || vb1[k] != 0);
+        const bool vis = okv[k];
         const uint64_t bal = __ballot(vis);
         if (el < n && r == 0)
           vmask[(c0 + el) & (kMaskRing - 1)] =
@@ -559,34 +583,27 @@ __global__ __launch_bounds__(256, MODE == kSplitHeads ? 2 : 1) void attn_staged_
     char *ktw = wt + w * kWaveTile;   // 16 K rows, kKRow apart
     char *vtw = ktw + 16 * kKRow;     // 16 V rows, kVRow apart
     const int nh = 2 * (e1 - e0);
-    // the guessed first half-block is loaded again when the list says otherwise
-    if (e0 + (w >> 1) < e1) {
-      int j, st;
-      entry_at(e0 + (w >> 1), j, st);
-      j = __builtin_amdgcn_readfirstlane(j);
-      if (j != spec(w >> 1)) {
-        const HalfRows hr = rows_of(j, w & 1);
-        load_k(hr, Set0{});
-        load_v(hr, Set0{});
+    // the guessed first two half-blocks are loaded again when the list says otherwise
+    auto recheck = [&](int e, auto set) __attribute__((always_inline)) {
+      if (e0 + e < e1) {
+        int j, st;
+        entry_at(e0 + e, j, st);
+        j = __builtin_amdgcn_readfirstlane(j);
+        if (j != spec(e)) {
+          const HalfRows hr = rows_of(j, w & 1);
+          load_k(hr, set);
+          load_v(hr, set);
+        }
       }
-    }
+    };
+    recheck(w >> 1, Set0{});
+    recheck(2 + (w >> 1), Set1{});
     // Q^T operand fragments (head h, dims 32ks + 8g .. +7) from the Q rows in LDS
     // (written before the list barrier; read before the barrier after the masks)
 #pragma unroll
     for (int ks = 0; ks < NKS; ++ks) qf[ks] = *(const half8 *)(wt + c16 * kKRow + 64 * ks + 16 * g);
-    // masks of the first two chunks of entries (the whole ring); their validity
-    // loads go out before the second half-block's rows, as waiting for them waits
-    // for everything issued earlier
+    // masks of the first two chunks of entries (the whole ring)
     build_masks(e0, e1 - e0 < kMaskRing ? e1 - e0 : kMaskRing, std::integral_constant<int, 8>{});
-    {
-      // the second half-block (u = w + 4) starts moving
-      const bool second = e0 + 2 + (w >> 1) < e1;
-      int j = 0, st;
-      if (second) entry_at(e0 + 2 + (w >> 1), j, st);
-      const HalfRows hr = second ? rows_of(__builtin_amdgcn_readfirstlane(j), w & 1) : no_rows();
-      load_k(hr, Set1{});
-      load_v(hr, Set1{});
-    }
     lds_barrier();   // masks visible
     // Round r: wave w takes half-block 4r + w, i.e. entries e0 + 2r and e0 + 2r + 1.
     // Every kMaskChunk entries all waves meet and fill the ring slots of the chunk
@@ -749,7 +766,7 @@ __global__ __launch_bounds__(256, MODE == kSplitHeads ? 2 : 1) void attn_staged_
     else merge(std::integral_constant<int, 3>{});
     if (nsplit > 1) {
       // partial record of this split: unnormalised O, then the maxima and the sums
-      char *rec = p.ws + (L * nsplit + split) * kSplitRecord;
+      char *rec = p.ws + ((int64_t)L * nsplit + split) * kSplitRecord;
       float *ob = (float *)rec + c16 * 512 + 128 * w + 4 * g;
 #pragma unroll
       for (int k = 0; k < 8; ++k) *(floatx4 *)(ob + 16 * k) = acc[k];
@@ -989,7 +1006,7 @@ __global__ __launch_bounds__(256, MODE == kSplitHeads ? 2 : 1) void attn_staged_
   lt = xor_sum(lt, 32);
   if (MODE == kSplitDims && nsplit > 1) {
     // partial record of this split: unnormalised O, then the maxima and the sums
-    char *rec = p.ws + (L * nsplit + split) * kSplitRecord;
+    char *rec = p.ws + ((int64_t)L * nsplit + split) * kSplitRecord;
     float *ob = (float *)rec + c16 * 512 + d0 + 4 * g;
 #pragma unroll
     for (int dt = 0; dt < NDT; ++dt) *(floatx4 *)(ob + 16 * dt) = o[dt];

@@ -63,6 +63,11 @@ struct AttnParams {
 // Workgroups are dealt to the dies round-robin; give each die a contiguous run of
 // logical work items so neighbours (head groups of one token, adjacent tokens)
 // share that die's L2.  A bijection on [0, n) for any n.
+__device__ __forceinline__ uint32_t xcd_remap32(uint32_t i, uint32_t n) {
+  const uint32_t x = i % kNumXcd, k = i / kNumXcd;
+  const uint32_t per = n / kNumXcd, rem = n % kNumXcd;
+  return (x < rem ? x * (per + 1) : rem * (per + 1) + (x - rem) * per) + k;
+}
 __device__ __forceinline__ int64_t xcd_remap(int64_t i, int64_t n) {
   const int64_t x = i % kNumXcd, k = i / kNumXcd;
   const int64_t per = n / kNumXcd, rem = n % kNumXcd;
