@@ -33,14 +33,14 @@
 //         16 heads; the four partial score tiles meet in LDS and every wave sums
 //         them in the same order; 4 workgroups per 64-head token fill the chip
 //         for small decode batches.
-//   KEYS  (HG = 16, decode, float16 rows): the waves take different key rows.
-//         Wave w consumes half-blocks (16 rows) w, w+4, w+8, ... of the list for
-//         all 16 heads over the full head dimension, with its own running max,
-//         sum and output; the four partial results are merged in LDS at the end
-//         (the log-sum-exp rule).  Its rows travel global -> registers (one
-//         contiguous 1 KiB row per load, the next half-block's while the current
-//         one is consumed) -> the wave's own K and V tiles, so no wave waits for
-//         another inside the key loop and the vector-memory path stays busy.
+//   KEYS  (HG = 16, decode): the waves take different key rows.  Wave w consumes
+//         units w, w+4, w+8, ... of the list (half-blocks of 16 float16 rows, or
+//         whole blocks of FP8 rows) for all 16 heads over the full head dimension,
+//         with its own running max, sum and output; the four partial results are
+//         merged in LDS at the end (the log-sum-exp rule).  Its rows travel
+//         global -> registers (1 KiB per load, a unit two rounds ahead of its
+//         use) -> the wave's own K and V tiles, so no wave waits for another
+//         inside the key loop and the vector-memory path stays busy.
 #include "staging.h"
 
 #include <algorithm>
@@ -58,7 +58,10 @@ enum : int { kSplitHeads = 0, kSplitDims = 1, kSplitKeys = 2 };
 template <int MODE, bool INDEXED, bool FP8>
 __global__ __launch_bounds__(256, MODE == kSplitHeads ? 2 : 1) void attn_staged_kernel(const AttnParams p) {
   constexpr bool KEYS = MODE == kSplitKeys;
-  static_assert(!(KEYS && FP8), "the KEYS split takes float16 rows");
+  // KEYS units: float16 rows go in half-blocks of 16 rows, FP8 rows in whole blocks
+  // (the FP8 tiles of a block take the space of a float16 half-block, and the
+  // 8-bit transpose read hands out 8 keys per lane)
+  constexpr int UPE = FP8 ? 1 : 2;   // KEYS units per list entry
   constexpr int HG = MODE == kSplitHeads ? 64 : 16;   // heads per workgroup
   constexpr int NKS = MODE == kSplitDims ? 4 : 16;    // 32-dim k-steps of S per wave
   constexpr int NDT = MODE == kSplitDims ? 8 : 32;    // 16-dim output tiles per wave
@@ -67,8 +70,8 @@ __global__ __launch_bounds__(256, MODE == kSplitHeads ? 2 : 1) void attn_staged_
   // computes while the other's transfers are in flight.
   // (FP8 tiles are half the size: DIMS keeps four blocks in flight)
   constexpr int NBUF = MODE == kSplitHeads ? 1 : (FP8 ? 4 : 2);
-  constexpr int KPD = KEYS ? 4 : 2;   // K operand reads in flight (k-steps)
-  constexpr int VPD = KEYS ? 8 : 4;   // V operand reads in flight (output tiles)
+  constexpr int KPD = KEYS && !FP8 ? 4 : 2;   // K operand reads in flight (k-steps)
+  constexpr int VPD = KEYS && !FP8 ? 8 : 4;   // V operand reads in flight (output tiles)
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave index (uniform)
@@ -95,9 +98,11 @@ __global__ __launch_bounds__(256, MODE == kSplitHeads ? 2 : 1) void attn_staged_
 
   // Two tile buffers as separate LDS objects (FP8: codes, plus the blocks' row scales).
   constexpr int KT = KEYS ? 16 : (FP8 ? kF8Tile : kKTile), VT = KEYS ? 16 : (FP8 ? kF8Tile : kVTile);
-  // KEYS: each wave's K tile (16 rows) and V tile (16 rows); at the end the same
-  // memory holds the waves' partial outputs, and mlw their maxima and sums
+  // KEYS: each wave's K tile and V tile (16 float16 rows each, or 32 FP8 rows each
+  // plus their 64 scales); at the end the same memory holds the waves' partial
+  // outputs, and mlw their maxima and sums
   constexpr int kWaveTile = 16 * kKRow + 16 * kVRow;
+  static_assert(2 * kF8Tile + 64 * 4 <= kWaveTile, "FP8 tiles fit in a wave's space");
   static_assert(4 * kWaveTile >= 4 * 32 * 64 * 16, "the partial outputs fit in the tiles");
   __shared__ __attribute__((aligned(16))) char wt[KEYS ? 4 * kWaveTile : 16];
   __shared__ float mlw[KEYS ? 2 * 4 * 16 : 1];
@@ -235,61 +240,115 @@ __global__ __launch_bounds__(256, MODE == kSplitHeads ? 2 : 1) void attn_staged_
   using Masked = std::integral_constant<bool, true>;
   using Unmasked = std::integral_constant<bool, false>;
 
-  // KEYS: a half-block's rows travel global -> this wave's staging registers, one
-  // contiguous 1 KiB row per load (K rows then, later, V rows).  `rows_of`
-  // resolves the 16 rows of half-block `hf` of key block j (uniform): region base
-  // offset and row numbers (gathered entries that are unused read row 0; every row
-  // is read, and the rows a mask hides are dealt with where they are used).
+  // KEYS: a unit's rows travel global -> this wave's staging registers, one
+  // contiguous 1 KiB per load (one float16 row, or two FP8 rows: lanes 0-31 the
+  // first, 32-63 the second, in the FP8 tile's pair order), K rows then, later, V
+  // rows.  `rows_of` resolves the rows of unit `hf` of key block j (uniform):
+  // region descriptors and offsets (gathered entries that are unused read row 0;
+  // every row is read, and the rows a mask hides are dealt with where they are
+  // used).  FP8 rows bring their scales: this lane's K and V scale of row lane & 31
+  // (rows past the region's live rows read 0).
   typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-  // (two staging sets: a wave's half-blocks alternate between them, so its rows
-  // are requested two rounds before they are used)
-  u32x4 stk0[KEYS ? 16 : 1], stv0[KEYS ? 16 : 1], stk1[KEYS ? 16 : 1], stv1[KEYS ? 16 : 1];
+  // (float16: two staging sets, a wave's units alternating between them, so its
+  // rows are requested two rounds before they are used; FP8 keeps one, for the
+  // registers its conversions need: rows come a round ahead)
+  constexpr int NSET = FP8 ? 1 : 2;
+  u32x4 stk0[KEYS ? 16 : 1], stv0[KEYS ? 16 : 1];
+  u32x4 stk1[KEYS && NSET == 2 ? 16 : 1], stv1[KEYS && NSET == 2 ? 16 : 1];
+  float sck0 = 0.f, scv0 = 0.f, sck1 = 0.f, scv1 = 0.f;
   struct HalfRows {
-    rsrc_t k, v;      // the region's K and V rows of this sequence
-    int32_t off[16];  // byte offsets of the 16 rows in them
+    rsrc_t k, v, ks, vs;  // the region's K and V rows (and FP8 scales) of this sequence
+    int32_t off[16];      // byte offsets of the 16 rows (FP8: of the first rows of the 16 pairs)
+    int32_t dif[FP8 ? 16 : 1];   // FP8: second row's offset minus the first's, per pair
+    int32_t soff;         // FP8: this lane's scale offset
   };
   auto rows_of = [&](int j, int hf) __attribute__((always_inline)) -> HalfRows {
     HalfRows hr;
     if constexpr (KEYS) {
-      int rb;
+      int rb, nlive;
       bool gath = false;
-      const char *kb, *vb;
+      const char *kb, *vb, *ksb = nullptr, *vsb = nullptr;
       int64_t sr, span;
       if (j < p.nb0) {
         kb = p.k0 + b * p.kv0_sb;
         vb = p.v0 + b * p.kv0_sb;
         sr = p.kv0_sr;
         span = (int64_t)p.nb0 * kRowsPerBlock * sr;
-        rb = j * kRowsPerBlock + 16 * hf;
+        rb = j * kRowsPerBlock + (32 / UPE) * hf;
+        nlive = p.n0;
+        if (FP8) {
+          ksb = p.ks0 + b * p.s0_sb;
+          vsb = p.vs0 + b * p.s0_sb;
+        }
       } else {
         kb = p.k1 + b * p.kv1_sb;
         vb = p.v1 + b * p.kv1_sb;
         sr = p.kv1_sr;
         // (gathered rows are any of the region's n1 rows; dense ones fill whole blocks)
         span = (INDEXED ? (int64_t)p.n1 : (int64_t)p.nb1 * kRowsPerBlock) * sr;
-        rb = (j - p.nb0) * kRowsPerBlock + 16 * hf;
+        rb = (j - p.nb0) * kRowsPerBlock + (32 / UPE) * hf;
+        nlive = p.n1;
         gath = INDEXED;
+        if (FP8) {
+          ksb = p.ks1 + b * p.s1_sb;
+          vsb = p.vs1 + b * p.s1_sb;
+        }
       }
       // (a sequence's rows span less than 2^31 bytes; loads past the span read 0)
       const uint32_t bytes = (uint32_t)(span < 0x7fffffff ? span : 0x7fffffff);
       hr.k = make_rsrc(kb, bytes);
       hr.v = make_rsrc(vb, bytes);
       const int32_t sr32 = (int32_t)sr;
-      if (gath) {
-        const int4 *src = (const int4 *)&idx_s[rb];
+      if constexpr (FP8) {
+        hr.ks = make_rsrc(ksb, 4u * (uint32_t)nlive);
+        hr.vs = make_rsrc(vsb, 4u * (uint32_t)nlive);
+        int rr[32];
+        if (gath) {
+          const int4 *src = (const int4 *)&idx_s[rb];
 #pragma unroll
-        for (int q4 = 0; q4 < 4; ++q4) {
-          const int4 c4 = src[q4];
-          const int cs[4] = {c4.x, c4.y, c4.z, c4.w};
+          for (int q4 = 0; q4 < 8; ++q4) {
+            const int4 c4 = src[q4];
+            const int cs[4] = {c4.x, c4.y, c4.z, c4.w};
 #pragma unroll
-          for (int q = 0; q < 4; ++q) {
-            const int c = __builtin_amdgcn_readfirstlane(cs[q]);
-            hr.off[4 * q4 + q] = ((c >= 0 && c < p.n1) ? c : 0) * sr32;
+            for (int q = 0; q < 4; ++q) {
+              const int c = __builtin_amdgcn_readfirstlane(cs[q]);
+              rr[4 * q4 + q] = (c >= 0 && c < p.n1) ? c : 0;
+            }
           }
-        }
-      } else {
+        } else {
 #pragma unroll
-        for (int q = 0; q < 16; ++q) hr.off[q] = (rb + q) * sr32;
+          for (int q = 0; q < 32; ++q) rr[q] = rb + q;
+        }
+#pragma unroll
+        for (int q = 0; q < 16; ++q) {
+          hr.off[q] = rr[q] * sr32;
+          hr.dif[q] = (rr[f8_second_row(q)] - rr[q]) * sr32;
+        }
+        int myrow = rb + (lane & 31);
+        if (gath) {
+          const int c = idx_s[rb + (lane & 31)];
+          myrow = (c >= 0 && c < p.n1) ? c : 0;
+        }
+        hr.soff = 4 * myrow;
+      } else {
+        hr.ks = hr.vs = hr.k;
+        hr.soff = 0;
+        if (gath) {
+          const int4 *src = (const int4 *)&idx_s[rb];
+#pragma unroll
+          for (int q4 = 0; q4 < 4; ++q4) {
+            const int4 c4 = src[q4];
+            const int cs[4] = {c4.x, c4.y, c4.z, c4.w};
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+              const int c = __builtin_amdgcn_readfirstlane(cs[q]);
+              hr.off[4 * q4 + q] = ((c >= 0 && c < p.n1) ? c : 0) * sr32;
+            }
+          }
+        } else {
+#pragma unroll
+          for (int q = 0; q < 16; ++q) hr.off[q] = (rb + q) * sr32;
+        }
       }
     }
     return hr;
@@ -297,25 +356,47 @@ __global__ __launch_bounds__(256, MODE == kSplitHeads ? 2 : 1) void attn_staged_
   // nothing to read: loads through it return zeros without touching memory
   auto no_rows = [&]() __attribute__((always_inline)) -> HalfRows {
     HalfRows hr;
-    hr.k = hr.v = make_rsrc(p.k0, 0u);
+    hr.k = hr.v = hr.ks = hr.vs = make_rsrc(p.k0, 0u);
 #pragma unroll
     for (int q = 0; q < 16; ++q) hr.off[q] = 0;
+    if constexpr (FP8) {
+#pragma unroll
+      for (int q = 0; q < 16; ++q) hr.dif[q] = 0;
+    }
+    hr.soff = 0;
     return hr;
   };
+  // (the row offset is a scalar and the lane offset a shared register; FP8 lanes
+  // 32-63 add the distance to the pair's second row)
+  const uint32_t lane16lo = 16u * (lane & 31);
   auto load_k = [&](const HalfRows &hr, auto set) __attribute__((always_inline)) {
     if constexpr (KEYS) {
-      u32x4 *dst = decltype(set)::value ? stk1 : stk0;
+      u32x4 *dst = (NSET == 2 && decltype(set)::value) ? stk1 : stk0;
 #pragma unroll
       for (int q = 0; q < 16; ++q)
-        dst[q] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(hr.k, lane16, hr.off[q], 0));
+        dst[q] = __builtin_bit_cast(
+            u32x4, FP8 ? __builtin_amdgcn_raw_buffer_load_b128(hr.k, lane16lo + (lane >= 32 ? hr.dif[q] : 0), hr.off[q], 0)
+                       : __builtin_amdgcn_raw_buffer_load_b128(hr.k, lane16, hr.off[q], 0));
+      if constexpr (FP8) {
+        const float sc = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(hr.ks, hr.soff, 0, 0));
+        if (decltype(set)::value) sck1 = sc;
+        else sck0 = sc;
+      }
     }
   };
   auto load_v = [&](const HalfRows &hr, auto set) __attribute__((always_inline)) {
     if constexpr (KEYS) {
-      u32x4 *dst = decltype(set)::value ? stv1 : stv0;
+      u32x4 *dst = (NSET == 2 && decltype(set)::value) ? stv1 : stv0;
 #pragma unroll
       for (int q = 0; q < 16; ++q)
-        dst[q] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(hr.v, lane16, hr.off[q], 0));
+        dst[q] = __builtin_bit_cast(
+            u32x4, FP8 ? __builtin_amdgcn_raw_buffer_load_b128(hr.v, lane16lo + (lane >= 32 ? hr.dif[q] : 0), hr.off[q], 0)
+                       : __builtin_amdgcn_raw_buffer_load_b128(hr.v, lane16, hr.off[q], 0));
+      if constexpr (FP8) {
+        const float sc = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(hr.vs, hr.soff, 0, 0));
+        if (decltype(set)::value) scv1 = sc;
+        else scv0 = sc;
+      }
     }
   };
   using Set0 = std::integral_constant<int, 0>;
@@ -413,18 +494,18 @@ __global__ __launch_bounds__(256, MODE == kSplitHeads ? 2 : 1) void attn_staged_
     for (int q = 0; q < 4; ++q)
       qst[q] = *(__attribute__((address_space(1))) const u32x4 *)(
           uniform_ptr(p.q + b * p.q_sb + t * p.q_st + (int64_t)(hg * HG + 4 * w + q) * p.q_sh) + lane16);
-    // each wave's first two half-blocks (u = w and w + 4: entries w >> 1 and
-    // 2 + (w >> 1), half w & 1) as guessed
+    // each wave's first two units (u = w and w + 4: entries u / UPE, unit u % UPE
+    // within its entry) as guessed
     {
-      const HalfRows hr = spec(w >> 1) >= 0 ? rows_of(spec(w >> 1), w & 1) : no_rows();
+      const HalfRows hr = spec(w / UPE) >= 0 ? rows_of(spec(w / UPE), w % UPE) : no_rows();
       load_k(hr, Set0{});
       load_v(hr, Set0{});
     }
     // Q rows into the first wave tile (free until the key loop starts)
 #pragma unroll
     for (int q = 0; q < 4; ++q) *(u32x4 *)(wt + (4 * w + q) * kKRow + lane16) = qst[q];
-    {
-      const HalfRows hr = spec(2 + (w >> 1)) >= 0 ? rows_of(spec(2 + (w >> 1)), w & 1) : no_rows();
+    if constexpr (NSET == 2) {
+      const HalfRows hr = spec((w + 4) / UPE) >= 0 ? rows_of(spec((w + 4) / UPE), w % UPE) : no_rows();
       load_k(hr, Set1{});
       load_v(hr, Set1{});
     }
@@ -579,25 +660,28 @@ __global__ __launch_bounds__(256, MODE == kSplitHeads ? 2 : 1) void attn_staged_
   const int tr_r0 = 4 * g + tr_e;   // slot rows 0-3 of group g; rows 16 + ... for slots 4-7
 
   if constexpr (KEYS) {
-    // ---- KEYS: wave w consumes half-blocks u = w, w + 4, ... of entries [e0, e1)
-    char *ktw = wt + w * kWaveTile;   // 16 K rows, kKRow apart
-    char *vtw = ktw + 16 * kKRow;     // 16 V rows, kVRow apart
-    const int nh = 2 * (e1 - e0);
-    // the guessed first two half-blocks are loaded again when the list says otherwise
+    // ---- KEYS: wave w consumes units u = w, w + 4, ... of entries [e0, e1)
+    // (float16: 16 K rows kKRow apart, then 16 V rows kVRow apart; FP8: the K tile
+    // and the V tile of a block in pair order, then 32 K scales and 32 V scales)
+    char *ktw = wt + w * kWaveTile;
+    char *vtw = ktw + (FP8 ? kF8Tile : 16 * kKRow);
+    float *sct = (float *)(ktw + 2 * kF8Tile);
+    const int nh = UPE * (e1 - e0);
+    // the guessed first two units are loaded again when the list says otherwise
     auto recheck = [&](int e, auto set) __attribute__((always_inline)) {
       if (e0 + e < e1) {
         int j, st;
         entry_at(e0 + e, j, st);
         j = __builtin_amdgcn_readfirstlane(j);
         if (j != spec(e)) {
-          const HalfRows hr = rows_of(j, w & 1);
+          const HalfRows hr = rows_of(j, w % UPE);
           load_k(hr, set);
           load_v(hr, set);
         }
       }
     };
-    recheck(w >> 1, Set0{});
-    recheck(2 + (w >> 1), Set1{});
+    recheck(w / UPE, Set0{});
+    if constexpr (NSET == 2) recheck((w + 4) / UPE, Set1{});
     // Q^T operand fragments (head h, dims 32ks + 8g .. +7) from the Q rows in LDS
     // (written before the list barrier; read before the barrier after the masks)
 #pragma unroll
@@ -605,20 +689,22 @@ __global__ __launch_bounds__(256, MODE == kSplitHeads ? 2 : 1) void attn_staged_
     // masks of the first two chunks of entries (the whole ring)
     build_masks(e0, e1 - e0 < kMaskRing ? e1 - e0 : kMaskRing, std::integral_constant<int, 8>{});
     lds_barrier();   // masks visible
-    // Round r: wave w takes half-block 4r + w, i.e. entries e0 + 2r and e0 + 2r + 1.
-    // Every kMaskChunk entries all waves meet and fill the ring slots of the chunk
-    // they have left with the masks of the chunk after the next.
+    // Round r: wave w takes unit 4r + w, i.e. entries e0 + 4r / UPE .. (two entries
+    // of half-blocks, or four blocks).  Every kMaskChunk entries all waves meet and
+    // fill the ring slots of the chunk they have left with the masks of the chunk
+    // after the next.
     const int nrounds = (nh + 3) >> 2;
     // Rounds in which every wave has a half-block two rounds on ("steady") issue
     // their loads unconditionally; the last rounds test for them.
     auto round = [&](int r, auto set, auto steady) __attribute__((always_inline)) {
       constexpr int S = decltype(set)::value;
       constexpr bool STEADY = decltype(steady)::value;
-      u32x4 *stk = S ? stk1 : stk0;
-      u32x4 *stv = S ? stv1 : stv0;
-      if (r > 0 && (r & (kMaskChunk / 2 - 1)) == 0) {
-        const int c0 = e0 + 2 * r + kMaskChunk;
-        lds_barrier();   // every wave is done with the entries below e0 + 2r
+      u32x4 *stk = (NSET == 2 && S) ? stk1 : stk0;
+      u32x4 *stv = (NSET == 2 && S) ? stv1 : stv0;
+      constexpr int kRoundsPerChunk = kMaskChunk * UPE / 4;
+      if (r > 0 && (r & (kRoundsPerChunk - 1)) == 0) {
+        const int c0 = e0 + 4 * r / UPE + kMaskChunk;
+        lds_barrier();   // every wave is done with the entries below e0 + 4r / UPE
         if (c0 < e1) {
           build_masks(c0, e1 - c0 < kMaskChunk ? e1 - c0 : kMaskChunk, std::integral_constant<int, 1>{});
           lds_barrier();
@@ -626,97 +712,210 @@ __global__ __launch_bounds__(256, MODE == kSplitHeads ? 2 : 1) void attn_staged_
       }
       const int u = 4 * r + w;
       if (!STEADY && u >= nh) return;
-      const int hf = u & 1;
-      const uint32_t vm =
-          (__builtin_amdgcn_readfirstlane(vmask[(e0 + (u >> 1)) & (kMaskRing - 1)]) >> (16 * hf)) & 0xffffu;
-      // staged K rows -> this wave's K tile; the K rows of the wave's half-block two
-      // rounds on start moving into the same staging set
+      const int hf = u % UPE;
+      const uint32_t vmw = __builtin_amdgcn_readfirstlane(vmask[(e0 + u / UPE) & (kMaskRing - 1)]);
+      const uint32_t vm = FP8 ? vmw : (vmw >> (16 * hf)) & 0xffffu;
+      // staged K rows -> this wave's K tile (FP8: and the K scales); the K rows of
+      // the wave's unit two rounds on start moving into the same staging set
+      if constexpr (FP8) {
 #pragma unroll
-      for (int q = 0; q < 16; ++q) *(u32x4 *)(ktw + q * kKRow + lane16) = stk[q];
-      const bool more = STEADY || u + 8 < nh;
+        for (int q = 0; q < 16; ++q) *(u32x4 *)(ktw + q * kF8Pair + lane16) = stk[q];
+        if (lane < 32) sct[lane] = S ? sck1 : sck0;
+      } else {
+#pragma unroll
+        for (int q = 0; q < 16; ++q) *(u32x4 *)(ktw + q * kKRow + lane16) = stk[q];
+      }
+      const bool more = STEADY || u + 4 * NSET < nh;
       HalfRows nx;
       if (STEADY || more) {
         int j, st;
-        entry_at(e0 + ((u + 8) >> 1), j, st);
-        nx = rows_of(__builtin_amdgcn_readfirstlane(j), (u + 8) & 1);
+        entry_at(e0 + (u + 4 * NSET) / UPE, j, st);
+        nx = rows_of(__builtin_amdgcn_readfirstlane(j), (u + 4 * NSET) % UPE);
         load_k(nx, set);
       }
-      // S^T = K Q^T: 16 keys x 16 heads over the 512 dims, K reads KPD steps ahead
-      floatx4 sacc = {0.f, 0.f, 0.f, 0.f};
-      const char *krow = ktw + c16 * kKRow + 16 * g;
-      uint4 ka[KPD];
+      // S^T = K Q^T over the 512 dims, K reads KPD steps ahead: float16, one tile of
+      // 16 keys x 16 heads; FP8, two tiles (rows c16 and 16 + c16 of the block)
+      floatx4 sacc = {0.f, 0.f, 0.f, 0.f}, sacc1 = {0.f, 0.f, 0.f, 0.f};
+      if constexpr (FP8) {
+        const char *krow0 = ktw + f8_row_off(c16) + 8 * g;
+        const char *krow1 = ktw + f8_row_off(16 + c16) + 8 * g;
+        uint2 ka[KPD], kb[KPD];
 #pragma unroll
-      for (int u2 = 0; u2 < KPD; ++u2) ka[u2] = *(const uint4 *)(krow + 64 * u2);
+        for (int u2 = 0; u2 < KPD; ++u2) {
+          ka[u2] = *(const uint2 *)(krow0 + 32 * u2);
+          kb[u2] = *(const uint2 *)(krow1 + 32 * u2);
+        }
 #pragma unroll
-      for (int ks = 0; ks < NKS; ++ks) {
-        sacc = mfma16(*(const half8 *)&ka[ks % KPD], qf[ks], sacc);
-        if (ks + KPD < NKS) ka[ks % KPD] = *(const uint4 *)(krow + 64 * (ks + KPD));
-        __builtin_amdgcn_sched_barrier(0);   // keep this order: MFMA, then the read it frees
+        for (int ks = 0; ks < NKS; ++ks) {
+          sacc = mfma16(e4m3x8_to_half8(ka[ks % KPD]), qf[ks], sacc);
+          sacc1 = mfma16(e4m3x8_to_half8(kb[ks % KPD]), qf[ks], sacc1);
+          if (ks + KPD < NKS) {
+            ka[ks % KPD] = *(const uint2 *)(krow0 + 32 * (ks + KPD));
+            kb[ks % KPD] = *(const uint2 *)(krow1 + 32 * (ks + KPD));
+          }
+          __builtin_amdgcn_sched_barrier(0);   // keep this order: MFMAs, then the reads they free
+        }
+      } else {
+        const char *krow = ktw + c16 * kKRow + 16 * g;
+        uint4 ka[KPD];
+#pragma unroll
+        for (int u2 = 0; u2 < KPD; ++u2) ka[u2] = *(const uint4 *)(krow + 64 * u2);
+#pragma unroll
+        for (int ks = 0; ks < NKS; ++ks) {
+          sacc = mfma16(*(const half8 *)&ka[ks % KPD], qf[ks], sacc);
+          if (ks + KPD < NKS) ka[ks % KPD] = *(const uint4 *)(krow + 64 * (ks + KPD));
+          __builtin_amdgcn_sched_barrier(0);   // keep this order: MFMA, then the read it frees
+        }
       }
-      // staged V rows -> this wave's V tile, the rows the mask hides as zeros; the
-      // next half-block's V rows start moving
+      // staged V rows -> this wave's V tile, the rows the mask hides as zeros (FP8:
+      // with zero scales); the next unit's V rows start moving
+      if constexpr (FP8) {
+        // transfer q: lanes 0-31 row q, lanes 32-63 row f8_second_row(q)
 #pragma unroll
-      for (int q = 0; q < 16; ++q)
-        *(u32x4 *)(vtw + q * kVRow + lane16) = ((vm >> q) & 1u) ? stv[q] : u32x4{0u, 0u, 0u, 0u};
+        for (int q = 0; q < 16; ++q) {
+          const int rq = lane < 32 ? q : f8_second_row(q);
+          *(u32x4 *)(vtw + q * kF8Pair + lane16) = ((vm >> rq) & 1u) ? stv[q] : u32x4{0u, 0u, 0u, 0u};
+        }
+        if (lane >= 32) sct[lane] = ((vm >> (lane & 31)) & 1u) ? (S ? scv1 : scv0) : 0.f;
+      } else {
+#pragma unroll
+        for (int q = 0; q < 16; ++q)
+          *(u32x4 *)(vtw + q * kVRow + lane16) = ((vm >> q) & 1u) ? stv[q] : u32x4{0u, 0u, 0u, 0u};
+      }
       if (STEADY || more) load_v(nx, set);
-      // online softmax: this lane holds keys 4g .. 4g+3 of head h
-      float sv[4];
+      if constexpr (FP8) {
+        // online softmax: this lane holds rows slot_row(g, 0..7) of head h; K row
+        // scales of slot rows 4g..4g+3 and 16+4g..16+4g+3
+        const float4 klo = *(const float4 *)(sct + 4 * g);
+        const float4 khi = *(const float4 *)(sct + 16 + 4 * g);
+        const float kq[8] = {klo.x, klo.y, klo.z, klo.w, khi.x, khi.y, khi.z, khi.w};
+        float sv[8];
 #pragma unroll
-      for (int i2 = 0; i2 < 4; ++i2) {
-        sv[i2] = sacc[i2] * p.scale_log2;
-        if (!((vm >> (4 * g + i2)) & 1u)) sv[i2] = -INFINITY;
-      }
-      float mx = fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3]));
-      mx = xor_max(mx, 16);
-      mx = xor_max(mx, 32);
-      const bool grow = mx > m + kRescaleSlack;
-      const float mref = grow ? mx : m;
-      const float msafe = (mref == -INFINITY) ? 0.f : mref;
-      const float alpha = __builtin_amdgcn_exp2f(m - msafe);
-      half4 pf;
-      float psum = 0.f;
+        for (int i2 = 0; i2 < 4; ++i2) {
+          sv[i2] = sacc[i2] * (p.scale_log2 * kq[i2]);
+          sv[4 + i2] = sacc1[i2] * (p.scale_log2 * kq[4 + i2]);
+        }
+        if (vm != 0xffffffffu) {
+          const uint32_t sm = slot_mask(vm, g);
 #pragma unroll
-      for (int i2 = 0; i2 < 4; ++i2) {
-        const _Float16 ph = (_Float16)__builtin_amdgcn_exp2f(sv[i2] - msafe);
-        pf[i2] = ph;
-        psum += (float)ph;
-      }
-      l = alpha * l + psum;
-      m = mref;
-      if (__ballot(grow)) {
+          for (int i2 = 0; i2 < 8; ++i2)
+            if (!((sm >> i2) & 1u)) sv[i2] = -INFINITY;
+        }
+        float mx = sv[0];
 #pragma unroll
-        for (int dt = 0; dt < NDT; ++dt) o[dt] *= alpha;
-      }
-      // O^T += V^T P^T, 16 keys per MFMA; one transpose read per output tile hands
-      // this lane dim 16dt + (lane & 15) of rows 4g .. 4g+3
-      const lds_char *vsrc = (const lds_char *)(__attribute__((address_space(3))) const void *)vtw +
-                             (4 * g + tr_e) * kVRow + 8 * tr_a;
-      auto vload = [&](int dt) __attribute__((always_inline)) -> half4 {
-        return __builtin_bit_cast(half4, __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                                             (__attribute__((address_space(3))) short4_t *)(vsrc + 32 * dt)));
-      };
-      half4 vq[VPD];
+        for (int i2 = 1; i2 < 8; ++i2) mx = fmaxf(mx, sv[i2]);
+        mx = xor_max(mx, 16);
+        mx = xor_max(mx, 32);
+        const bool grow = mx > m + kRescaleSlack;
+        const float mref = grow ? mx : m;
+        const float msafe = (mref == -INFINITY) ? 0.f : mref;
+        const float alpha = __builtin_amdgcn_exp2f(m - msafe);
+        half8 pf;
+        float psum = 0.f;
 #pragma unroll
-      for (int u2 = 0; u2 < VPD; ++u2) vq[u2] = vload(u2);
+        for (int i2 = 0; i2 < 8; ++i2) {
+          const _Float16 ph = (_Float16)__builtin_amdgcn_exp2f(sv[i2] - msafe);
+          pf[i2] = ph;
+          psum += (float)ph;
+        }
+        l = alpha * l + psum;
+        m = mref;
+        if (__ballot(grow)) {
 #pragma unroll
-      for (int dt = 0; dt < NDT; ++dt) {
-        o[dt] = mfma16k16(vq[dt % VPD], pf, o[dt]);
-        if (dt + VPD < NDT) vq[dt % VPD] = vload(dt + VPD);
-        __builtin_amdgcn_sched_barrier(0);   // keep this order: MFMA, then the read it frees
+          for (int dt = 0; dt < NDT; ++dt) o[dt] *= alpha;
+        }
+        // O^T += V^T P^T, 32 keys per MFMA: the 8-bit transpose read hands lane
+        // 16g + c dim 16dt + c of its group's eight slot rows (this lane supplies
+        // row slot_row(g, (lane & 15) >> 1), dims 16dt + 8(lane & 1) .. +7); times
+        // the rows' V scales in float16
+        const int trk = (lane & 15) >> 1;
+        const int trow = trk < 4 ? 4 * g + trk : 16 + 4 * g + (trk - 4);
+        const lds_char *vsrc = (const lds_char *)(__attribute__((address_space(3))) const void *)vtw +
+                               f8_row_off(trow) + 8 * (lane & 1);
+        const float4 vlo = *(const float4 *)(sct + 32 + 4 * g);
+        const float4 vhi = *(const float4 *)(sct + 48 + 4 * g);
+        const half8 vsc = {(_Float16)vlo.x, (_Float16)vlo.y, (_Float16)vlo.z, (_Float16)vlo.w,
+                           (_Float16)vhi.x, (_Float16)vhi.y, (_Float16)vhi.z, (_Float16)vhi.w};
+        auto vload = [&](int dt) __attribute__((always_inline)) -> uint2 {
+          const int2v rv = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
+              (__attribute__((address_space(3))) int2v *)(vsrc + 16 * dt));
+          return make_uint2((uint32_t)rv.x, (uint32_t)rv.y);
+        };
+        uint2 vq[VPD];
+#pragma unroll
+        for (int u2 = 0; u2 < VPD; ++u2) vq[u2] = vload(u2);
+#pragma unroll
+        for (int dt = 0; dt < NDT; ++dt) {
+          o[dt] = mfma16(e4m3x8_to_half8(vq[dt % VPD]) * vsc, pf, o[dt]);
+          if (dt + VPD < NDT) vq[dt % VPD] = vload(dt + VPD);
+          __builtin_amdgcn_sched_barrier(0);   // keep this order: MFMA, then the read it frees
+        }
+      } else {
+        // online softmax: this lane holds keys 4g .. 4g+3 of head h
+        float sv[4];
+#pragma unroll
+        for (int i2 = 0; i2 < 4; ++i2) {
+          sv[i2] = sacc[i2] * p.scale_log2;
+          if (!((vm >> (4 * g + i2)) & 1u)) sv[i2] = -INFINITY;
+        }
+        float mx = fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3]));
+        mx = xor_max(mx, 16);
+        mx = xor_max(mx, 32);
+        const bool grow = mx > m + kRescaleSlack;
+        const float mref = grow ? mx : m;
+        const float msafe = (mref == -INFINITY) ? 0.f : mref;
+        const float alpha = __builtin_amdgcn_exp2f(m - msafe);
+        half4 pf;
+        float psum = 0.f;
+#pragma unroll
+        for (int i2 = 0; i2 < 4; ++i2) {
+          const _Float16 ph = (_Float16)__builtin_amdgcn_exp2f(sv[i2] - msafe);
+          pf[i2] = ph;
+          psum += (float)ph;
+        }
+        l = alpha * l + psum;
+        m = mref;
+        if (__ballot(grow)) {
+#pragma unroll
+          for (int dt = 0; dt < NDT; ++dt) o[dt] *= alpha;
+        }
+        // O^T += V^T P^T, 16 keys per MFMA; one transpose read per output tile hands
+        // this lane dim 16dt + (lane & 15) of rows 4g .. 4g+3
+        const lds_char *vsrc = (const lds_char *)(__attribute__((address_space(3))) const void *)vtw +
+                               (4 * g + tr_e) * kVRow + 8 * tr_a;
+        auto vload = [&](int dt) __attribute__((always_inline)) -> half4 {
+          return __builtin_bit_cast(half4, __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                                               (__attribute__((address_space(3))) short4_t *)(vsrc + 32 * dt)));
+        };
+        half4 vq[VPD];
+#pragma unroll
+        for (int u2 = 0; u2 < VPD; ++u2) vq[u2] = vload(u2);
+#pragma unroll
+        for (int dt = 0; dt < NDT; ++dt) {
+          o[dt] = mfma16k16(vq[dt % VPD], pf, o[dt]);
+          if (dt + VPD < NDT) vq[dt % VPD] = vload(dt + VPD);
+          __builtin_amdgcn_sched_barrier(0);   // keep this order: MFMA, then the read it frees
+        }
       }
     };
     using Steady = std::integral_constant<bool, true>;
     using Tail = std::integral_constant<bool, false>;
-    // steady rounds: 4r + 3 + 8 < nh; an even number of them, then the rest
-    const int rsteady = (nh > 11 ? (nh - 11 + 3) >> 2 : 0) & ~1;
+    // steady rounds: 4r + 3 + 4 NSET < nh (a multiple of NSET of them), then the rest
+    constexpr int kAhead = 3 + 4 * NSET;
+    const int rsteady = (nh > kAhead ? (nh - kAhead + 3) >> 2 : 0) & ~(NSET - 1);
     int r = 0;
-    for (; r < rsteady; r += 2) {
-      round(r, Set0{}, Steady{});
-      round(r + 1, Set1{}, Steady{});
-    }
-    for (; r < nrounds; r += 2) {
-      round(r, Set0{}, Tail{});
-      if (r + 1 < nrounds) round(r + 1, Set1{}, Tail{});
+    if constexpr (NSET == 2) {
+      for (; r < rsteady; r += 2) {
+        round(r, Set0{}, Steady{});
+        round(r + 1, Set1{}, Steady{});
+      }
+      for (; r < nrounds; r += 2) {
+        round(r, Set0{}, Tail{});
+        if (r + 1 < nrounds) round(r + 1, Set1{}, Tail{});
+      }
+    } else {
+      for (; r < rsteady; ++r) round(r, Set0{}, Steady{});
+      for (; r < nrounds; ++r) round(r, Set0{}, Tail{});
     }
 
     // ---- merge the four waves: with M = max_w m_w and f_w = 2^(m_w - M), the
@@ -1028,10 +1227,7 @@ static hipError_t launch_staged(const AttnParams &p, hipStream_t s) {
   const int64_t n = (int64_t)p.B * p.T * (p.H / HG) * (MODE == kSplitHeads ? 1 : p.nsplit);
   if (n == 0) return hipSuccess;
   const dim3 grid((unsigned)n), block(256);
-  if constexpr (MODE == kSplitKeys) {
-    if (p.indexed) hipLaunchKernelGGL((attn_staged_kernel<MODE, true, false>), grid, block, 0, s, p);
-    else hipLaunchKernelGGL((attn_staged_kernel<MODE, false, false>), grid, block, 0, s, p);
-  } else if (p.fp8) {
+  if (p.fp8) {
     if (p.indexed) hipLaunchKernelGGL((attn_staged_kernel<MODE, true, true>), grid, block, 0, s, p);
     else hipLaunchKernelGGL((attn_staged_kernel<MODE, false, true>), grid, block, 0, s, p);
   } else {
@@ -1041,15 +1237,13 @@ static hipError_t launch_staged(const AttnParams &p, hipStream_t s) {
   return hipGetLastError();
 }
 
-// Decode: float16 rows whose lists can be long take the KEYS split; short lists
-// (a few blocks: each wave would see one or two half-blocks, and the merge of the
-// four partial results would cost more than the overlap gains) and FP8 rows take
-// the DIMS split.  The bound on a token's list: the dense blocks its window can
+// Decode: lists that can be long take the KEYS split; short lists (a few blocks:
+// each wave would see one or two units, and the merge of the four partial results
+// would cost more than the overlap gains) take the DIMS split.  The bound on a token's list: the dense blocks its window can
 // reach (all dense blocks without a window), plus the gathered blocks.
 constexpr int64_t kKeysMinEntries = 8;
 static bool use_keys(const AttnParams &p) {
   if (p.decode_split) return p.decode_split == 2;
-  if (p.fp8) return false;
   int64_t dense = p.nbd;
   if (p.window > 0) dense = std::min<int64_t>(dense, (int64_t)p.window / kRowsPerBlock + 2);
   const int64_t entries = dense + (p.indexed ? p.nb1 : 0);

@@ -155,8 +155,8 @@ int run_attention(const ds4attn_args *a, const void *q, const uint8_t *blk, int3
   const bool want_dims = a->flags & DS4ATTN_FLAG_DECODE_DIMS, want_keys = a->flags & DS4ATTN_FLAG_DECODE_KEYS;
   if (want_dims && want_keys) return DS4ATTN_E_INVAL;
   if (want_dims || want_keys) {
-    // a chosen decode split: the matrix-core decode kernel, float16 rows for KEYS
-    if (!mfma || (prefill && a->n_head % 64 == 0) || (want_keys && fp8)) return DS4ATTN_E_UNSUPPORTED;
+    // a chosen decode split: the matrix-core decode kernel
+    if (!mfma || (prefill && a->n_head % 64 == 0)) return DS4ATTN_E_UNSUPPORTED;
     P.decode_split = want_keys ? 2 : 1;
   }
   if (splits > 1) {

@@ -334,7 +334,6 @@ def _prefill(a, q=FAKE, o=FAKE, blk=None, bq=1):
 
 @pytest.mark.parametrize("flags,fp8,entry,expect", [
     (da.FLAG_DECODE_DIMS | da.FLAG_DECODE_KEYS, False, "decode", da.E_INVAL),
-    (da.FLAG_DECODE_KEYS, True, "decode", da.E_UNSUPPORTED),             # KEYS takes float16 rows
     (da.FLAG_DECODE_KEYS | da.FLAG_GENERIC, False, "decode", da.E_UNSUPPORTED),
     (da.FLAG_DECODE_DIMS | da.FLAG_GENERIC, False, "decode", da.E_UNSUPPORTED),
     (da.FLAG_DECODE_DIMS, False, "prefill", da.E_UNSUPPORTED),           # 64-head prefill kernel

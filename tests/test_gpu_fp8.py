@@ -208,3 +208,58 @@ def test_quantize_then_attend():
                                                    None, w.r0.ring_offset, torch.from_numpy(wks),
                                                    torch.from_numpy(wvs)))
     _compare(out.cpu().double().numpy(), ref.attention(_oracle_problem(w8)), "quantize -> decode")
+
+
+# --------------------------------------------------------------------------- both decode work splits
+
+FP8_SPLITS = {"dims": da.FLAG_DECODE_DIMS, "keys": da.FLAG_DECODE_KEYS}
+
+FP8_DECODE_CASES = [(c[0], c[1]) for c in FP8_CASES] + [
+    # lists longer than a chunk of 64 entries, index lists longer than 512 entries
+    ("f8_long_dense", dict(batch=1, tokens=1, heads=16, head_dim=512, n0=4500, valid0_frac=0.9)),
+    ("f8_long_index", dict(batch=1, tokens=2, heads=16, head_dim=512, n0=128, n1=3000, r1_mode="index",
+                           r1_k=1500, idx_invalid_frac=0.05)),
+]
+
+
+def _run_flags(w, flags, splits=1):
+    dp = pipeline.to_device(w, DEV)
+    dp.flags = flags
+    out = pipeline.step(dp, "decode", 1, splits=splits)
+    torch.cuda.synchronize()
+    return out.cpu().double().numpy()
+
+
+@pytest.mark.parametrize("split", list(FP8_SPLITS))
+@pytest.mark.parametrize("label,kw", FP8_DECODE_CASES, ids=[c[0] for c in FP8_DECODE_CASES])
+def test_attention_fp8_decode_splits(label, kw, split):
+    """Every case through the decode kernel with each way of dividing a workgroup's
+    work over its waves forced; hidden rows hold NaN codes and NaN scales."""
+    seed = zlib.crc32(label.encode()) % 1000
+    w = wl.fp8_variant(wl.random_problem(seed, **kw), seed + 1)
+    want = ref.attention(_oracle_problem(w))
+    _poison_hidden_rows(w)
+    out = _run_flags(w, FP8_SPLITS[split])
+    _compare(out, want, f"{label}/{split}")
+    if label == "f8_masked_tokens":
+        assert (out[0, :3] == 0).all()
+
+
+@pytest.mark.parametrize("split", list(FP8_SPLITS))
+def test_attention_fp8_workloads_splits(split):
+    w = wl.named("decode_r128_fp8")
+    _compare(_run_flags(w, FP8_SPLITS[split]), ref.attention(_oracle_problem(w)), f"decode_r128_fp8/{split}")
+    w = wl.named("decode_r4_fp8")
+    out = _run_flags(w, FP8_SPLITS[split])
+    seqs = [0, 9, 33, 63]
+    want = ref.attention(_oracle_problem(w), tokens=[(b, 0) for b in seqs])
+    _compare(out[seqs, 0], want, f"decode_r4_fp8/{split}")
+
+
+@pytest.mark.parametrize("split", list(FP8_SPLITS))
+def test_attention_fp8_split_over_workgroups(split):
+    kw = dict(batch=1, tokens=2, heads=64, head_dim=512, n0=70, window=32, q_pos0=60, k_pos0=0, n1=900,
+              r1_mode="index", r1_k=300, idx_invalid_frac=0.1)
+    w = wl.fp8_variant(wl.random_problem(77, **kw), 78)
+    want = ref.attention(_oracle_problem(w))
+    _compare(_run_flags(w, FP8_SPLITS[split], splits=3), want, f"fp8 index/{split} x3")
