@@ -70,8 +70,8 @@ __global__ __launch_bounds__(256, MODE == kSplitHeads ? 2 : 1) void attn_staged_
   // computes while the other's transfers are in flight.
   // (FP8 tiles are half the size: DIMS keeps four blocks in flight)
   constexpr int NBUF = MODE == kSplitHeads ? 1 : (FP8 ? 4 : 2);
-  constexpr int KPD = KEYS && !FP8 ? 4 : 2;   // K operand reads in flight (k-steps)
-  constexpr int VPD = KEYS && !FP8 ? 8 : 4;   // V operand reads in flight (output tiles)
+  constexpr int KPD = KEYS ? 4 : 2;   // K operand reads in flight (k-steps)
+  constexpr int VPD = KEYS ? 8 : 4;   // V operand reads in flight (output tiles)
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave index (uniform)
