@@ -242,21 +242,14 @@ class Runner:
             evs[k][1].record()
         torch.cuda.synchronize()
         d = sorted(a.elapsed_time(b) for a, b in evs)
-        return {"mean": mean, "launches": reps * r, "single_launch_median": d[len(d) // 2]}
+        return {"mean": mean, "launches": reps * r, "single_launch_median": d[len(d) // 2],
+                "single_launch_p10": d[len(d) // 10], "single_launch_p90": d[(9 * len(d)) // 10]}
 
 
 # --------------------------------------------------------------------------- CPU baseline
 
-def cpu_baseline(w, kv_bytes_per_step, seconds):
-    """The float64 oracle on the host, over whole batches of the same workload,
-    repeated until `seconds` of CPU work; K/V GB/s on the same algorithmic bytes."""
+def _oracle_rate(p, seconds):
     from oracle import reference as ref
-    try:
-        from threadpoolctl import threadpool_info
-        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
-    except Exception:  # pragma: no cover - threadpoolctl is optional
-        threads = 1
-    p = ref.from_workload(w)
     reps = 0
     t0 = time.perf_counter()
     while True:
@@ -264,11 +257,93 @@ def cpu_baseline(w, kv_bytes_per_step, seconds):
         reps += 1
         el = time.perf_counter() - t0
         if el >= seconds:
-            break
-    return {"value": round(kv_bytes_per_step * reps / el / 1e9, 3), "unit": "GB/s", "cores": threads,
-            "kind": "oracle",
-            "sample": f"float64 NumPy oracle over the whole batch ({w.q.shape[0]} sequences), "
-                      f"{reps} repetitions in {el:.1f} s"}
+            return reps, el
+
+
+def cpu_baseline(w, kv_bytes_per_step, seconds):
+    """The float64 oracle on the host, over whole batches of the same workload,
+    repeated until `seconds` of CPU work; K/V GB/s on the same algorithmic bytes.
+    Run with the BLAS threads the process has, and again with one thread."""
+    from oracle import reference as ref
+    try:
+        from threadpoolctl import threadpool_info, threadpool_limits
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover - threadpoolctl is optional
+        threads, threadpool_limits = 1, None
+    p = ref.from_workload(w)
+    reps, el = _oracle_rate(p, seconds)
+    out = {"value": round(kv_bytes_per_step * reps / el / 1e9, 3), "unit": "GB/s", "cores": threads,
+           "kind": "oracle",
+           "sample": f"float64 NumPy oracle over the whole batch ({w.q.shape[0]} sequences), "
+                     f"{reps} repetitions in {el:.1f} s"}
+    if threadpool_limits is not None:
+        with threadpool_limits(1):
+            reps1, el1 = _oracle_rate(p, seconds / 2)
+        out["single_thread"] = {"value": round(kv_bytes_per_step * reps1 / el1 / 1e9, 3), "unit": "GB/s",
+                                "cores": 1, "sample": f"{reps1} repetitions in {el1:.1f} s"}
+    return out
+
+
+# --------------------------------------------------------------------------- measured peaks
+
+def measured_peaks(torch):
+    """Achievable HBM read bandwidth and float16 MFMA throughput of this device,
+    from the probe library (libds4probes.so): a streaming read of 4 GiB, and a loop
+    of independent MFMA chains on 2 waves per SIMD.  Also the shader clock during
+    the MFMA loop (cycles over 100 MHz reference ticks)."""
+    import ctypes
+    lib = ctypes.CDLL(os.path.join(ROOT, "query_flashattention_amd", "libds4probes.so"))
+    lib.ds4probe_stream_read.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p, ctypes.c_int32,
+                                         ctypes.c_void_p]
+    lib.ds4probe_mfma_loop.argtypes = [ctypes.c_int32, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int32,
+                                       ctypes.c_void_p]
+    lib.ds4probe_mfma_loop_flops.argtypes = [ctypes.c_int32, ctypes.c_int32]
+    lib.ds4probe_mfma_loop_flops.restype = ctypes.c_int64
+    stream = torch.cuda.current_stream().cuda_stream
+    nbytes, grid, reps = 4 << 30, 4096, 5
+    buf = torch.ones(nbytes // 4, dtype=torch.float32, device="cuda")
+    sink = torch.empty(grid * 256, dtype=torch.int32, device="cuda")
+    assert lib.ds4probe_stream_read(buf.data_ptr(), nbytes, sink.data_ptr(), grid, stream) == 0
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record()
+    for _ in range(reps):
+        assert lib.ds4probe_stream_read(buf.data_ptr(), nbytes, sink.data_ptr(), grid, stream) == 0
+    e1.record()
+    torch.cuda.synchronize()
+    hbm = nbytes * reps / (e0.elapsed_time(e1) * 1e-3) / 1e9
+    del buf, sink
+    mgrid, iters = 512, 4000
+    out = torch.empty(mgrid * 256, dtype=torch.float32, device="cuda")
+    clocks = torch.zeros(2 * mgrid * 4, dtype=torch.int64, device="cuda")
+    assert lib.ds4probe_mfma_loop(iters, out.data_ptr(), clocks.data_ptr(), mgrid, stream) == 0
+    torch.cuda.synchronize()
+    e0.record()
+    for _ in range(reps):
+        assert lib.ds4probe_mfma_loop(iters, out.data_ptr(), clocks.data_ptr(), mgrid, stream) == 0
+    e1.record()
+    torch.cuda.synchronize()
+    tflops = lib.ds4probe_mfma_loop_flops(iters, mgrid) * reps / (e0.elapsed_time(e1) * 1e-3) / 1e12
+    ck = clocks.view(-1, 2).cpu().double()
+    mhz = float((ck[:, 0] / (ck[:, 1] * 10e-9)).median()) / 1e6
+    return {"hbm_read_GBps": round(hbm, 1), "mfma_f16_TFLOPs": round(tflops, 1),
+            "shader_clock_MHz_in_mfma_loop": round(mhz, 1),
+            "method": "libds4probes.so: 5 streaming reads of 4 GiB (4096 x 256 threads, 16-byte loads); "
+                      f"{mgrid} workgroups x 4 waves x {iters} x 8 independent v_mfma_f32_16x16x32_f16"}
+
+
+def decode_kernel_label(w):
+    """The decode kernel the library picks for a workload (the same rule as its
+    dispatch: the KEYS split when a token's list can hold at least 8 blocks)."""
+    nb0 = -(-w.r0.n_rows // 32)
+    indexed = w.r1_index is not None
+    nb1 = 0
+    if w.r1 is not None and w.r1.n_rows > 0:
+        nb1 = -(-w.r1_index.shape[-1] // 32) if indexed else -(-w.r1.n_rows // 32)
+    nbd = nb0 + (0 if indexed else nb1)
+    dense = min(nbd, w.window // 32 + 2) if w.window > 0 else nbd
+    mode = 2 if dense + (nb1 if indexed else 0) >= 8 else 1
+    return mode
 
 
 def prefill_cpu_tflops(w, n_tokens, seconds):
@@ -400,6 +475,7 @@ def main():
     ap.add_argument("--launches", type=int, default=100, help="attention launches timed by events")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-extra", action="store_true", help="skip the prefill / ratio-128 lines")
+    ap.add_argument("--no-peaks", action="store_true", help="skip the measured-peak probes")
     ap.add_argument("--copy-probe-mb", type=int, default=0,
                     help="only run a device-to-device copy of this many MiB (counter calibration)")
     args = ap.parse_args()
@@ -441,11 +517,14 @@ def main():
         roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": round(achieved / HBM_PEAK_GBS, 4),
                 "traffic": traffic_from_profiles(DECODE_KERNEL_SRC) if name == "decode_swa" else None,
-                "kernel": "attn_staged_kernel<1,%s,%s> (ds4attn_decode)" % (
-                    str(runner.w.r1_index is not None).lower(), str(name.endswith("_fp8")).lower()),
+                "kernel": "attn_staged_kernel<%d,%s,%s> (ds4attn_decode)" % (
+                    decode_kernel_label(runner.w), str(runner.w.r1_index is not None).lower(),
+                    str(name.endswith("_fp8")).lower()),
                 "bytes_per_launch": compulsory, "kernel_ms_mean": round(kern["mean"], 5),
                 "kernel_launches_timed": kern["launches"],
-                "single_launch_ms_median": round(kern["single_launch_median"], 5)}
+                "single_launch_ms_median": round(kern["single_launch_median"], 5),
+                "single_launch_ms_p10": round(kern["single_launch_p10"], 5),
+                "single_launch_ms_p90": round(kern["single_launch_p90"], 5)}
     else:
         value = c["flops"] / (ms_step * 1e-3) / 1e12
         unit = "TFLOP/s"
@@ -455,7 +534,10 @@ def main():
                 "kernel": "attn_staged_kernel<0,%s,%s> (ds4attn_prefill)" % (
                     str(runner.w.r1_index is not None).lower(), str(name.endswith("_fp8")).lower()),
                 "flops_per_launch": c["flops"],
-                "kernel_ms_mean": round(kern["mean"], 5), "kernel_launches_timed": kern["launches"]}
+                "kernel_ms_mean": round(kern["mean"], 5), "kernel_launches_timed": kern["launches"],
+                "single_launch_ms_median": round(kern["single_launch_median"], 5),
+                "single_launch_ms_p10": round(kern["single_launch_p10"], 5),
+                "single_launch_ms_p90": round(kern["single_launch_p90"], 5)}
 
     out = {
         "metric": METRIC, "value": round(value, 2), "unit": unit, "n_gpus": 1, "steps": args.steps,
@@ -465,6 +547,12 @@ def main():
                    "head_dim": d, "input_sets_rotated": n_sets, "step": "pad + blockmap + attention"},
         "roofline": roof,
     }
+    if not args.no_peaks:
+        pk = measured_peaks(torch)
+        out["measured_peaks"] = pk
+        meas = pk["hbm_read_GBps"] if roof["unit"] == "GB/s" else pk["mfma_f16_TFLOPs"]
+        roof["peak_measured"] = meas
+        roof["frac_of_measured"] = round(roof["achieved"] / meas, 4)
     if runner.kind == "decode":
         out["kv_bytes_per_step"] = c["kv_bytes"]
         out["pct_hbm_peak_kv"] = round(100 * value / HBM_PEAK_GBS, 2)
@@ -482,7 +570,11 @@ def main():
             cc = counts(r.w)
             ms = s * 1e3 / steps
             entry = {"ms_per_step": round(ms, 5), "kernel_ms_mean": round(k["mean"], 5),
-                     "single_launch_ms_median": round(k["single_launch_median"], 5)}
+                     "single_launch_ms_median": round(k["single_launch_median"], 5),
+                     "single_launch_ms_p10": round(k["single_launch_p10"], 5),
+                     "single_launch_ms_p90": round(k["single_launch_p90"], 5)}
+            if not other.startswith("prefill"):
+                entry["kernel_split"] = {1: "DIMS", 2: "KEYS"}[decode_kernel_label(r.w)]
             if other.startswith("prefill"):
                 entry["tflops_step"] = round(cc["flops"] / (ms * 1e-3) / 1e12, 2)
                 entry["tflops_kernel"] = round(cc["flops"] / (k["mean"] * 1e-3) / 1e12, 2)

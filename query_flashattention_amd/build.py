@@ -19,6 +19,7 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libds4attn.so")
+PROBES_LIB = os.path.join(PKG, "libds4probes.so")
 ARCH = "gfx950"
 
 # Packed fp32 instructions stay off: only scalar/vector fp32 code is emitted.
@@ -61,7 +62,23 @@ def build(verbose: bool = False) -> str:
     os.replace(tmp, LIB)
     if verbose:
         print(f"built {LIB}")
+    build_probes(verbose)
     return LIB
+
+
+def build_probes(verbose: bool = False) -> str:
+    """The measurement probes (achievable HBM read bandwidth and MFMA throughput)
+    as their own library, libds4probes.so; only the benchmark loads it."""
+    src = os.path.join(PKG, "probes", "peaks.hip")
+    tmp = PROBES_LIB + ".tmp"
+    cmd = [hipcc(), *COMMON, "-shared", src, "-o", tmp]
+    res = subprocess.run(cmd, capture_output=True, text=True)
+    if res.returncode != 0:
+        raise RuntimeError(f"hipcc failed on {src}:\n{res.stdout}\n{res.stderr}")
+    os.replace(tmp, PROBES_LIB)
+    if verbose:
+        print(f"built {PROBES_LIB}")
+    return PROBES_LIB
 
 
 if __name__ == "__main__":
