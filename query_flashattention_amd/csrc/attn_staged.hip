@@ -1216,6 +1216,41 @@ __global__ __launch_bounds__(256, MODE == kSplitHeads ? 2 : 1) void attn_staged_
     return;
   }
   const float inv = lt > 0.f ? 1.f / lt : 0.f;
+  if constexpr (MODE == kSplitHeads) {
+    // HEADS: the 64 x 512 float32 outputs leave through the free tile buffers, so
+    // that every store writes 1 KiB of one row (stores shaped like the accumulator,
+    // 16 rows x 64 bytes each, cost the vector-memory path about three times as
+    // much).  Per pass WPP waves write their 16 rows; then all four waves store them.
+    typedef __attribute__((address_space(3))) char lds_w;
+    lds_w *kts = (lds_w *)(__attribute__((address_space(3))) void *)kt0;
+    lds_w *vts = (lds_w *)(__attribute__((address_space(3))) void *)vt0;
+    constexpr int kORow = 2064;         // 512 float32, padded
+    constexpr int RPT = KT / kORow;     // rows per tile buffer: float16 16, FP8 8
+    static_assert((RPT == 16 || RPT == 8) && RPT * kORow <= VT, "output rows fit the tiles");
+    constexpr int WPP = 2 * RPT / 16;   // waves per pass
+    auto slot = [&](int sl) __attribute__((always_inline)) -> lds_w * {
+      return (sl < RPT ? kts : vts) + (sl % RPT) * kORow;
+    };
+#pragma unroll
+    for (int pass = 0; pass < 4 / WPP; ++pass) {
+      const int wj = w - pass * WPP;
+      if (wj >= 0 && wj < WPP) {
+        lds_w *row = slot(16 * wj + c16) + 16 * g;
+#pragma unroll
+        for (int dt = 0; dt < NDT; ++dt) *(__attribute__((address_space(3))) floatx4 *)(row + 64 * dt) = o[dt] * inv;
+      }
+      lds_barrier();
+#pragma unroll
+      for (int k = 0; k < RPT; ++k) {
+        const int sl = (RPT / 2) * w + (k >> 1), half = k & 1;
+        const int head = hg * HG + 16 * (pass * WPP + sl / 16) + (sl % 16);
+        const floatx4 v = *(const __attribute__((address_space(3))) floatx4 *)(slot(sl) + 1024 * half + lane16);
+        *(floatx4 *)((float *)(p.o + b * p.o_sb + t * p.o_st + (int64_t)head * p.o_sh) + 256 * half + 4 * lane) = v;
+      }
+      if (pass + 1 < 4 / WPP) lds_barrier();
+    }
+    return;
+  }
   float *ob = (float *)(p.o + b * p.o_sb + t * p.o_st + (int64_t)h * p.o_sh) + d0 + 4 * g;
 #pragma unroll
   for (int dt = 0; dt < NDT; ++dt) *(floatx4 *)(ob + 16 * dt) = o[dt] * inv;
