@@ -1203,19 +1203,41 @@ __global__ __launch_bounds__(256, MODE == kSplitHeads ? 2 : 1) void attn_staged_
   float lt = l;
   lt = xor_sum(lt, 16);
   lt = xor_sum(lt, 32);
-  if (MODE == kSplitDims && nsplit > 1) {
-    // partial record of this split: unnormalised O, then the maxima and the sums
-    char *rec = p.ws + ((int64_t)L * nsplit + split) * kSplitRecord;
-    float *ob = (float *)rec + c16 * 512 + d0 + 4 * g;
+  const float inv = lt > 0.f ? 1.f / lt : 0.f;
+  if constexpr (MODE == kSplitDims) {
+    // DIMS: the workgroup's 16 x 512 float32 outputs (or, for a split part, its
+    // unnormalised partial record) leave through the free tile buffers, so that
+    // every store writes 1 KiB of one row instead of 16 rows x 64 bytes
+    typedef __attribute__((address_space(3))) char lds_w;
+    lds_w *kts = (lds_w *)(__attribute__((address_space(3))) void *)kt0;
+    lds_w *vts = (lds_w *)(__attribute__((address_space(3))) void *)vt0;
+    constexpr int kORow = 2064;                          // 512 float32, padded
+    constexpr int RPT = KT / kORow < 16 ? KT / kORow : 16;   // rows per tile buffer
+    static_assert(2 * RPT >= 16 && RPT * kORow <= VT, "the 16 output rows fit the tiles");
+    auto slot = [&](int sl) __attribute__((always_inline)) -> lds_w * {
+      return (sl < RPT ? kts : vts) + (sl % RPT) * kORow;
+    };
+    const bool part = nsplit > 1;
+    const float sc = part ? 1.f : inv;
+    lds_w *row = slot(c16) + 4 * d0 + 16 * g;
 #pragma unroll
-    for (int dt = 0; dt < NDT; ++dt) *(floatx4 *)(ob + 16 * dt) = o[dt];
-    if (w == 0 && g == 0) {
+    for (int dt = 0; dt < NDT; ++dt) *(__attribute__((address_space(3))) floatx4 *)(row + 64 * dt) = o[dt] * sc;
+    lds_barrier();
+    char *rec = part ? p.ws + ((int64_t)L * nsplit + split) * kSplitRecord : nullptr;
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      const int r = 4 * w + (k >> 1), half = k & 1;
+      const floatx4 v = *(const __attribute__((address_space(3))) floatx4 *)(slot(r) + 1024 * half + lane16);
+      float *dst = part ? (float *)rec + r * 512 : (float *)(p.o + b * p.o_sb + t * p.o_st + (int64_t)(hg * HG + r) * p.o_sh);
+      *(floatx4 *)(dst + 256 * half + 4 * lane) = v;
+    }
+    if (part && w == 0 && g == 0) {
+      // then the maxima and the sums
       ((float *)(rec + 16 * 512 * 4))[c16] = m;
       ((float *)(rec + 16 * 512 * 4))[16 + c16] = lt;
     }
     return;
   }
-  const float inv = lt > 0.f ? 1.f / lt : 0.f;
   if constexpr (MODE == kSplitHeads) {
     // HEADS: the 64 x 512 float32 outputs leave through the free tile buffers, so
     // that every store writes 1 KiB of one row (stores shaped like the accumulator,
