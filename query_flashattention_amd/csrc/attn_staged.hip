@@ -71,7 +71,9 @@ __global__ __launch_bounds__(256, MODE == kSplitHeads ? 2 : 1) void attn_staged_
   // (FP8 tiles are half the size: DIMS keeps four blocks in flight)
   constexpr int NBUF = MODE == kSplitHeads ? 1 : (FP8 ? 4 : 2);
   constexpr int KPD = KEYS ? 4 : 2;   // K operand reads in flight (k-steps)
-  constexpr int VPD = KEYS ? 8 : 4;   // V operand reads in flight (output tiles)
+  // V operand reads in flight (output tiles); FP8 rows in HEADS take one fewer,
+  // which keeps their conversions within 256 registers without spilling
+  constexpr int VPD = KEYS ? 8 : (MODE == kSplitHeads && FP8 ? 3 : 4);
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave index (uniform)

@@ -103,10 +103,12 @@ constexpr int kMaskRing = 128, kMaskChunk = 64;
 constexpr int kTable = 256 / kRowsPerBlock;   // dense blocks masked at the start, a row per thread
 
 // Tile rows are padded so that rows start on different banks while every operand
-// address stays affine (base + immediate): K rows every 1040 bytes (the 16 rows of
-// an A operand spread over 16-byte bank groups), V rows every 1056 bytes (the 4
-// rows x 32 bytes of a transpose read spread over 8-byte bank groups).
-constexpr int kKRow = 1040, kVRow = 1056;
+// address stays affine (base + immediate).  Both K and V rows are 1056 bytes apart
+// (32 bytes past a multiple of 256): the 16-byte K operand reads of 16 rows and the
+// 4 rows x 32 bytes of a V transpose read then meet no bank conflict (rocprofv3
+// SQ_LDS_BANK_CONFLICT reads 0).  K rows 1040 bytes apart (16 past a multiple of
+// 256) made the K reads conflict: about one stall cycle per LDS instruction.
+constexpr int kKRow = 1056, kVRow = 1056;
 constexpr int kKTile = 32 * kKRow, kVTile = 32 * kVRow;
 
 // FP8 tiles (512-byte rows of E4M3 codes).  One transfer moves a pair of rows,
