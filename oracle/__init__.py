@@ -20,9 +20,15 @@ Modules:
 * ``brute`` -- an independent pure-Python formulation over a materialised
   -inf mask (lists and ``math.exp`` only), used to pin ``reference`` on tiny
   inputs.
+* ``fp8`` -- the FP8 (E4M3, per-row scale) quantize step and its inverse.
+* ``topk`` -- the indexer's top-k selection from given scores.
+* ``compress`` -- compressor pooling of raw rows into compressed rows, with the
+  rolling state of the incomplete group.
 
-Every function is pinned by at least one check in ``tests/test_oracle.py``
+Every function is pinned by at least one check in ``tests/test_oracle*.py``
 (brute force, closed forms, invariants); no function is "parity unpinned".
+``compress`` is pinned to its stated reading of the pages (which name the
+compressor's state but not its formula), not to values the pages print.
 """
 
 from . import reference, brute  # noqa: F401
