@@ -12,8 +12,9 @@
  *   ds4attn_decode    fused Q.K^T, online softmax and P.V (tuned for few tokens)
  *   ds4attn_prefill   the same computation, tuned for long token chunks
  *
- * and two steps around it: ds4attn_quantize_fp8 (K/V rows into the FP8 cache
- * format) and ds4attn_topk (an index list from given scores).
+ * and three steps around it: ds4attn_quantize_fp8 (K/V rows into the FP8 cache
+ * format), ds4attn_topk (an index list from given scores) and ds4attn_compress
+ * (raw rows pooled into compressed rows).
  *
  * Pages the operations follow:
  *   [P-Metal] "How DeepSeek V4 Flash Model Inference Works on Apple Silicon with
@@ -309,6 +310,46 @@ int ds4attn_quantize_fp8(const void *x, int32_t dtype, int32_t batch, int32_t n_
                          int64_t x_stride_b, int64_t x_stride_row, uint8_t *codes,
                          int64_t code_stride_b, int64_t code_stride_row, float *scales,
                          int64_t scale_stride_b, void *stream);
+
+/*
+ * ds4attn_compress -- the compressor step of a compressed layer ([P-DS4]
+ * "Architecture Deep Dive", Layer Compression and KV Cache Design: the compressor
+ * keeps a rolling KV/score state and appends a pooled row at every ratio
+ * boundary, every 4 raw rows in ratio-4 layers and every 128 in ratio-128 layers).
+ * The pages name the state but not the pooling formula; this library's reading:
+ * every raw row carries a score per element, and element d of a compressed row is
+ * the softmax over the group's rows i of the scores s_i[d], weighting kv_i[d].
+ *
+ * The stream of a sequence is its n_state pending rows followed by its n_new new
+ * rows.  Rows c*ratio .. c*ratio + ratio - 1 of the stream form group c, for the
+ * n_out = (n_state + n_new) / ratio complete groups, and
+ *     comp[c][d] = sum_i exp(s_i[d] - M) kv_i[d] / sum_i exp(s_i[d] - M),  M = max_i s_i[d],
+ * computed in float32 and rounded once to float16.  The new state is the trailing
+ * (n_state + n_new) mod ratio rows of the stream, written to state rows 0, 1, ...
+ *
+ *   state_kv     device float16 [batch][ratio][head_dim], packed rows (row r of
+ *                sequence b at byte b*state_kv_stride_b + r*2*head_dim); rows
+ *                [0, n_state) are read, and the new state is written in place
+ *   state_score  device float32, the same layout with 4*head_dim bytes per row
+ *   kv_new       device float16 [batch][n_new][head_dim], packed rows, batch stride in bytes
+ *   score_new    device float32 [batch][n_new][head_dim], packed rows
+ *   comp         device float16 output [batch][n_out][head_dim], packed rows (the
+ *                caller points it at its next free compressed row); may be NULL
+ *                when n_out is 0
+ * The caller advances its own counts: n_state' = (n_state + n_new) mod ratio and
+ * n_comp' = n_comp + n_out.  Scores must be finite.  head_dim in {64, 128, 256,
+ * 512}; 1 <= ratio <= 1024 and 0 <= n_state < ratio (the same for every sequence);
+ * pointers and batch strides 16-byte aligned; batch strides large enough for their
+ * rows when batch > 1.  The state buffers must not overlap each other or the new
+ * rows, and comp must not overlap any input.  Both kernels run on `stream`, the
+ * pooling first (it reads the old state), then the state update.
+ * Returns DS4ATTN_OK, DS4ATTN_E_INVAL, DS4ATTN_E_UNSUPPORTED or DS4ATTN_E_HIP; on an
+ * error nothing is enqueued.
+ */
+int ds4attn_compress(int32_t batch, int32_t head_dim, int32_t ratio, int32_t n_state, int32_t n_new,
+                     void *state_kv, int64_t state_kv_stride_b, float *state_score, int64_t state_score_stride_b,
+                     const void *kv_new, int64_t kv_new_stride_b, const float *score_new,
+                     int64_t score_new_stride_b, void *comp, int64_t comp_stride_b, void *stream);
 
 /* A static, NUL-terminated description of a status code. */
 const char *ds4attn_status_string(int status);

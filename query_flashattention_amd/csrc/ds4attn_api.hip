@@ -342,6 +342,52 @@ int ds4attn_quantize_fp8(const void *x, int32_t dtype, int32_t batch, int32_t n_
   return e == hipSuccess ? DS4ATTN_OK : DS4ATTN_E_HIP;
 }
 
+int ds4attn_compress(int32_t batch, int32_t head_dim, int32_t ratio, int32_t n_state, int32_t n_new,
+                     void *state_kv, int64_t state_kv_stride_b, float *state_score, int64_t state_score_stride_b,
+                     const void *kv_new, int64_t kv_new_stride_b, const float *score_new,
+                     int64_t score_new_stride_b, void *comp, int64_t comp_stride_b, void *stream) {
+  if (batch < 0 || n_new < 0 || head_dim <= 0) return DS4ATTN_E_INVAL;
+  if (ratio < 1 || n_state < 0 || n_state >= ratio) return DS4ATTN_E_INVAL;
+  if (!head_dim_ok(head_dim) || ratio > kMaxCompressRatio) return DS4ATTN_E_UNSUPPORTED;
+  if (batch == 0 || n_new == 0) return DS4ATTN_OK;
+  const int64_t n_out = ((int64_t)n_state + n_new) / ratio;
+  if ((int64_t)n_state + n_new > 0x7fffffffLL || (int64_t)batch * n_out * head_dim > 0x7fffffffLL ||
+      (int64_t)batch * n_new * head_dim > 0x7fffffffLL)
+    return DS4ATTN_E_UNSUPPORTED;
+  const int64_t vrow = 2LL * head_dim, srow = 4LL * head_dim;
+  if (!state_kv || !state_score || !kv_new || !score_new || !aligned16(state_kv) || !aligned16(state_score) ||
+      !aligned16(kv_new) || !aligned16(score_new))
+    return DS4ATTN_E_INVAL;
+  if (n_out > 0 && (!comp || !aligned16(comp))) return DS4ATTN_E_INVAL;
+  if (!stride16(state_kv_stride_b) || !stride16(state_score_stride_b) || !stride16(kv_new_stride_b) ||
+      !stride16(score_new_stride_b) || !stride16(comp_stride_b))
+    return DS4ATTN_E_INVAL;
+  if (batch > 1 && (state_kv_stride_b < ratio * vrow || state_score_stride_b < ratio * srow ||
+                    kv_new_stride_b < n_new * vrow || score_new_stride_b < n_new * srow ||
+                    (n_out > 0 && comp_stride_b < n_out * vrow)))
+    return DS4ATTN_E_INVAL;
+  const int64_t st_kv_len = (batch - 1) * state_kv_stride_b + ratio * vrow;
+  const int64_t st_sc_len = (batch - 1) * state_score_stride_b + ratio * srow;
+  const int64_t kv_len = (batch - 1) * kv_new_stride_b + n_new * vrow;
+  const int64_t sc_len = (batch - 1) * score_new_stride_b + n_new * srow;
+  const int64_t c_len = (batch - 1) * comp_stride_b + n_out * vrow;
+  // the state is updated in place: it must not overlap the new rows or each other;
+  // the compressed rows must not overlap anything read
+  if (ranges_overlap(state_kv, st_kv_len, state_score, st_sc_len) ||
+      ranges_overlap(state_kv, st_kv_len, kv_new, kv_len) || ranges_overlap(state_kv, st_kv_len, score_new, sc_len) ||
+      ranges_overlap(state_score, st_sc_len, kv_new, kv_len) ||
+      ranges_overlap(state_score, st_sc_len, score_new, sc_len))
+    return DS4ATTN_E_INVAL;
+  if (n_out > 0 && (ranges_overlap(comp, c_len, state_kv, st_kv_len) ||
+                    ranges_overlap(comp, c_len, state_score, st_sc_len) ||
+                    ranges_overlap(comp, c_len, kv_new, kv_len) || ranges_overlap(comp, c_len, score_new, sc_len)))
+    return DS4ATTN_E_INVAL;
+  const hipError_t e = launch_compress(state_kv, state_score, state_kv_stride_b, state_score_stride_b, n_state,
+                                       kv_new, score_new, kv_new_stride_b, score_new_stride_b, n_new, batch,
+                                       head_dim, ratio, comp, comp_stride_b, (hipStream_t)stream);
+  return e == hipSuccess ? DS4ATTN_OK : DS4ATTN_E_HIP;
+}
+
 const char *ds4attn_status_string(int status) {
   switch (status) {
     case DS4ATTN_OK: return "ok";

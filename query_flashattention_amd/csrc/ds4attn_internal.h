@@ -5,6 +5,7 @@
 // [P-DS4]   = page "DwarfStar 4 (DS4) -- DeepSeek V4 Flash Inference Engine".
 #pragma once
 
+#include <hip/hip_fp16.h>
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -145,5 +146,12 @@ constexpr int32_t kMaxTopkN = (1 << 30) - 1;  // scores per row (row bytes fit a
 constexpr int kMaxTopkK = 2048;               // selected entries per row (staged in LDS)
 hipError_t launch_topk(const float *scores, int64_t rows, int n, int64_t s_stride, int k, int32_t *idx,
                        int64_t o_stride, hipStream_t s);
+// Compressor step: pool every complete group of `ratio` stream rows (state rows,
+// then new rows) into a float16 row of comp, then keep the trailing rows as the state.
+constexpr int kMaxCompressRatio = 1024;
+hipError_t launch_compress(void *state_kv, float *state_score, int64_t state_kv_sb, int64_t state_score_sb,
+                           int n_state, const void *kv_new, const float *score_new, int64_t kv_new_sb,
+                           int64_t score_new_sb, int n_new, int B, int D, int ratio, void *comp,
+                           int64_t comp_sb, hipStream_t s);
 
 }  // namespace ds4attn

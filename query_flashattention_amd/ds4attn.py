@@ -50,7 +50,8 @@ class Args(ctypes.Structure):
 
 EXPORTS = ("ds4attn_pad", "ds4attn_blockmap", "ds4attn_blockmap_dims", "ds4attn_decode",
            "ds4attn_prefill", "ds4attn_prefill_bq", "ds4attn_topk", "ds4attn_quantize_fp8",
-           "ds4attn_decode_split", "ds4attn_decode_workspace_bytes", "ds4attn_status_string")
+           "ds4attn_decode_split", "ds4attn_decode_workspace_bytes", "ds4attn_compress",
+           "ds4attn_status_string")
 
 _lib = None
 
@@ -76,9 +77,11 @@ def lib() -> ctypes.CDLL:
         h.ds4attn_decode_workspace_bytes.argtypes = [ctypes.POINTER(Args), _i32, ctypes.POINTER(_i64)]
         h.ds4attn_quantize_fp8.argtypes = [_c_void_p, _i32, _i32, _i32, _i32, _i64, _i64, _c_void_p,
                                            _i64, _i64, _c_void_p, _i64, _c_void_p]
+        h.ds4attn_compress.argtypes = [_i32, _i32, _i32, _i32, _i32, _c_void_p, _i64, _c_void_p, _i64,
+                                       _c_void_p, _i64, _c_void_p, _i64, _c_void_p, _i64, _c_void_p]
         for name in ("ds4attn_pad", "ds4attn_blockmap", "ds4attn_blockmap_dims", "ds4attn_decode",
                      "ds4attn_prefill", "ds4attn_prefill_bq", "ds4attn_topk", "ds4attn_quantize_fp8",
-                     "ds4attn_decode_split", "ds4attn_decode_workspace_bytes"):
+                     "ds4attn_decode_split", "ds4attn_decode_workspace_bytes", "ds4attn_compress"):
             getattr(h, name).restype = _i32
         h.ds4attn_status_string.argtypes = [_i32]
         h.ds4attn_status_string.restype = ctypes.c_char_p
@@ -266,6 +269,36 @@ def quantize_fp8(x: torch.Tensor, stream=None):
     scales = torch.empty((b, n), dtype=torch.float32, device=x.device)
     ds4attn_quantize_fp8(x, codes, scales, stream=stream)
     return codes, scales
+
+
+def ds4attn_compress(state_kv: torch.Tensor, state_score: torch.Tensor, n_state: int, kv_new: torch.Tensor,
+                     score_new: torch.Tensor, ratio: int, comp: Optional[torch.Tensor], stream=None) -> int:
+    """Compressor step: state_kv [B, ratio, D] float16 and state_score [B, ratio, D]
+    float32 (rows [0, n_state) pending, updated in place), new rows kv_new [B, n, D]
+    float16 and score_new [B, n, D] float32 -> comp [B, >= n_out, D] float16 (rows
+    0 .. n_out - 1 written).  Returns n_out = (n_state + n) // ratio; the new state
+    count is (n_state + n) % ratio."""
+    b, n, d = kv_new.shape
+    if state_kv.dtype != torch.float16 or kv_new.dtype != torch.float16 or \
+            state_score.dtype != torch.float32 or score_new.dtype != torch.float32:
+        raise TypeError("ds4attn_compress takes float16 rows and float32 scores")
+    if comp is not None and comp.dtype != torch.float16:
+        raise TypeError("ds4attn_compress writes float16 rows")
+    for t in (state_kv, state_score, kv_new, score_new) + ((comp,) if comp is not None else ()):
+        if t.dim() != 3 or t.shape[0] != b or t.shape[2] != d or t.stride(2) != 1 or \
+                (t.shape[1] > 1 and t.stride(1) != d):
+            raise ValueError("ds4attn_compress needs [B, rows, D] tensors with packed rows")
+    if state_kv.shape[1] < ratio or state_score.shape[1] < ratio:
+        raise ValueError("the state buffers hold ratio rows")
+    n_out = (n_state + n) // ratio
+    if n_out and (comp is None or comp.shape[1] < n_out):
+        raise ValueError("comp holds fewer than n_out rows")
+    _check(lib().ds4attn_compress(b, d, ratio, n_state, n, state_kv.data_ptr(), state_kv.stride(0) * 2,
+                                  state_score.data_ptr(), state_score.stride(0) * 4, kv_new.data_ptr(),
+                                  kv_new.stride(0) * 2, score_new.data_ptr(), score_new.stride(0) * 4,
+                                  _ptr(comp), comp.stride(0) * 2 if comp is not None else 0,
+                                  _stream(stream)), "ds4attn_compress")
+    return n_out
 
 
 def ds4attn_prefill_bq() -> int:

@@ -331,3 +331,29 @@ def indexer_scores(seed: int, rows: int, n: int, kind: str = "normal") -> torch.
         special = bits[which].view(torch.float32)
         return torch.where(pick, special, s)
     raise ValueError(f"unknown score kind {kind!r}")
+
+
+@dataclass
+class CompressInputs:
+    """One compressor call's inputs: the rolling state (ratio rows, the first
+    n_state pending) and the new raw rows, with a score per element."""
+    ratio: int
+    n_state: int
+    state_kv: torch.Tensor      # float16 [B, ratio, D]
+    state_score: torch.Tensor   # float32 [B, ratio, D]
+    kv_new: torch.Tensor        # float16 [B, n_new, D]
+    score_new: torch.Tensor     # float32 [B, n_new, D]
+
+
+def compress_inputs(seed: int, batch: int, ratio: int, n_state: int, n_new: int,
+                    head_dim: int = HEAD_DIM, score_std: float = 1.0) -> CompressInputs:
+    """Seeded compressor inputs (the learned score projection is not on the pages,
+    so scores are drawn).  Draw order: state rows, state scores, new rows, new
+    scores; rows N(0, 1) rounded to float16, scores N(0, score_std) float32.  State
+    rows past n_state are drawn too (the step must neither read nor keep them)."""
+    g = torch.Generator().manual_seed(seed)
+    st_kv = _normal(g, (batch, ratio, head_dim), torch.float16)
+    st_sc = _normal(g, (batch, ratio, head_dim), torch.float32, score_std)
+    kv = _normal(g, (batch, n_new, head_dim), torch.float16)
+    sc = _normal(g, (batch, n_new, head_dim), torch.float32, score_std)
+    return CompressInputs(ratio, n_state, st_kv, st_sc, kv, sc)

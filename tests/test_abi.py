@@ -270,6 +270,38 @@ def test_quantize_rejects_bad_arguments():
     assert q(batch=0, x=None, c=None, s=None) == da.OK
 
 
+def test_compress_rejects_bad_arguments():
+    lib = da.lib()
+    d = 512
+    st_kv, st_sc, kv, sc, comp = (FAKE, FAKE + (1 << 26), FAKE + (2 << 26), FAKE + (3 << 26), FAKE + (4 << 26))
+
+    def c(**kw):
+        p = dict(batch=2, d=d, ratio=4, n_state=3, n_new=10, st_kv=st_kv, st_kv_sb=4 * 2 * d, st_sc=st_sc,
+                 st_sc_sb=4 * 4 * d, kv=kv, kv_sb=10 * 2 * d, sc=sc, sc_sb=10 * 4 * d, comp=comp,
+                 comp_sb=3 * 2 * d)
+        p.update(kw)
+        return lib.ds4attn_compress(p["batch"], p["d"], p["ratio"], p["n_state"], p["n_new"], p["st_kv"],
+                                    p["st_kv_sb"], p["st_sc"], p["st_sc_sb"], p["kv"], p["kv_sb"], p["sc"],
+                                    p["sc_sb"], p["comp"], p["comp_sb"], None)
+
+    assert c(ratio=0) == da.E_INVAL
+    assert c(n_state=4) == da.E_INVAL                # the state holds fewer than ratio rows
+    assert c(n_state=-1) == da.E_INVAL
+    assert c(n_new=-1) == da.E_INVAL
+    assert c(d=96) == da.E_UNSUPPORTED
+    assert c(ratio=2048, n_state=0) == da.E_UNSUPPORTED
+    assert c(st_kv=st_kv + 8) == da.E_INVAL          # alignment
+    assert c(kv_sb=10 * 2 * d - 16) == da.E_INVAL    # sequences' new rows overlap
+    assert c(st_sc_sb=3 * 4 * d) == da.E_INVAL       # a state shorter than ratio rows
+    assert c(comp_sb=2 * 2 * d) == da.E_INVAL        # fewer than n_out = 3 compressed rows
+    assert c(comp=None) == da.E_INVAL                # n_out > 0 needs an output
+    assert c(comp=kv + 64) == da.E_INVAL             # output overlaps an input
+    assert c(st_kv=kv + 1024) == da.E_INVAL          # state overlaps the new rows
+    assert c(st_sc=st_kv + 16) == da.E_INVAL         # the two state buffers overlap
+    assert c(n_new=0) == da.OK                       # nothing to do, nothing launched
+    assert c(batch=0) == da.OK
+
+
 def test_pad_accepts_fp8_rows():
     """E4M3 rows are 1-byte elements: a 512-dim row is 512 bytes; a region that
     fills whole blocks in place launches nothing."""
