@@ -418,6 +418,48 @@ def topk_timing(rows, n, k, n_sets=4, reps=25):
             "rows_per_s": round(rows / (ms * 1e-3), 1)}
 
 
+def compress_timing(b, ratio, n_state, n_new, d=512, n_sets=4, reps=25):
+    """Mean duration of one ds4attn_compress call (pooling, plus the state update when
+    rows remain) over seeded inputs, with its algorithmic bytes: every stream row's
+    values (float16) and scores (float32) read once, the compressed rows and the new
+    state written once."""
+    import torch
+    from query_flashattention_amd import ds4attn as da, workloads
+
+    ins = [workloads.compress_inputs(500 + i, b, ratio, n_state, n_new, d) for i in range(n_sets)]
+    dev = [(ci.state_kv.cuda(), ci.state_score.cuda(), ci.kv_new.cuda(), ci.score_new.cuda()) for ci in ins]
+    n_out = (n_state + n_new) // ratio
+    outs = [torch.empty(b, max(n_out, 1), d, dtype=torch.float16, device="cuda") for _ in range(n_sets)]
+
+    def calls():
+        for (skv, ssc, kv, sc), o in zip(dev, outs):
+            da.ds4attn_compress(skv, ssc, n_state, kv, sc, ratio, o)
+
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        calls()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    gr = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(gr):
+        calls()
+    gr.replay()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        gr.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / (reps * n_sets)
+    n_next = (n_state + n_new) % ratio
+    nbytes = b * ((n_state + n_new) * 6.0 * d + n_out * 2.0 * d + n_next * 6.0 * d)
+    return {"batch": b, "ratio": ratio, "n_state": n_state, "n_new": n_new, "head_dim": d,
+            "compressed_rows_per_seq": n_out, "kernel_us_mean": round(ms * 1e3, 2),
+            "algorithmic_bytes": nbytes, "gbs_kernel": round(nbytes / (ms * 1e-3) / 1e9, 1)}
+
+
 def quantize_timing(b, n, d=512, n_sets=4, reps=25):
     """Mean duration of one ds4attn_quantize_fp8 launch over [b, n, d] float16 rows,
     with its algorithmic bytes (rows read once; codes and scales written once)."""
@@ -604,6 +646,9 @@ def main():
         extra["topk_decode_r4"] = topk_timing(64, 2048, 512)
         # the FP8 quantize step over a 64-sequence x 2048-row cache of float16 rows
         extra["quantize_fp8_64x2048"] = quantize_timing(64, 2048)
+        extra["compress_prefill_r4"] = compress_timing(1, 4, 0, 2048)
+        extra["compress_prefill_r128"] = compress_timing(1, 128, 0, 2048)
+        extra["compress_decode_r128_b64"] = compress_timing(64, 128, 127, 1)
         out["extra"] = extra
 
     if args.cpu_seconds > 0:

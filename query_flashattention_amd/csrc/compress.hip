@@ -8,9 +8,11 @@
 //
 // Memory-bound: per raw row, head_dim float16 values and head_dim float32 scores
 // are read (the scores twice, the second time from L2), and per group one float16
-// row is written.  One thread owns two adjacent elements of one compressed row
-// (4-byte and 8-byte loads, coalesced across the row); threads of a workgroup
-// cover consecutive element pairs, rows and sequences.
+// row is written.  A thread owns two adjacent elements of one compressed row
+// (4-byte and 8-byte loads, coalesced across the row).  Short groups: one thread
+// walks the whole group, and threads of a workgroup cover consecutive element
+// pairs, rows and sequences.  Long groups: the group's rows are split over eight
+// thread slices of a workgroup, combined through LDS.
 #include "ds4attn_internal.h"
 
 namespace ds4attn {
@@ -85,6 +87,76 @@ __global__ __launch_bounds__(256) void compress_pool_kernel(const CompressArgs a
   *((__half2 *)(a.comp + b * a.comp_sb + (int64_t)c * 2 * a.D) + e) = out;
 }
 
+// Long groups (ratio >= kSplitRatio): the group's rows are split over RS thread
+// slices.  A workgroup owns one group and P = 256 / RS element pairs; slice rs takes
+// rows rs, rs + RS, ...  The slices' maxima, then their sums and weighted sums,
+// meet in LDS and are combined in slice order (the same order on every call).
+constexpr int kSplitRatio = 32;
+template <int RS>
+__global__ __launch_bounds__(256) void compress_pool_rows_kernel(const CompressArgs a) {
+  constexpr int P = 256 / RS;
+  __shared__ float2 smax[RS][P];
+  __shared__ float4 ssum[RS][P];
+  const int el = threadIdx.x % P, rs = threadIdx.x / P;
+  const int nchunk = (a.D >> 1) / P;
+  const int chunk = (int)(blockIdx.x % (unsigned)nchunk);
+  const int bc = (int)(blockIdx.x / (unsigned)nchunk);
+  const int c = bc % a.n_out, b = bc / a.n_out;
+  const int e = chunk * P + el;
+  const int r0 = c * a.ratio;
+  float m0 = -INFINITY, m1 = -INFINITY;
+#pragma unroll 4
+  for (int k = rs; k < a.ratio; k += RS) {
+    const __half2 *kv;
+    const float2 *sc;
+    stream_row(a, b, r0 + k, e, &kv, &sc);
+    const float2 s = *sc;
+    m0 = fmaxf(m0, s.x);
+    m1 = fmaxf(m1, s.y);
+  }
+  smax[rs][el] = make_float2(m0, m1);
+  __syncthreads();
+#pragma unroll
+  for (int q = 0; q < RS; ++q) {
+    const float2 x = smax[q][el];
+    m0 = fmaxf(m0, x.x);
+    m1 = fmaxf(m1, x.y);
+  }
+  constexpr float kLog2e = 1.4426950408889634f;
+  float l0 = 0.f, l1 = 0.f, acc0 = 0.f, acc1 = 0.f;
+#pragma unroll 4
+  for (int k = rs; k < a.ratio; k += RS) {
+    const __half2 *kv;
+    const float2 *sc;
+    stream_row(a, b, r0 + k, e, &kv, &sc);
+    const float2 s = *sc;
+    const float2 v = __half22float2(*kv);
+    const float w0 = __builtin_amdgcn_exp2f((s.x - m0) * kLog2e);
+    const float w1 = __builtin_amdgcn_exp2f((s.y - m1) * kLog2e);
+    l0 += w0;
+    l1 += w1;
+    acc0 = fmaf(w0, v.x, acc0);
+    acc1 = fmaf(w1, v.y, acc1);
+  }
+  ssum[rs][el] = make_float4(l0, l1, acc0, acc1);
+  __syncthreads();
+  if (rs == 0) {
+    float4 t = ssum[0][el];
+#pragma unroll
+    for (int q = 1; q < RS; ++q) {
+      const float4 x = ssum[q][el];
+      t.x += x.x;
+      t.y += x.y;
+      t.z += x.z;
+      t.w += x.w;
+    }
+    __half2 out;
+    out.x = __float2half_rn(t.z / t.x);
+    out.y = __float2half_rn(t.w / t.y);
+    *((__half2 *)(a.comp + b * a.comp_sb + (int64_t)c * 2 * a.D) + e) = out;
+  }
+}
+
 // The new state: rows [n_out * ratio, n_state + n_new) of the stream.  With a
 // complete group (n_out > 0) they are all new rows; otherwise the pending rows
 // stay where they are and the new rows follow them.  16 bytes per thread.
@@ -137,9 +209,15 @@ hipError_t launch_compress(void *state_kv, float *state_score, int64_t state_kv_
     a.n_state = n_state;
     a.n_out = n_out;
     a.batch = B;
-    const int64_t total = (int64_t)B * n_out * (D / 2);
-    hipLaunchKernelGGL(compress_pool_kernel, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, s, a,
-                       total);
+    if (ratio >= kSplitRatio) {
+      constexpr int RS = 8;
+      const int64_t blocks = (int64_t)B * n_out * ((D / 2) / (256 / RS));
+      hipLaunchKernelGGL(compress_pool_rows_kernel<RS>, dim3((unsigned)blocks), dim3(256), 0, s, a);
+    } else {
+      const int64_t total = (int64_t)B * n_out * (D / 2);
+      hipLaunchKernelGGL(compress_pool_kernel, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, s, a,
+                         total);
+    }
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
