@@ -260,7 +260,7 @@ int ds4attn_blockmap(const ds4attn_args *a, int32_t bq, uint8_t *blk, void *stre
   const int64_t total = (int64_t)P.B * P.ntiles * P.nbd;
   if (total == 0) return DS4ATTN_OK;
   if (!blk) return DS4ATTN_E_INVAL;
-  if ((total + 3) / 4 > 0x7fffffffLL) return DS4ATTN_E_UNSUPPORTED;
+  if (total > 0x7fffffffLL) return DS4ATTN_E_UNSUPPORTED;   // 32-bit entry indices
   hipError_t e = launch_blockmap(P, blk, (hipStream_t)stream);
   return e == hipSuccess ? DS4ATTN_OK : DS4ATTN_E_HIP;
 }

@@ -80,33 +80,53 @@ hipError_t launch_pad(const void *k, const void *v, const uint8_t *valid, int64_
   return hipSuccess;
 }
 
+// What the map reads, packed so that one burst of scalar loads brings it in (the
+// full attention parameter block made the kernel wait on a chain of dependent
+// argument loads).
+struct BlkParams {
+  const uint8_t *valid0, *valid1;
+  uint8_t *blk;
+  int64_t valid0_sb, valid1_sb;
+  int64_t qk_delta;          // q_pos0 - k_pos0
+  uint32_t total, nbd, ntiles;
+  int T, bq, nb0, n0, n1, window;
+};
+
 // One wave per (sequence, query tile, key block).  Lane r (mod 32) owns row r of
 // the block; lanes 0-31 take the tile's even tokens, lanes 32-63 the odd ones.
 // The block is SKIP when no lane saw a visible pair, FULL when every lane saw
-// only visible pairs (all 32 rows for every token), PARTIAL otherwise.
-__global__ __launch_bounds__(256) void blockmap_kernel(const AttnParams p, uint8_t *__restrict__ blk,
-                                                       int64_t total) {
+// only visible pairs (all 32 rows for every token), PARTIAL otherwise.  Index
+// arithmetic is 32-bit: the map has fewer than 2^31 entries.
+__global__ __launch_bounds__(256) void blockmap_kernel(const BlkParams p) {
   const int lane = threadIdx.x & 63;
-  const int64_t wid = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (wid >= total) return;  // whole wave exits together
+  const uint32_t wid = blockIdx.x * 4u + (threadIdx.x >> 6);
+  if (wid >= p.total) return;  // whole wave exits together
   const int j = (int)(wid % p.nbd);
-  const int64_t bt = wid / p.nbd;
-  const int64_t tile = bt % p.ntiles;
+  const uint32_t bt = wid / p.nbd;
+  const int tile = (int)(bt % p.ntiles);
   const int b = (int)(bt / p.ntiles);
   const int r = lane & 31;
-  const int t0 = (int)(tile * p.bq);
+  const int t0 = tile * p.bq;
   const int t1 = min(p.T, t0 + p.bq);
   bool any = false, all = true;
   if (j < p.nb0) {
     const int row = j * kRowsPerBlock + r;
+    bool live = row < p.n0;
+    if (live && p.valid0) live = p.valid0[b * p.valid0_sb + row] != 0;
     for (int t = t0 + (lane >> 5); t < t1; t += 2) {
-      const bool vis = r0_visible(p, b, t, row);
+      bool vis = live;
+      if (p.window > 0) {
+        const int64_t d = p.qk_delta + t - row;
+        vis = vis && d >= 0 && d < p.window;
+      }
       any |= vis;
       all &= vis;
     }
   } else {
     // dense region 1: visibility does not depend on the token
-    const bool vis = r1_visible(p, b, (j - p.nb0) * kRowsPerBlock + r);
+    const int c = (j - p.nb0) * kRowsPerBlock + r;
+    bool vis = c < p.n1;
+    if (vis && p.valid1) vis = p.valid1[b * p.valid1_sb + c] != 0;
     if (t0 + (lane >> 5) < t1) {
       any = vis;
       all = vis;
@@ -114,14 +134,29 @@ __global__ __launch_bounds__(256) void blockmap_kernel(const AttnParams p, uint8
   }
   const unsigned long long many = __ballot(any);
   const unsigned long long mall = __ballot(all);
-  if (lane == 0) blk[wid] = (uint8_t)(many == 0ull ? kSkip : (mall == ~0ull ? kFull : kPartial));
+  if (lane == 0) p.blk[wid] = (uint8_t)(many == 0ull ? kSkip : (mall == ~0ull ? kFull : kPartial));
 }
 
 hipError_t launch_blockmap(const AttnParams &p, uint8_t *blk, hipStream_t s) {
   const int64_t total = (int64_t)p.B * p.ntiles * p.nbd;
   if (total == 0) return hipSuccess;
-  hipLaunchKernelGGL(blockmap_kernel, dim3((unsigned)((total + 3) / 4)), dim3(256), 0, s, p, blk,
-                     total);
+  BlkParams q;
+  q.valid0 = p.valid0;
+  q.valid1 = p.valid1;
+  q.blk = blk;
+  q.valid0_sb = p.valid0_sb;
+  q.valid1_sb = p.valid1_sb;
+  q.qk_delta = p.qk_delta;
+  q.total = (uint32_t)total;
+  q.nbd = (uint32_t)p.nbd;
+  q.ntiles = (uint32_t)p.ntiles;
+  q.T = p.T;
+  q.bq = p.bq;
+  q.nb0 = p.nb0;
+  q.n0 = p.n0;
+  q.n1 = p.n1;
+  q.window = p.window;
+  hipLaunchKernelGGL(blockmap_kernel, dim3((unsigned)((total + 3) / 4)), dim3(256), 0, s, q);
   return hipGetLastError();
 }
 
