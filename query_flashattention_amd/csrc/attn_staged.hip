@@ -74,6 +74,12 @@ __global__ __launch_bounds__(256, MODE == kSplitHeads ? 2 : 1) void attn_staged_
   // V operand reads in flight (output tiles); FP8 rows in HEADS take one fewer,
   // which keeps their conversions within 256 registers without spilling
   constexpr int VPD = KEYS ? 8 : (MODE == kSplitHeads && FP8 ? 3 : 4);
+  // One field of every 64-byte line of the parameter block is read here, so that
+  // the block arrives in one burst of scalar loads; the code below then finds each
+  // field in the scalar cache instead of waiting one memory round trip per line in
+  // the order it first needs them (four to five serial rounds before the first
+  // key-block transfer otherwise).
+  asm volatile("" ::"s"(p.q), "s"(p.B), "s"(p.valid0), "s"(p.valid1_sb), "s"(p.vs1), "s"(p.nbd));
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave index (uniform)
