@@ -98,6 +98,7 @@ struct BlkParams {
 // only visible pairs (all 32 rows for every token), PARTIAL otherwise.  Index
 // arithmetic is 32-bit: the map has fewer than 2^31 entries.
 __global__ __launch_bounds__(256) void blockmap_kernel(const BlkParams p) {
+  asm volatile("" ::"s"(p.valid0), "s"(p.bq));   // both lines of the block in one burst
   const int lane = threadIdx.x & 63;
   const uint32_t wid = blockIdx.x * 4u + (threadIdx.x >> 6);
   if (wid >= p.total) return;  // whole wave exits together
