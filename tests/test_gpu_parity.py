@@ -307,3 +307,31 @@ def test_split_decode_random(label, kw, splits):
     _compare(no_map.double().numpy(), want, label + " no map")
     if label == "split_masked_tokens":
         assert (with_map[0, :3] == 0).all()   # tokens 0..2 see no row in any part: exact zeros
+
+
+def test_split_decode_reuses_its_workspace():
+    """One workspace serves split calls of different sizes and work splits in a row
+    (its contents on entry do not matter); each result matches the oracle."""
+    ws = None
+    for name, flags in (("decode_r128", 0), ("decode_r128_b64", da.FLAG_DECODE_DIMS), ("decode_r128", da.FLAG_DECODE_KEYS),
+                        ("decode_r128", 0)):
+        w = wl.named(name)
+        dp = pipeline.to_device(w, DEV)
+        dp.flags = flags
+        dp.r0.pad_in_place()
+        if dp.r1 is not None:
+            dp.r1.pad_in_place()
+        a = dp.args()
+        need = da.ds4attn_decode_workspace_bytes(a, 4)
+        if ws is None:
+            # large enough for the 64-sequence batch too; filled with a byte pattern
+            ws = torch.full((need * 64,), 0x7F, dtype=torch.uint8, device=DEV)
+        assert need <= ws.numel()
+        blk = da.blockmap(a, 1, DEV)
+        da.ds4attn_decode_split(a, dp.q, blk, 1, dp.o, 4, ws)
+        torch.cuda.synchronize()
+        out = dp.o.cpu().double().numpy()
+        b = w.q.shape[0]
+        seqs = [0] if b == 1 else [0, 17, 63]
+        want = ref.attention(ref.from_workload(w), tokens=[(s, 0) for s in seqs])
+        _compare(out[seqs, 0], want, f"{name} split 4 flags {flags}, reused workspace")
