@@ -24,7 +24,9 @@
 //   * masked V rows are zeroed in LDS before use, so whatever a masked row holds
 //     never reaches the output; masked scores are -inf;
 //   * the softmax reference max moves lazily (see kRescaleSlack), so O is rescaled
-//     only when a block raises a row's max by more than 2^8.
+//     only when a block raises a row's max by more than 2^8;
+//   * O leaves through non-temporal (streaming) stores: nothing reads it back in
+//     the launch, and cached stores would evict K/V rows other workgroups reuse.
 // Two ways of splitting the work over the four waves:
 //   HEADS (HG = 64, prefill): wave w owns heads 16w..16w+15 over the full head
 //         dimension; no cross-wave exchange; one workgroup per token fetches each
@@ -986,7 +988,7 @@ __global__ __launch_bounds__(256, MODE == kSplitHeads ? 2 : 1) void attn_staged_
     const float inv = lall > 0.f ? 1.f / lall : 0.f;
     float *ob = (float *)(p.o + b * p.o_sb + t * p.o_st + (int64_t)h * p.o_sh) + 128 * w + 4 * g;
 #pragma unroll
-    for (int k = 0; k < 8; ++k) *(floatx4 *)(ob + 16 * k) = acc[k] * inv;
+    for (int k = 0; k < 8; ++k) __builtin_nontemporal_store(acc[k] * inv, (floatx4 *)(ob + 16 * k));
     return;
   }
 
@@ -1237,7 +1239,7 @@ __global__ __launch_bounds__(256, MODE == kSplitHeads ? 2 : 1) void attn_staged_
       const int r = 4 * w + (k >> 1), half = k & 1;
       const floatx4 v = *(const __attribute__((address_space(3))) floatx4 *)(slot(r) + 1024 * half + lane16);
       float *dst = part ? (float *)rec + r * 512 : (float *)(p.o + b * p.o_sb + t * p.o_st + (int64_t)(hg * HG + r) * p.o_sh);
-      *(floatx4 *)(dst + 256 * half + 4 * lane) = v;
+      __builtin_nontemporal_store(v, (floatx4 *)(dst + 256 * half + 4 * lane));
     }
     if (part && w == 0 && g == 0) {
       // then the maxima and the sums
@@ -1275,7 +1277,7 @@ __global__ __launch_bounds__(256, MODE == kSplitHeads ? 2 : 1) void attn_staged_
         const int sl = (RPT / 2) * w + (k >> 1), half = k & 1;
         const int head = hg * HG + 16 * (pass * WPP + sl / 16) + (sl % 16);
         const floatx4 v = *(const __attribute__((address_space(3))) floatx4 *)(slot(sl) + 1024 * half + lane16);
-        *(floatx4 *)((float *)(p.o + b * p.o_sb + t * p.o_st + (int64_t)head * p.o_sh) + 256 * half + 4 * lane) = v;
+        __builtin_nontemporal_store(v, (floatx4 *)((float *)(p.o + b * p.o_sb + t * p.o_st + (int64_t)head * p.o_sh) + 256 * half + 4 * lane));
       }
       if (pass + 1 < 4 / WPP) lds_barrier();
     }
