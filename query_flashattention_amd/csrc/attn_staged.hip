@@ -57,7 +57,9 @@ enum : int { kSplitHeads = 0, kSplitDims = 1, kSplitKeys = 2 };
 // are read: K codes to float16 (exact), with the row's scale applied to the fp32
 // scores; V codes through an 8-bit transpose read to float16 (exact), times the
 // rows' scales in float16.  P and the accumulators are as for float16 rows.
-template <int MODE, bool INDEXED, bool FP8>
+// PARTS (decode only): the launch is a split decode; each workgroup takes one part
+// of its token's block list and leaves a record for the combine pass.
+template <int MODE, bool INDEXED, bool FP8, bool PARTS = false>
 __global__ __launch_bounds__(256, MODE == kSplitHeads ? 2 : 1) void attn_staged_kernel(const AttnParams p) {
   constexpr bool KEYS = MODE == kSplitKeys;
   // KEYS units: float16 rows go in half-blocks of 16 rows, FP8 rows in whole blocks
@@ -92,7 +94,8 @@ __global__ __launch_bounds__(256, MODE == kSplitHeads ? 2 : 1) void attn_staged_
   const int ngroups = p.H / HG;
   // split decode: consecutive workgroups share (token, head group) and take
   // consecutive parts of its block list
-  const int nsplit = MODE == kSplitHeads ? 1 : p.nsplit;
+  static_assert(!(PARTS && MODE == kSplitHeads), "split parts are a decode launch");
+  const int nsplit = PARTS ? p.nsplit : 1;
   // (32-bit unsigned arithmetic: the grid is below 2^31 workgroups, and 64-bit
   // divisions by values known only at run time cost hundreds of instructions)
   const uint32_t L0 = xcd_remap32(blockIdx.x, gridDim.x);
@@ -973,7 +976,7 @@ __global__ __launch_bounds__(256, MODE == kSplitHeads ? 2 : 1) void attn_staged_
     else if (w == 1) merge(std::integral_constant<int, 1>{});
     else if (w == 2) merge(std::integral_constant<int, 2>{});
     else merge(std::integral_constant<int, 3>{});
-    if (nsplit > 1) {
+    if constexpr (PARTS) {
       // partial record of this split: unnormalised O, then the maxima and the sums
       char *rec = p.ws + ((int64_t)L * nsplit + split) * kSplitRecord;
       float *ob = (float *)rec + c16 * 512 + 128 * w + 4 * g;
@@ -1227,19 +1230,29 @@ __global__ __launch_bounds__(256, MODE == kSplitHeads ? 2 : 1) void attn_staged_
     auto slot = [&](int sl) __attribute__((always_inline)) -> lds_w * {
       return (sl < RPT ? kts : vts) + (sl % RPT) * kORow;
     };
-    const bool part = nsplit > 1;
+    constexpr bool part = PARTS;
     const float sc = part ? 1.f : inv;
     lds_w *row = slot(c16) + 4 * d0 + 16 * g;
 #pragma unroll
     for (int dt = 0; dt < NDT; ++dt) *(__attribute__((address_space(3))) floatx4 *)(row + 64 * dt) = o[dt] * sc;
     lds_barrier();
     char *rec = part ? p.ws + ((int64_t)L * nsplit + split) * kSplitRecord : nullptr;
+    if constexpr (part) {
+      // a split part's record is read back by the combine pass: cached stores
 #pragma unroll
-    for (int k = 0; k < 8; ++k) {
-      const int r = 4 * w + (k >> 1), half = k & 1;
-      const floatx4 v = *(const __attribute__((address_space(3))) floatx4 *)(slot(r) + 1024 * half + lane16);
-      float *dst = part ? (float *)rec + r * 512 : (float *)(p.o + b * p.o_sb + t * p.o_st + (int64_t)(hg * HG + r) * p.o_sh);
-      __builtin_nontemporal_store(v, (floatx4 *)(dst + 256 * half + 4 * lane));
+      for (int k = 0; k < 8; ++k) {
+        const int r = 4 * w + (k >> 1), half = k & 1;
+        const floatx4 v = *(const __attribute__((address_space(3))) floatx4 *)(slot(r) + 1024 * half + lane16);
+        *(floatx4 *)((float *)rec + r * 512 + 256 * half + 4 * lane) = v;
+      }
+    } else {
+#pragma unroll
+      for (int k = 0; k < 8; ++k) {
+        const int r = 4 * w + (k >> 1), half = k & 1;
+        const floatx4 v = *(const __attribute__((address_space(3))) floatx4 *)(slot(r) + 1024 * half + lane16);
+        float *dst = (float *)(p.o + b * p.o_sb + t * p.o_st + (int64_t)(hg * HG + r) * p.o_sh);
+        __builtin_nontemporal_store(v, (floatx4 *)(dst + 256 * half + 4 * lane));
+      }
     }
     if (part && w == 0 && g == 0) {
       // then the maxima and the sums
@@ -1294,13 +1307,19 @@ static hipError_t launch_staged(const AttnParams &p, hipStream_t s) {
   const int64_t n = (int64_t)p.B * p.T * (p.H / HG) * (MODE == kSplitHeads ? 1 : p.nsplit);
   if (n == 0) return hipSuccess;
   const dim3 grid((unsigned)n), block(256);
-  if (p.fp8) {
-    if (p.indexed) hipLaunchKernelGGL((attn_staged_kernel<MODE, true, true>), grid, block, 0, s, p);
-    else hipLaunchKernelGGL((attn_staged_kernel<MODE, false, true>), grid, block, 0, s, p);
-  } else {
-    if (p.indexed) hipLaunchKernelGGL((attn_staged_kernel<MODE, true, false>), grid, block, 0, s, p);
-    else hipLaunchKernelGGL((attn_staged_kernel<MODE, false, false>), grid, block, 0, s, p);
-  }
+  auto go = [&](auto parts) {
+    constexpr bool P = decltype(parts)::value;
+    if (p.fp8) {
+      if (p.indexed) hipLaunchKernelGGL((attn_staged_kernel<MODE, true, true, P>), grid, block, 0, s, p);
+      else hipLaunchKernelGGL((attn_staged_kernel<MODE, false, true, P>), grid, block, 0, s, p);
+    } else {
+      if (p.indexed) hipLaunchKernelGGL((attn_staged_kernel<MODE, true, false, P>), grid, block, 0, s, p);
+      else hipLaunchKernelGGL((attn_staged_kernel<MODE, false, false, P>), grid, block, 0, s, p);
+    }
+  };
+  if constexpr (MODE == kSplitHeads) go(std::false_type{});
+  else if (p.nsplit > 1) go(std::true_type{});
+  else go(std::false_type{});
   return hipGetLastError();
 }
 
