@@ -559,7 +559,7 @@ def main():
         roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": round(achieved / HBM_PEAK_GBS, 4),
                 "traffic": traffic_from_profiles(DECODE_KERNEL_SRC) if name == "decode_swa" else None,
-                "kernel": "attn_staged_kernel<%d,%s,%s> (ds4attn_decode)" % (
+                "kernel": "attn_staged_kernel<%d,%s,%s,false> (ds4attn_decode)" % (
                     decode_kernel_label(runner.w), str(runner.w.r1_index is not None).lower(),
                     str(name.endswith("_fp8")).lower()),
                 "bytes_per_launch": compulsory, "kernel_ms_mean": round(kern["mean"], 5),
@@ -573,7 +573,7 @@ def main():
         achieved = c["flops"] / kern_s / 1e12
         roof = {"bound": "mfma", "achieved": round(achieved, 2), "peak": MFMA_F16_PEAK_TFLOPS,
                 "unit": "TFLOP/s", "frac": round(achieved / MFMA_F16_PEAK_TFLOPS, 4), "traffic": None,
-                "kernel": "attn_staged_kernel<0,%s,%s> (ds4attn_prefill)" % (
+                "kernel": "attn_staged_kernel<0,%s,%s,false> (ds4attn_prefill)" % (
                     str(runner.w.r1_index is not None).lower(), str(name.endswith("_fp8")).lower()),
                 "flops_per_launch": c["flops"],
                 "kernel_ms_mean": round(kern["mean"], 5), "kernel_launches_timed": kern["launches"],
