@@ -101,10 +101,13 @@ __global__ __launch_bounds__(256, MODE == kSplitHeads ? 2 : 1) void attn_staged_
   const uint32_t L0 = xcd_remap32(blockIdx.x, gridDim.x);
   const int split = (int)(L0 % (uint32_t)nsplit);
   const uint32_t L = L0 / (uint32_t)nsplit;
-  const int hg = (int)(L % (uint32_t)ngroups);
-  const uint32_t bt = L / (uint32_t)ngroups;
-  const int t = (int)(bt % (uint32_t)p.T);
-  const int b = (int)(bt / (uint32_t)p.T);
+  // (indices below 2^31: multiply-shift divisions by the run-time H/HG and T)
+  const uint32_t bt = fast_div(L, HG == 16 ? p.div_g16 : p.div_g64);
+  const int hg = (int)(L - bt * (uint32_t)ngroups);
+  const uint32_t bb = fast_div(bt, p.div_t);
+  const int t = (int)(bt - bb * (uint32_t)p.T);
+  const int b = (int)bb;
+  const int tile = (int)fast_div((uint32_t)t, p.div_bq);   // the token's query tile in the map
   // this lane's head and the first head dim of this wave's operands
   const int h = hg * HG + (MODE == kSplitHeads ? 16 * w : 0) + c16;
   const int d0 = MODE == kSplitDims ? 128 * w : 0;
@@ -420,7 +423,7 @@ __global__ __launch_bounds__(256, MODE == kSplitHeads ? 2 : 1) void attn_staged_
   // starts at the first block the window reaches.  A wrong guess is redone below.
   int jlo = 0;
   if (p.blk && p.window > 0) {
-    const int64_t lo = p.qk_delta + (int64_t)(t / p.bq) * p.bq - p.window + 1;   // tile's first row
+    const int64_t lo = p.qk_delta + (int64_t)tile * p.bq - p.window + 1;   // tile's first row
     jlo = lo <= 0 ? 0 : (int)(lo / kRowsPerBlock < p.nb0 ? lo / kRowsPerBlock : p.nb0);
   }
   // a split's list part starts at its share of the dense blocks from jlo on
@@ -436,7 +439,7 @@ __global__ __launch_bounds__(256, MODE == kSplitHeads ? 2 : 1) void attn_staged_
   // when there is nothing to read): the compiler's wait counts assume the fewest
   // loads any path issues, so a load skipped on some path makes the common path
   // wait for everything in flight.
-  const uint8_t *blkrow = p.blk ? p.blk + ((int64_t)b * p.ntiles + t / p.bq) * p.nbd : nullptr;
+  const uint8_t *blkrow = p.blk ? p.blk + ((int64_t)b * p.ntiles + tile) * p.nbd : nullptr;
   int s_first = -1;
   if constexpr (KEYS) {
     const int sraw = buf_load_u8(make_rsrc(blkrow, blkrow ? (uint32_t)p.nbd : 0u), (uint32_t)tid);

@@ -2,6 +2,8 @@
 // Every check runs on the host before anything is enqueued (see include/ds4attn.h).
 #include "ds4attn.h"
 #include "ds4attn_internal.h"
+
+#include <algorithm>
 #include "mfma_common.h"
 
 #include <cmath>
@@ -141,6 +143,10 @@ int run_attention(const ds4attn_args *a, const void *q, const uint8_t *blk, int3
   P.blk = blk;
   P.bq = blk ? bq : 1;
   P.ntiles = (a->n_tok + P.bq - 1) / P.bq;
+  P.div_g16 = make_fast_div((uint32_t)std::max(1, a->n_head / 16));
+  P.div_g64 = make_fast_div((uint32_t)std::max(1, a->n_head / 64));
+  P.div_t = make_fast_div((uint32_t)std::max(1, a->n_tok));
+  P.div_bq = make_fast_div((uint32_t)P.bq);
   hipStream_t s = (hipStream_t)stream;
   hipError_t e;
   // The matrix-core kernels list the token's non-skipped map blocks in LDS

@@ -18,6 +18,24 @@ constexpr int kIdxCap = 2048;       // largest index list held in LDS by the mat
 enum : int { kSkip = 0, kPartial = 1, kFull = 2 };
 
 // Everything a kernel needs, resolved on the host from ds4attn_args.
+// Division by a run-time divisor d >= 1 of indices n < 2^31, exact: with
+// l = ceil(log2 d) and m = ceil(2^(31+l) / d) < 2^32, n / d = (n * m) >> (31 + l)
+// (the rounding error of m adds less than n / 2^(31+l) < 1/d to n/d, which never
+// crosses the next integer).  Built on the host by make_fast_div.
+struct FastDiv {
+  uint32_t m;
+  uint32_t shift;   // 31 + l
+};
+inline FastDiv make_fast_div(uint32_t d) {
+  uint32_t l = 0;
+  while ((1ull << l) < d) ++l;
+  const uint64_t pow = 1ull << (31 + l);
+  return FastDiv{(uint32_t)((pow + d - 1) / d), 31 + l};
+}
+__device__ __forceinline__ uint32_t fast_div(uint32_t n, FastDiv f) {
+  return (uint32_t)(((uint64_t)n * f.m) >> f.shift);
+}
+
 struct AttnParams {
   const char *q;
   char *o;
@@ -57,6 +75,9 @@ struct AttnParams {
   int bq;
   int64_t ntiles;
   int nbd;                 // blocks covered by the map: nb0 (+ nb1 when not indexed)
+  // the matrix-core kernels' index divisions by run-time values, as multiply and
+  // shift (see fast_div): by H/16, H/64, T and bq
+  FastDiv div_g16, div_g64, div_t, div_bq;
 };
 
 // ----------------------------------------------------------------------------- device helpers
