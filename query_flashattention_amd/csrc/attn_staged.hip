@@ -625,6 +625,17 @@ __global__ __launch_bounds__(256, MODE == kSplitHeads ? 2 : 1) void attn_staged_
     }
   };
 
+  // The masks of the part's first entries (up to `cap` of them), in as few rounds of
+  // eight entries as the list needs: the unrolled rounds of a long batch cost about
+  // 0.8 us when the list has only a few entries.
+  auto build_masks_first = [&](int cap) __attribute__((always_inline)) {
+    const int n = e1 - e0 < cap ? e1 - e0 : cap;
+    if (n <= 8) build_masks(e0, n, std::integral_constant<int, 1>{});
+    else if (n <= 16) build_masks(e0, n, std::integral_constant<int, 2>{});
+    else if (n <= 32) build_masks(e0, n, std::integral_constant<int, 4>{});
+    else build_masks(e0, n, std::integral_constant<int, 8>{});
+  };
+
   // Start the transfers of list entry i (< nlist) into buffer pair `buf`, with the
   // entry's mask (MASKED) or unmasked.
   auto stage = [&](int i, auto buf, auto masked) __attribute__((always_inline)) {
@@ -703,7 +714,7 @@ __global__ __launch_bounds__(256, MODE == kSplitHeads ? 2 : 1) void attn_staged_
 #pragma unroll
     for (int ks = 0; ks < NKS; ++ks) qf[ks] = *(const half8 *)(wt + c16 * kKRow + 64 * ks + 16 * g);
     // masks of the first two chunks of entries (the whole ring)
-    build_masks(e0, e1 - e0 < kMaskRing ? e1 - e0 : kMaskRing, std::integral_constant<int, 8>{});
+    build_masks_first(kMaskRing);
     lds_barrier();   // masks visible
     // Round r: wave w takes unit 4r + w, i.e. entries e0 + 4r / UPE .. (two entries
     // of half-blocks, or four blocks).  Every kMaskChunk entries all waves meet and
@@ -1021,7 +1032,7 @@ __global__ __launch_bounds__(256, MODE == kSplitHeads ? 2 : 1) void attn_staged_
       });
     }
   }
-  build_masks(e0, e1 - e0 < kMaskChunk ? e1 - e0 : kMaskChunk, std::integral_constant<int, 8>{});
+  build_masks_first(kMaskChunk);
   wait_vmcnt<0>();
   lds_barrier();   // masks visible
   for_bufs([&](auto E) { clear_masked(e0 + E, E); });
