@@ -74,6 +74,11 @@ __global__ __launch_bounds__(256, MODE == kSplitHeads ? 2 : 1) void attn_staged_
   // computes while the other's transfers are in flight.
   // (FP8 tiles are half the size: DIMS keeps four blocks in flight)
   constexpr int NBUF = MODE == kSplitHeads ? 1 : (FP8 ? 4 : 2);
+  // DIMS with float16 rows stages a block's K rows as soon as the score exchange
+  // has freed the K tile and its V rows after P.V, so the transfer issue (bound by
+  // the CU's vector-memory path) overlaps the softmax and P.V instead of stalling
+  // the waves at the end of the block
+  constexpr bool SPLITKV = MODE == kSplitDims && !FP8;
   constexpr int KPD = KEYS ? 4 : 2;   // K operand reads in flight (k-steps)
   // V operand reads in flight (output tiles); FP8 rows in HEADS take one fewer,
   // which keeps their conversions within 256 registers without spilling
@@ -165,7 +170,9 @@ __global__ __launch_bounds__(256, MODE == kSplitHeads ? 2 : 1) void attn_staged_
   // instructions in all.  Rows whose bit in `vm` is clear arrive as zeros (and are
   // not read from memory); with vm = all ones every row is transferred (gathered
   // entries that are unused read row 0) and hidden rows are cleared afterwards.
-  auto stage_rows = [&](int j, uint32_t vm, auto buf) __attribute__((always_inline)) {
+  // `part` (float16 rows): 0 = K and V rows, 1 = K rows only, 2 = V rows only.
+  auto stage_rows = [&](int j, uint32_t vm, auto buf, auto part) __attribute__((always_inline)) {
+    constexpr int PART = decltype(part)::value;
     const uint32_t kbase = lds_addr(ktile(buf)), vbase = lds_addr(vtile(buf));
     const char *kb, *vb, *ksb = nullptr, *vsb = nullptr;
     int64_t sr;
@@ -248,13 +255,16 @@ __global__ __launch_bounds__(256, MODE == kSplitHeads ? 2 : 1) void attn_staged_
         const int rr = 8 * w + q;
         const int row = rows[q];
         const bool shown = (vm >> rr) & 1u;
-        dma16(shown ? kb + row * sr : kZeroRow, lane16, kbase + rr * kKRow);
-        dma16(shown ? vb + row * sr : kZeroRow, lane16, vbase + rr * kVRow);
+        if (PART != 2) dma16(shown ? kb + row * sr : kZeroRow, lane16, kbase + rr * kKRow);
+        if (PART != 1) dma16(shown ? vb + row * sr : kZeroRow, lane16, vbase + rr * kVRow);
       }
     }
   };
   using Masked = std::integral_constant<bool, true>;
   using Unmasked = std::integral_constant<bool, false>;
+  using BothParts = std::integral_constant<int, 0>;
+  using KPart = std::integral_constant<int, 1>;
+  using VPart = std::integral_constant<int, 2>;
 
   // KEYS: a unit's rows travel global -> this wave's staging registers, one
   // contiguous 1 KiB per load (one float16 row, or two FP8 rows: lanes 0-31 the
@@ -446,7 +456,7 @@ __global__ __launch_bounds__(256, MODE == kSplitHeads ? 2 : 1) void attn_staged_
     s_first = tid < p.nbd ? (blkrow ? sraw : kPartial) : 0;
   } else {
     for_bufs([&](auto E) {
-      if (spec(E) >= 0) stage_rows(spec(E), 0xffffffffu, E);
+      if (spec(E) >= 0) stage_rows(spec(E), 0xffffffffu, E, BothParts{});
     });
   }
 
@@ -638,12 +648,12 @@ __global__ __launch_bounds__(256, MODE == kSplitHeads ? 2 : 1) void attn_staged_
 
   // Start the transfers of list entry i (< nlist) into buffer pair `buf`, with the
   // entry's mask (MASKED) or unmasked.
-  auto stage = [&](int i, auto buf, auto masked) __attribute__((always_inline)) {
+  auto stage = [&](int i, auto buf, auto masked, auto part) __attribute__((always_inline)) {
     constexpr bool MASKED = decltype(masked)::value;
     int j, status;
     entry_at(i, j, status);
     const uint32_t vm = MASKED ? __builtin_amdgcn_readfirstlane(vmask[i & (kMaskRing - 1)]) : 0xffffffffu;
-    stage_rows(__builtin_amdgcn_readfirstlane(j), vm, buf);
+    stage_rows(__builtin_amdgcn_readfirstlane(j), vm, buf, part);
   };
 
   // Clear the V rows of entry i that its mask hides, among this wave's own rows
@@ -1028,7 +1038,7 @@ __global__ __launch_bounds__(256, MODE == kSplitHeads ? 2 : 1) void attn_staged_
     if (!all) {
       wait_vmcnt<0>();   // the guessed transfers land before their buffers are refilled
       for_bufs([&](auto E) {
-        if (!hit[E]) stage(e0 + E, E, Unmasked{});
+        if (!hit[E]) stage(e0 + E, E, Unmasked{}, BothParts{});
       });
     }
   }
@@ -1093,6 +1103,19 @@ __global__ __launch_bounds__(256, MODE == kSplitHeads ? 2 : 1) void attn_staged_
       for (int ww = 1; ww < 4; ++ww) {
         s0 += xs[(ww * 2 + 0) * 64 + lane];
         s1 += xs[(ww * 2 + 1) * 64 + lane];
+      }
+    }
+    const int nx = i + NBUF;   // the entry buffer B takes next
+    if constexpr (SPLITKV) {
+      // the exchange barrier ended every wave's K reads: the K tile takes entry nx
+      if (nx < e1) {
+        if ((nx & (kMaskChunk - 1)) == 0) {
+          // next chunk of masks (entries i and i + 1 sit in the other half of the ring)
+          const int n = e1 - nx;
+          build_masks(nx, n < kMaskChunk ? n : kMaskChunk, std::integral_constant<int, 1>{});
+          lds_barrier();
+        }
+        stage(nx, buf, Masked{}, KPart{});
       }
     }
     // ---- online softmax: this lane holds rows slot_row(g, 0..7) of head h
@@ -1202,15 +1225,22 @@ __global__ __launch_bounds__(256, MODE == kSplitHeads ? 2 : 1) void attn_staged_
     }
 
     lds_barrier();   // every wave is done with buffer B
-    const int nx = i + NBUF;   // the entry buffer B takes next
-    if (nx < e1) {
+    if constexpr (SPLITKV) {
+      if (nx < e1) {
+        stage(nx, buf, Masked{}, VPart{});
+        // block i+1 landed: only the stage of entry nx may be in flight
+        wait_vmcnt<(NBUF - 1) * kStageOps>();
+      } else {
+        wait_vmcnt<0>();
+      }
+    } else if (nx < e1) {
       if ((nx & (kMaskChunk - 1)) == 0) {
         // next chunk of masks (one batch of loads per 8 entries; drains the transfers)
         const int n = e1 - nx;
         build_masks(nx, n < kMaskChunk ? n : kMaskChunk, std::integral_constant<int, 1>{});
         lds_barrier();
       }
-      stage(nx, buf, Masked{});
+      stage(nx, buf, Masked{}, BothParts{});
       // block i+1 (staged earlier) landed: only the NBUF - 1 newer stages may be in flight
       if constexpr (NBUF >= 2) wait_vmcnt<(NBUF - 1) * (FP8 ? kF8StageOps : kStageOps)>();
       else wait_vmcnt<0>();
