@@ -1225,6 +1225,9 @@ __global__ __launch_bounds__(256, MODE == kSplitHeads ? 2 : 1) void attn_staged_
     }
 
     lds_barrier();   // every wave is done with buffer B
+    // HEADS (two workgroups per CU): a wave issuing its block's transfers runs at
+    // raised priority, so the other workgroup's MFMA phase yields issue slots to it
+    if constexpr (MODE == kSplitHeads) __builtin_amdgcn_s_setprio(1);
     if constexpr (SPLITKV) {
       if (nx < e1) {
         stage(nx, buf, Masked{}, VPart{});
@@ -1247,6 +1250,7 @@ __global__ __launch_bounds__(256, MODE == kSplitHeads ? 2 : 1) void attn_staged_
     } else {
       wait_vmcnt<0>();
     }
+    if constexpr (MODE == kSplitHeads) __builtin_amdgcn_s_setprio(0);
     lds_barrier();   // publishes block i+1
   };
 
