@@ -52,6 +52,7 @@ enum {
   DS4ATTN_OK = 0,
   DS4ATTN_E_INVAL = 1,        /* a null pointer, a negative size, a bad stride or alignment */
   DS4ATTN_E_UNSUPPORTED = 2,  /* a valid request this build has no kernel for */
+  DS4ATTN_E_WORKSPACE = 3,    /* a workspace smaller than the call needs */
   DS4ATTN_E_HIP = 4           /* the HIP runtime refused a launch */
 };
 
@@ -213,8 +214,21 @@ int ds4attn_blockmap_dims(const ds4attn_args *a, int32_t bq, int64_t *n_tiles, i
  *   q    device [B][T][H][D] of a->dtype by a->q_stride_*
  *   blk  device map from ds4attn_blockmap with the same *a and this bq, or NULL
  *        (then no block is skipped and every block is masked pair by pair; the
- *        result is the same)
+ *        result is the same).  A bq larger than n_tok means one tile.
  *   o    device float32 [B][T][H][D] by a->o_stride_*; every element is written.
+ *   workspace, workspace_bytes
+ *        device scratch for the work split the library picks for this call
+ *        (ds4attn_workspace_bytes gives its size; 0 bytes when the call runs
+ *        unsplit).  decode divides each token's key blocks over several
+ *        workgroups when the batch leaves most compute units idle (one sequence
+ *        of a long-context layer), and combines the parts with the online-softmax
+ *        rescale ([P-DS4] "Architecture Deep Dive", Whole-Model Graph Execution:
+ *        the attention path depends on the layer's ratio and the batch size).
+ *        NULL: no workspace, the call runs unsplit (same result up to rounding).
+ *        Otherwise 16-byte aligned, not overlapping o, and at least the size
+ *        ds4attn_workspace_bytes returns (else DS4ATTN_E_WORKSPACE); its contents
+ *        on entry do not matter and it is free again once the call's work on
+ *        `stream` has run.  prefill currently plans no split (0 bytes).
  * Both compute the same result.  decode splits the heads of a token over
  * several workgroups (for T = 1 and small batches); prefill keeps all heads of a
  * token in one workgroup (for 2048-token chunks,
@@ -227,33 +241,46 @@ int ds4attn_blockmap_dims(const ds4attn_args *a, int32_t bq, int64_t *n_tiles, i
  * scale_stride_b a multiple of 4 and >= 4*n_rows when batch > 1); anything else
  * with FP8 rows returns DS4ATTN_E_UNSUPPORTED (shapes) or DS4ATTN_E_INVAL
  * (pointers, strides).
- * Returns DS4ATTN_OK, DS4ATTN_E_INVAL, DS4ATTN_E_UNSUPPORTED or DS4ATTN_E_HIP.
+ * Returns DS4ATTN_OK, DS4ATTN_E_INVAL, DS4ATTN_E_UNSUPPORTED, DS4ATTN_E_WORKSPACE
+ * or DS4ATTN_E_HIP.
  */
 int ds4attn_decode(const ds4attn_args *a, const void *q, const uint8_t *blk, int32_t bq,
-                   float *o, void *stream);
+                   float *o, void *workspace, int64_t workspace_bytes, void *stream);
 int ds4attn_prefill(const ds4attn_args *a, const void *q, const uint8_t *blk, int32_t bq,
-                    float *o, void *stream);
+                    float *o, void *workspace, int64_t workspace_bytes, void *stream);
+
+/* Workspace bytes ds4attn_decode (is_prefill = 0) or ds4attn_prefill (nonzero)
+ * uses for *a: B * T * (H / 16) * splits records of 16 * 512 * 4 + 128 bytes for
+ * the split the library picks, 0 when it runs the call unsplit.  It depends on the
+ * shapes, sizes, window, index length and flags of *a, not on its pointers.
+ * Host only; returns the status ds4attn_decode / ds4attn_prefill would return for
+ * the same *a before looking at q, blk and o (DS4ATTN_OK, DS4ATTN_E_INVAL or
+ * DS4ATTN_E_UNSUPPORTED). */
+int ds4attn_workspace_bytes(const ds4attn_args *a, int32_t is_prefill, int64_t *bytes);
 
 /* The query-tile size the prefill kernel is tuned for (a map built with any
  * bq >= 1 is accepted). */
 int32_t ds4attn_prefill_bq(void);
 
 /*
- * ds4attn_decode_split -- ds4attn_decode with each token's key blocks divided over
- * `splits` workgroups per group of 16 heads, for batches too small to fill the
- * chip (one sequence of a long-context layer: [P-DS4] "Architecture Deep Dive",
+ * ds4attn_decode_split -- ds4attn_decode with a chosen split: each token's key
+ * blocks divided over `splits` workgroups per group of 16 heads, for batches too
+ * small to fill the chip (one sequence of a long-context layer: [P-DS4] "Architecture Deep Dive",
  * 32K-1M contexts; the fused step of [P-Metal] "FlashAttention Kernel
  * Architecture" run on parts of the block list).  Each part keeps its own running
  * maximum, sum and unnormalised output in `workspace`; a second kernel combines
  * them: O = sum_s 2^(m_s - M) O_s / sum_s 2^(m_s - M) l_s with M = max_s m_s (the
  * online-softmax rescale, applied once across parts).  The result equals
- * ds4attn_decode's up to rounding.
- *   splits     1..64; 1 is ds4attn_decode (no workspace needed)
+ * ds4attn_decode's up to rounding.  (ds4attn_decode picks the split itself; this
+ * entry point fixes it, for measurement and cross-checks.)
+ *   splits     1..64; 1 runs unsplit (no workspace needed)
  *   workspace  device, 16-byte aligned, at least ds4attn_decode_workspace_bytes
- *              bytes, not overlapping o; its contents on entry do not matter
+ *              bytes (else DS4ATTN_E_WORKSPACE), not overlapping o; its contents
+ *              on entry do not matter
  * Needs the matrix-core case (F16 Q, D = 512, H % 16 == 0, no DS4ATTN_FLAG_GENERIC;
  * either KV format), else DS4ATTN_E_UNSUPPORTED.
- * Returns DS4ATTN_OK, DS4ATTN_E_INVAL, DS4ATTN_E_UNSUPPORTED or DS4ATTN_E_HIP.
+ * Returns DS4ATTN_OK, DS4ATTN_E_INVAL, DS4ATTN_E_UNSUPPORTED, DS4ATTN_E_WORKSPACE
+ * or DS4ATTN_E_HIP.
  */
 int ds4attn_decode_split(const ds4attn_args *a, const void *q, const uint8_t *blk, int32_t bq,
                          float *o, int32_t splits, void *workspace, int64_t workspace_bytes,

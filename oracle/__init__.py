@@ -25,10 +25,16 @@ Modules:
 * ``compress`` -- compressor pooling of raw rows into compressed rows, with the
   rolling state of the incomplete group.
 
-Every function is pinned by at least one check in ``tests/test_oracle*.py``
-(brute force, closed forms, invariants); no function is "parity unpinned".
-``compress`` is pinned to its stated reading of the pages (which name the
-compressor's state but not its formula), not to values the pages print.
+Every function of ``reference``, ``brute``, ``fp8`` and ``topk`` is pinned by at
+least one check in ``tests/test_oracle*.py`` (brute force, closed forms,
+invariants, library routines) against what the pages and the mathematics fix.
+
+``compress`` is **parity unpinned**: the pages name the compressor's rolling
+KV/score state and its ratio boundaries but give no pooling formula, so no value
+they print, and no definition they state, can pin it.  Its checks pin the code
+to this package's own reading of the pages (a per-element softmax over each
+group); a different reading would pass none of them, but nothing shows that the
+reading is the engine's.
 """
 
 from . import reference, brute  # noqa: F401

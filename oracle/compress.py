@@ -21,6 +21,10 @@ scores) but give no formula.  Readings taken (each is listed in the design doc):
 
 The definition is written out plainly in float64: per group, per element, a max,
 the exponentials, their sum and the weighted sum.
+
+Parity unpinned: the formula is this package's reading, not the pages'.  The
+checks in tests/test_oracle_compress.py pin the code to the reading (brute force,
+closed forms, invariants, planted mistakes); nothing on the pages pins the reading.
 """
 
 from __future__ import annotations

@@ -1373,15 +1373,12 @@ static hipError_t launch_staged(const AttnParams &p, hipStream_t s) {
 
 // Decode: lists that can be long take the KEYS split; short lists (a few blocks:
 // each wave would see one or two units, and the merge of the four partial results
-// would cost more than the overlap gains) take the DIMS split.  The bound on a token's list: the dense blocks its window can
-// reach (all dense blocks without a window), plus the gathered blocks.
+// would cost more than the overlap gains) take the DIMS split.  The list length
+// is bounded by list_bound, per split part.
 constexpr int64_t kKeysMinEntries = 8;
 static bool use_keys(const AttnParams &p) {
   if (p.decode_split) return p.decode_split == 2;
-  int64_t dense = p.nbd;
-  if (p.window > 0) dense = std::min<int64_t>(dense, (int64_t)p.window / kRowsPerBlock + 2);
-  const int64_t entries = dense + (p.indexed ? p.nb1 : 0);
-  return entries / (p.nsplit > 0 ? p.nsplit : 1) >= kKeysMinEntries;
+  return list_bound(p) / (p.nsplit > 0 ? p.nsplit : 1) >= kKeysMinEntries;
 }
 hipError_t launch_attn_decode(const AttnParams &p, hipStream_t s) {
   return use_keys(p) ? launch_staged<kSplitKeys>(p, s) : launch_staged<kSplitDims>(p, s);

@@ -95,8 +95,17 @@ int64_t split_workspace_bytes(const ds4attn_args *a, int32_t splits) {
   return splits > 1 ? (int64_t)a->batch * a->n_tok * (a->n_head / 16) * splits * kSplitRecord : 0;
 }
 
-int run_attention(const ds4attn_args *a, const void *q, const uint8_t *blk, int32_t bq, float *o,
-                  void *stream, bool prefill, int32_t splits = 1, void *ws = nullptr, int64_t ws_bytes = 0) {
+// An attention call resolved on the host: kernel parameters (pointers not yet
+// set), which kernel family applies, and whether there is any work.
+struct Resolved {
+  AttnParams P;
+  bool mfma;     // the matrix-core kernels apply
+  bool empty;    // B * T == 0: nothing to launch
+  int eb;        // element bytes of Q (and of plain K/V rows)
+};
+
+// Every check that needs only *a: shapes, strides, regions, formats, flags.
+int resolve_args(const ds4attn_args *a, bool prefill, Resolved &R) {
   if (!a) return DS4ATTN_E_INVAL;
   if (a->dtype != DS4ATTN_F16 && a->dtype != DS4ATTN_F32) return DS4ATTN_E_INVAL;
   if (a->head_dim <= 0) return DS4ATTN_E_INVAL;
@@ -104,10 +113,10 @@ int run_attention(const ds4attn_args *a, const void *q, const uint8_t *blk, int3
   if (!std::isfinite(a->scale)) return DS4ATTN_E_INVAL;
   if (a->kv_format != DS4ATTN_KV_PLAIN && a->kv_format != DS4ATTN_KV_FP8_E4M3) return DS4ATTN_E_INVAL;
   const bool fp8 = a->kv_format == DS4ATTN_KV_FP8_E4M3;
-  const int eb = elem_bytes(a->dtype);
-  const int row_bytes = a->head_dim * eb;                       // Q rows
+  R.eb = elem_bytes(a->dtype);
+  const int row_bytes = a->head_dim * R.eb;                     // Q rows
   const int kv_row_bytes = fp8 ? a->head_dim : row_bytes;       // K/V rows
-  AttnParams P;
+  AttnParams &P = R.P;
   int st = resolve_mask(a, kv_row_bytes, true, P);
   if (st) return st;
   if (fp8) {
@@ -121,16 +130,61 @@ int run_attention(const ds4attn_args *a, const void *q, const uint8_t *blk, int3
     P.s1_sb = a->r1.scale_stride_b;
   }
   const int64_t work = (int64_t)a->batch * a->n_tok;
-  if (work == 0) return DS4ATTN_OK;
-  if (!q || !o || !aligned16(q) || !aligned16(o)) return DS4ATTN_E_INVAL;
+  R.empty = work == 0;
+  if (R.empty) {
+    R.mfma = false;
+    return DS4ATTN_OK;
+  }
   if (!stride16(a->q_stride_b) || !stride16(a->q_stride_t) || !stride16(a->q_stride_h) ||
       !stride16(a->o_stride_b) || !stride16(a->o_stride_t) || !stride16(a->o_stride_h))
     return DS4ATTN_E_INVAL;
   if (a->n_head > 1 && (a->q_stride_h < row_bytes || a->o_stride_h < a->head_dim * 4))
     return DS4ATTN_E_INVAL;
-  if (blk && bq < 1) return DS4ATTN_E_INVAL;
-  if (P.indexed && !a->r1_index) return DS4ATTN_E_INVAL;
   if (work * a->n_head > 0x7fffffffLL) return DS4ATTN_E_UNSUPPORTED;
+  // The matrix-core kernels list the token's non-skipped map blocks in LDS (up to
+  // kListCap of them) and address each sequence's K/V region with 32-bit offsets
+  // (< 2^31 bytes); longer dense regions run on the vector-ALU kernel.
+  const int64_t rows1 = P.indexed ? ceil32(P.n1) : (int64_t)P.nb1 * 32;
+  const bool fits32 = (int64_t)P.nb0 * 32 * P.kv0_sr < 0x80000000LL && rows1 * P.kv1_sr < 0x80000000LL;
+  R.mfma = a->dtype == DS4ATTN_F16 && a->head_dim == 512 && a->n_head % 16 == 0 &&
+           !(a->flags & DS4ATTN_FLAG_GENERIC) && P.nbd <= kListCap && fits32;
+  // FP8 rows are dequantized inside the matrix-core kernels only
+  if (fp8 && !R.mfma) return DS4ATTN_E_UNSUPPORTED;
+  const bool want_dims = a->flags & DS4ATTN_FLAG_DECODE_DIMS, want_keys = a->flags & DS4ATTN_FLAG_DECODE_KEYS;
+  if (want_dims && want_keys) return DS4ATTN_E_INVAL;
+  if (want_dims || want_keys) {
+    // a chosen decode split: the matrix-core decode kernel
+    if (!R.mfma || (prefill && a->n_head % 64 == 0)) return DS4ATTN_E_UNSUPPORTED;
+    P.decode_split = want_keys ? 2 : 1;
+  }
+  return DS4ATTN_OK;
+}
+
+// The split the library picks for a decode call ([P-DS4] "Architecture Deep
+// Dive", Whole-Model Graph Execution: the attention path is chosen by layer type
+// and batch size).  A decode workgroup covers one token's 16 heads; a batch with
+// fewer than 128 such groups leaves most of the 256 CUs idle, so each token's
+// block list is divided over up to 256 / groups workgroups, about three key
+// blocks per part (measured: one sequence of the ratio-128 layer at 32K, 12
+// blocks, runs fastest in 4 parts; 64-sequence batches only lose from splitting).
+int plan_splits(const Resolved &R, bool prefill) {
+  if (prefill || R.empty || !R.mfma) return 1;
+  const AttnParams &P = R.P;
+  const int64_t groups = (int64_t)P.B * P.T * (P.H / 16);
+  if (groups >= 128) return 1;
+  const int64_t by_len = list_bound(P) / 3;
+  const int64_t by_cus = 256 / groups;
+  return (int)std::max<int64_t>(1, std::min<int64_t>({(int64_t)kMaxSplits, by_len, by_cus}));
+}
+
+// Pointer checks and the launch of a resolved call with `splits` parts (> 1: the
+// records go to `ws`, which must hold split_workspace_bytes).
+int launch_resolved(const ds4attn_args *a, Resolved &R, const void *q, const uint8_t *blk, int32_t bq,
+                    float *o, bool prefill, int32_t splits, void *ws, int64_t ws_bytes, void *stream) {
+  if (R.empty) return DS4ATTN_OK;
+  if (!q || !o || !aligned16(q) || !aligned16(o)) return DS4ATTN_E_INVAL;
+  if (blk && bq < 1) return DS4ATTN_E_INVAL;
+  AttnParams &P = R.P;
   P.q = (const char *)q;
   P.o = (char *)o;
   P.q_sb = a->q_stride_b;
@@ -141,36 +195,23 @@ int run_attention(const ds4attn_args *a, const void *q, const uint8_t *blk, int3
   P.o_sh = a->o_stride_h;
   P.scale_log2 = a->scale * 1.4426950408889634f;
   P.blk = blk;
-  P.bq = blk ? bq : 1;
-  P.ntiles = (a->n_tok + P.bq - 1) / P.bq;
+  // a tile longer than the chunk is the whole chunk (same map, same tile of every token)
+  P.bq = blk ? (int)std::min<int64_t>(bq, std::max(1, a->n_tok)) : 1;
+  P.ntiles = ((int64_t)a->n_tok + P.bq - 1) / P.bq;
   P.div_g16 = make_fast_div((uint32_t)std::max(1, a->n_head / 16));
   P.div_g64 = make_fast_div((uint32_t)std::max(1, a->n_head / 64));
   P.div_t = make_fast_div((uint32_t)std::max(1, a->n_tok));
   P.div_bq = make_fast_div((uint32_t)P.bq);
   hipStream_t s = (hipStream_t)stream;
   hipError_t e;
-  // The matrix-core kernels list the token's non-skipped map blocks in LDS
-  // (up to kListCap of them); longer dense regions run on the vector-ALU kernel.
-  // ... and address each sequence's K/V region with 32-bit offsets (< 2^31 bytes).
-  const int64_t rows1 = P.indexed ? ceil32(P.n1) : (int64_t)P.nb1 * 32;
-  const bool fits32 = (int64_t)P.nb0 * 32 * P.kv0_sr < 0x80000000LL && rows1 * P.kv1_sr < 0x80000000LL;
-  const bool mfma = a->dtype == DS4ATTN_F16 && a->head_dim == 512 && a->n_head % 16 == 0 &&
-                    !(a->flags & DS4ATTN_FLAG_GENERIC) && P.nbd <= kListCap && fits32;
-  // FP8 rows are dequantized inside the matrix-core kernels only
-  if (fp8 && !mfma) return DS4ATTN_E_UNSUPPORTED;
-  const bool want_dims = a->flags & DS4ATTN_FLAG_DECODE_DIMS, want_keys = a->flags & DS4ATTN_FLAG_DECODE_KEYS;
-  if (want_dims && want_keys) return DS4ATTN_E_INVAL;
-  if (want_dims || want_keys) {
-    // a chosen decode split: the matrix-core decode kernel
-    if (!mfma || (prefill && a->n_head % 64 == 0)) return DS4ATTN_E_UNSUPPORTED;
-    P.decode_split = want_keys ? 2 : 1;
-  }
   if (splits > 1) {
     // split decode runs on the matrix-core decode kernel only
-    if (!mfma || prefill) return DS4ATTN_E_UNSUPPORTED;
+    if (!R.mfma || prefill) return DS4ATTN_E_UNSUPPORTED;
+    const int64_t work = (int64_t)a->batch * a->n_tok;
     if (work * (a->n_head / 16) * splits > 0x7fffffffLL) return DS4ATTN_E_UNSUPPORTED;
     const int64_t need = split_workspace_bytes(a, splits);
-    if (!ws || !aligned16(ws) || ws_bytes < need) return DS4ATTN_E_INVAL;
+    if (!ws || !aligned16(ws)) return DS4ATTN_E_INVAL;
+    if (ws_bytes < need) return DS4ATTN_E_WORKSPACE;
     const int64_t o_len = (a->batch - 1) * a->o_stride_b + (a->n_tok - 1) * a->o_stride_t +
                           (a->n_head - 1) * a->o_stride_h + 4LL * a->head_dim;
     if (ranges_overlap(ws, need, o, o_len)) return DS4ATTN_E_INVAL;
@@ -179,10 +220,23 @@ int run_attention(const ds4attn_args *a, const void *q, const uint8_t *blk, int3
     e = launch_attn_decode_split(P, s);
     return e == hipSuccess ? DS4ATTN_OK : DS4ATTN_E_HIP;
   }
-  if (mfma && prefill && a->n_head % 64 == 0) e = launch_attn_prefill(P, s);
-  else if (mfma) e = launch_attn_decode(P, s);
-  else e = launch_attn_generic(P, eb, s);
+  if (R.mfma && prefill && a->n_head % 64 == 0) e = launch_attn_prefill(P, s);
+  else if (R.mfma) e = launch_attn_decode(P, s);
+  else e = launch_attn_generic(P, R.eb, s);
   return e == hipSuccess ? DS4ATTN_OK : DS4ATTN_E_HIP;
+}
+
+// ds4attn_decode / ds4attn_prefill: the library's plan, run in the caller's workspace.
+int run_planned(const ds4attn_args *a, const void *q, const uint8_t *blk, int32_t bq, float *o, void *ws,
+                int64_t ws_bytes, void *stream, bool prefill) {
+  if (ws_bytes < 0) return DS4ATTN_E_INVAL;
+  Resolved R;
+  int st = resolve_args(a, prefill, R);
+  if (st) return st;
+  const int splits = plan_splits(R, prefill);
+  // no workspace: the call runs unsplit
+  const int use = (splits > 1 && ws) ? splits : 1;
+  return launch_resolved(a, R, q, blk, bq, o, prefill, use, ws, ws_bytes, stream);
 }
 
 
@@ -221,6 +275,8 @@ int ds4attn_pad(const ds4attn_region *in, int32_t batch, int32_t head_dim, int32
     if (!inplace_k && ranges_overlap(k_pad, out_len, in->k, in_len)) return DS4ATTN_E_INVAL;
     if (!inplace_v && ranges_overlap(v_pad, out_len, in->v, in_len)) return DS4ATTN_E_INVAL;
     if (!inplace_k && ranges_overlap(k_pad, out_len, in->v, in_len) && in->k != in->v)
+      return DS4ATTN_E_INVAL;
+    if (!inplace_v && ranges_overlap(v_pad, out_len, in->k, in_len) && in->k != in->v)
       return DS4ATTN_E_INVAL;
   }
   // K and V outputs may be one buffer only when K and V inputs are one buffer too.
@@ -261,8 +317,9 @@ int ds4attn_blockmap(const ds4attn_args *a, int32_t bq, uint8_t *blk, void *stre
   // Only the mask side is read: sizes, window, positions, validity, index presence.
   int st = resolve_mask(a, 16, false, P);
   if (st) return st;
-  P.bq = bq;
-  P.ntiles = ((int64_t)a->n_tok + bq - 1) / bq;
+  // a tile longer than the chunk is the whole chunk (the same map)
+  P.bq = (int)std::min<int64_t>(bq, std::max(1, a->n_tok));
+  P.ntiles = ((int64_t)a->n_tok + P.bq - 1) / P.bq;
   const int64_t total = (int64_t)P.B * P.ntiles * P.nbd;
   if (total == 0) return DS4ATTN_OK;
   if (!blk) return DS4ATTN_E_INVAL;
@@ -272,13 +329,22 @@ int ds4attn_blockmap(const ds4attn_args *a, int32_t bq, uint8_t *blk, void *stre
 }
 
 int ds4attn_decode(const ds4attn_args *a, const void *q, const uint8_t *blk, int32_t bq, float *o,
-                   void *stream) {
-  return run_attention(a, q, blk, bq, o, stream, false);
+                   void *workspace, int64_t workspace_bytes, void *stream) {
+  return run_planned(a, q, blk, bq, o, workspace, workspace_bytes, stream, false);
 }
 
 int ds4attn_prefill(const ds4attn_args *a, const void *q, const uint8_t *blk, int32_t bq, float *o,
-                    void *stream) {
-  return run_attention(a, q, blk, bq, o, stream, true);
+                    void *workspace, int64_t workspace_bytes, void *stream) {
+  return run_planned(a, q, blk, bq, o, workspace, workspace_bytes, stream, true);
+}
+
+int ds4attn_workspace_bytes(const ds4attn_args *a, int32_t is_prefill, int64_t *bytes) {
+  if (!bytes) return DS4ATTN_E_INVAL;
+  Resolved R;
+  const int st = resolve_args(a, is_prefill != 0, R);
+  if (st) return st;
+  *bytes = split_workspace_bytes(a, plan_splits(R, is_prefill != 0));
+  return DS4ATTN_OK;
 }
 
 int ds4attn_decode_workspace_bytes(const ds4attn_args *a, int32_t splits, int64_t *bytes) {
@@ -292,7 +358,10 @@ int ds4attn_decode_workspace_bytes(const ds4attn_args *a, int32_t splits, int64_
 int ds4attn_decode_split(const ds4attn_args *a, const void *q, const uint8_t *blk, int32_t bq, float *o,
                          int32_t splits, void *workspace, int64_t workspace_bytes, void *stream) {
   if (splits < 1 || splits > kMaxSplits || workspace_bytes < 0) return DS4ATTN_E_INVAL;
-  return run_attention(a, q, blk, bq, o, stream, false, splits, workspace, workspace_bytes);
+  Resolved R;
+  const int st = resolve_args(a, false, R);
+  if (st) return st;
+  return launch_resolved(a, R, q, blk, bq, o, false, splits, workspace, workspace_bytes, stream);
 }
 
 int32_t ds4attn_prefill_bq(void) { return 16; }

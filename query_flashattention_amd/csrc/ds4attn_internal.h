@@ -80,6 +80,16 @@ struct AttnParams {
   FastDiv div_g16, div_g64, div_t, div_bq;
 };
 
+// Bound on the length of a token's block list: the dense blocks of region 0 its
+// window can reach (all of them without a window: 128 rows span at most 5
+// blocks, window / 32 + 2 is an upper bound), plus the blocks of region 1 (dense
+// blocks, or gathered blocks of 32 index entries).
+inline int64_t list_bound(const AttnParams &p) {
+  int64_t r0 = p.nb0;
+  if (p.window > 0 && (int64_t)p.window / kRowsPerBlock + 2 < r0) r0 = (int64_t)p.window / kRowsPerBlock + 2;
+  return r0 + p.nb1;
+}
+
 // ----------------------------------------------------------------------------- device helpers
 
 // Workgroups are dealt to the dies round-robin; give each die a contiguous run of

@@ -18,7 +18,7 @@ import torch
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libds4attn.so")
 
-OK, E_INVAL, E_UNSUPPORTED, E_HIP = 0, 1, 2, 4
+OK, E_INVAL, E_UNSUPPORTED, E_WORKSPACE, E_HIP = 0, 1, 2, 3, 4
 F16, F32, E4M3 = 0, 1, 2
 KV_PLAIN, KV_FP8_E4M3 = 0, 1
 BLK_SKIP, BLK_PARTIAL, BLK_FULL = 0, 1, 2
@@ -49,9 +49,9 @@ class Args(ctypes.Structure):
 
 
 EXPORTS = ("ds4attn_pad", "ds4attn_blockmap", "ds4attn_blockmap_dims", "ds4attn_decode",
-           "ds4attn_prefill", "ds4attn_prefill_bq", "ds4attn_topk", "ds4attn_quantize_fp8",
-           "ds4attn_decode_split", "ds4attn_decode_workspace_bytes", "ds4attn_compress",
-           "ds4attn_status_string")
+           "ds4attn_prefill", "ds4attn_workspace_bytes", "ds4attn_prefill_bq", "ds4attn_topk",
+           "ds4attn_quantize_fp8", "ds4attn_decode_split", "ds4attn_decode_workspace_bytes",
+           "ds4attn_compress", "ds4attn_status_string")
 
 _lib = None
 
@@ -70,7 +70,8 @@ def lib() -> ctypes.CDLL:
                                             ctypes.POINTER(_i32)]
         for name in ("ds4attn_decode", "ds4attn_prefill"):
             getattr(h, name).argtypes = [ctypes.POINTER(Args), _c_void_p, _c_void_p, _i32,
-                                         _c_void_p, _c_void_p]
+                                         _c_void_p, _c_void_p, _i64, _c_void_p]
+        h.ds4attn_workspace_bytes.argtypes = [ctypes.POINTER(Args), _i32, ctypes.POINTER(_i64)]
         h.ds4attn_topk.argtypes = [_c_void_p, _i64, _i32, _i64, _i32, _c_void_p, _i64, _c_void_p]
         h.ds4attn_decode_split.argtypes = [ctypes.POINTER(Args), _c_void_p, _c_void_p, _i32, _c_void_p,
                                            _i32, _c_void_p, _i64, _c_void_p]
@@ -79,9 +80,7 @@ def lib() -> ctypes.CDLL:
                                            _i64, _i64, _c_void_p, _i64, _c_void_p]
         h.ds4attn_compress.argtypes = [_i32, _i32, _i32, _i32, _i32, _c_void_p, _i64, _c_void_p, _i64,
                                        _c_void_p, _i64, _c_void_p, _i64, _c_void_p, _i64, _c_void_p]
-        for name in ("ds4attn_pad", "ds4attn_blockmap", "ds4attn_blockmap_dims", "ds4attn_decode",
-                     "ds4attn_prefill", "ds4attn_prefill_bq", "ds4attn_topk", "ds4attn_quantize_fp8",
-                     "ds4attn_decode_split", "ds4attn_decode_workspace_bytes", "ds4attn_compress"):
+        for name in EXPORTS[:-1]:
             getattr(h, name).restype = _i32
         h.ds4attn_status_string.argtypes = [_i32]
         h.ds4attn_status_string.restype = ctypes.c_char_p
@@ -190,16 +189,30 @@ def ds4attn_blockmap(a: Args, bq: int, blk: Optional[torch.Tensor], stream=None)
     _check(lib().ds4attn_blockmap(ctypes.byref(a), bq, _ptr(blk), _stream(stream)), "ds4attn_blockmap")
 
 
+def _nbytes(t: Optional[torch.Tensor]) -> int:
+    return 0 if t is None else t.numel() * t.element_size()
+
+
 def ds4attn_decode(a: Args, q: torch.Tensor, blk: Optional[torch.Tensor], bq: int, o: torch.Tensor,
-                   stream=None) -> None:
+                   workspace: Optional[torch.Tensor] = None, stream=None) -> None:
+    """Decode; ``workspace`` (a device tensor of ``ds4attn_workspace_bytes(a, 0)``
+    bytes) lets the library split small batches over more workgroups; None runs
+    unsplit."""
     _check(lib().ds4attn_decode(ctypes.byref(a), q.data_ptr(), _ptr(blk), bq, o.data_ptr(),
-                                _stream(stream)), "ds4attn_decode")
+                                _ptr(workspace), _nbytes(workspace), _stream(stream)), "ds4attn_decode")
 
 
 def ds4attn_prefill(a: Args, q: torch.Tensor, blk: Optional[torch.Tensor], bq: int, o: torch.Tensor,
-                    stream=None) -> None:
+                    workspace: Optional[torch.Tensor] = None, stream=None) -> None:
     _check(lib().ds4attn_prefill(ctypes.byref(a), q.data_ptr(), _ptr(blk), bq, o.data_ptr(),
-                                 _stream(stream)), "ds4attn_prefill")
+                                 _ptr(workspace), _nbytes(workspace), _stream(stream)), "ds4attn_prefill")
+
+
+def ds4attn_workspace_bytes(a: Args, is_prefill: bool) -> int:
+    n = _i64()
+    _check(lib().ds4attn_workspace_bytes(ctypes.byref(a), int(bool(is_prefill)), ctypes.byref(n)),
+           "ds4attn_workspace_bytes")
+    return int(n.value)
 
 
 def ds4attn_decode_workspace_bytes(a: Args, splits: int) -> int:
@@ -211,20 +224,9 @@ def ds4attn_decode_workspace_bytes(a: Args, splits: int) -> int:
 
 def ds4attn_decode_split(a: Args, q: torch.Tensor, blk: Optional[torch.Tensor], bq: int, o: torch.Tensor,
                          splits: int, workspace: Optional[torch.Tensor], stream=None) -> None:
-    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     _check(lib().ds4attn_decode_split(ctypes.byref(a), q.data_ptr(), _ptr(blk), bq, o.data_ptr(), splits,
-                                      _ptr(workspace), ws_bytes, _stream(stream)), "ds4attn_decode_split")
-
-
-def split_count(a: Args, n_blocks: int) -> int:
-    """A split count for ds4attn_decode_split: about three key blocks per part, and
-    no split once the batch already puts a workgroup on half the CUs (measured: one
-    sequence of 12 blocks runs fastest with 4 parts; a 64-sequence batch only
-    loses from splitting)."""
-    groups = max(1, a.batch * a.n_tok * (a.n_head // 16))
-    if groups >= 128:
-        return 1
-    return max(1, min(64, n_blocks // 3, 256 // groups))
+                                      _ptr(workspace), _nbytes(workspace), _stream(stream)),
+           "ds4attn_decode_split")
 
 
 def ds4attn_topk(scores: torch.Tensor, k: int, idx: torch.Tensor, stream=None) -> None:

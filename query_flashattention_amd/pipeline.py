@@ -95,13 +95,14 @@ def to_device(w, device="cuda") -> DeviceProblem:
 
 
 def step(dp: DeviceProblem, entry: str = "decode", bq: int = 1, blk: Optional[torch.Tensor] = None,
-         stream=None, splits: int = 1, workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
+         stream=None, splits: Optional[int] = None, workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
     """One pass of the hot path: pad (in place) -> block map -> fused attention.
 
     ``blk`` may be a preallocated map buffer of the right size; the output is
-    ``dp.o`` (float32 [B, T, H, D]).  Decode with ``splits`` > 1 divides each
-    token's blocks over that many workgroups (``workspace``: a uint8 device buffer
-    of ``ds4attn_decode_workspace_bytes`` bytes, allocated here when omitted)."""
+    ``dp.o`` (float32 [B, T, H, D]).  ``splits``: None = the library's own plan for
+    the call (``ds4attn_workspace_bytes``; its workspace is allocated here when
+    ``workspace`` is omitted), 1 = unsplit, > 1 = decode with each token's blocks
+    divided over that many workgroups (``ds4attn_decode_split``)."""
     dp.r0.pad_in_place(stream)
     if dp.r1 is not None:
         dp.r1.pad_in_place(stream)
@@ -110,12 +111,20 @@ def step(dp: DeviceProblem, entry: str = "decode", bq: int = 1, blk: Optional[to
         blk = da.blockmap(a, bq, dp.q.device, stream)
     else:
         da.ds4attn_blockmap(a, bq, blk if blk.numel() else None, stream)
-    if entry == "decode" and splits > 1:
+    mp = blk if blk.numel() else None
+    if entry == "decode" and splits is not None and splits > 1:
         if workspace is None:
             nbytes = da.ds4attn_decode_workspace_bytes(a, splits)
             workspace = torch.empty(nbytes, dtype=torch.uint8, device=dp.q.device)
-        da.ds4attn_decode_split(a, dp.q, blk if blk.numel() else None, bq, dp.o, splits, workspace, stream)
+        da.ds4attn_decode_split(a, dp.q, mp, bq, dp.o, splits, workspace, stream)
         return dp.o
-    fn = da.ds4attn_decode if entry == "decode" else da.ds4attn_prefill
-    fn(a, dp.q, blk if blk.numel() else None, bq, dp.o, stream)
+    prefill = entry != "decode"
+    if splits is None and workspace is None:
+        nbytes = da.ds4attn_workspace_bytes(a, prefill)
+        if nbytes:
+            workspace = torch.empty(nbytes, dtype=torch.uint8, device=dp.q.device)
+    if splits == 1:
+        workspace = None
+    fn = da.ds4attn_prefill if prefill else da.ds4attn_decode
+    fn(a, dp.q, mp, bq, dp.o, workspace, stream)
     return dp.o

@@ -79,8 +79,8 @@ def _good_args(head_dim=512, dtype=da.F16, heads=64):
     return a
 
 
-def _decode(a, q=FAKE, o=FAKE, blk=None, bq=1):
-    return da.lib().ds4attn_decode(ctypes.byref(a), q, blk, bq, o, None)
+def _decode(a, q=FAKE, o=FAKE, blk=None, bq=1, ws=None, ws_bytes=0):
+    return da.lib().ds4attn_decode(ctypes.byref(a), q, blk, bq, o, ws, ws_bytes, None)
 
 
 @pytest.mark.parametrize("mutate,expect", [
@@ -108,7 +108,7 @@ def test_decode_rejects_bad_arguments(mutate, expect):
 
 def test_null_pointers_and_tile_size():
     lib = da.lib()
-    assert lib.ds4attn_decode(None, FAKE, None, 1, FAKE, None) == da.E_INVAL
+    assert lib.ds4attn_decode(None, FAKE, None, 1, FAKE, None, 0, None) == da.E_INVAL
     a = _good_args()
     assert _decode(a, q=None) == da.E_INVAL
     assert _decode(a, o=FAKE + 4) == da.E_INVAL
@@ -124,7 +124,7 @@ def test_empty_problems_succeed_without_launch():
     assert _decode(a, q=None, o=None) == da.OK
     a = _good_args()
     a.n_tok = 0
-    assert da.lib().ds4attn_prefill(ctypes.byref(a), None, None, 16, None, None) == da.OK
+    assert da.lib().ds4attn_prefill(ctypes.byref(a), None, None, 16, None, None, 0, None) == da.OK
     assert da.lib().ds4attn_blockmap(ctypes.byref(a), 16, None, None) == da.OK
 
 
@@ -157,6 +157,13 @@ def test_pad_rejects_bad_arguments():
     r.v = FAKE + (1 << 24)
     assert lib.ds4attn_pad(ctypes.byref(r), 1, 64, da.F32, out, out, 32 * 256, 256, None, 0,
                            None) == da.E_INVAL
+    # a V output overlapping the K input (K and V inputs distinct), and the mirror case
+    r.v = FAKE + (1 << 24)
+    assert lib.ds4attn_pad(ctypes.byref(r), 1, 64, da.F32, out, FAKE + 512, 32 * 256, 256, None, 0,
+                           None) == da.E_INVAL
+    assert lib.ds4attn_pad(ctypes.byref(r), 1, 64, da.F32, r.v + 512, out, 32 * 256, 256, None, 0,
+                           None) == da.E_INVAL
+    r.v = FAKE
     r0 = da.Region()
     assert lib.ds4attn_pad(ctypes.byref(r0), 1, 64, da.F32, None, None, 0, 0, None, 0, None) == da.OK
     # validity output overlapping the validity input without being it
@@ -329,7 +336,7 @@ def test_split_decode_rejects_bad_arguments():
     assert split(a, 0) == da.E_INVAL
     assert split(a, 65) == da.E_INVAL
     assert split(a, 4, w=None) == da.E_INVAL
-    assert split(a, 4, nbytes=need - 1) == da.E_INVAL
+    assert split(a, 4, nbytes=need - 1) == da.E_WORKSPACE
     assert split(a, 4, w=ws + 8) == da.E_INVAL                   # misaligned
     assert split(a, 4, w=FAKE) == da.E_INVAL                     # overlaps o
     g = _good_args(heads=8)                                      # no matrix-core kernel
@@ -361,7 +368,7 @@ def test_binding_fails_loudly_without_library(tmp_path, monkeypatch):
 
 
 def _prefill(a, q=FAKE, o=FAKE, blk=None, bq=1):
-    return da.lib().ds4attn_prefill(ctypes.byref(a), q, blk, bq, o, None)
+    return da.lib().ds4attn_prefill(ctypes.byref(a), q, blk, bq, o, None, 0, None)
 
 
 @pytest.mark.parametrize("flags,fp8,entry,expect", [
@@ -380,3 +387,62 @@ def test_decode_split_flags_need_the_matrix_core_kernel():
     a = _good_args(head_dim=128)
     a.flags = da.FLAG_DECODE_KEYS
     assert _decode(a) == da.E_UNSUPPORTED
+
+
+def _ratio128_args(batch=1):
+    """One decode token of a ratio-128 layer at 32K: 128 raw rows + 256 compressed slots."""
+    a = _good_args()
+    a.batch = batch
+    a.r1.k = a.r1.v = FAKE + (1 << 30)
+    a.r1.n_rows = 256
+    a.r1.stride_row = 1024
+    a.r1.stride_b = 256 * 1024
+    return a
+
+
+def test_workspace_plan():
+    """The library splits a decode batch that leaves most CUs idle: one sequence of
+    the ratio-128 layer (4 groups of 16 heads, 12 key blocks) in 4 parts; a
+    64-sequence batch, prefill and the vector-ALU kernel run unsplit."""
+    rec = 16 * 512 * 4 + 128
+    assert da.ds4attn_workspace_bytes(_ratio128_args(), False) == 4 * 4 * rec
+    assert da.ds4attn_workspace_bytes(_ratio128_args(64), False) == 0
+    assert da.ds4attn_workspace_bytes(_ratio128_args(), True) == 0
+    assert da.ds4attn_workspace_bytes(_good_args(), False) == 0               # 4 blocks: too short to split
+    assert da.ds4attn_workspace_bytes(_good_args(heads=8), False) == 0        # vector-ALU kernel
+    g = _ratio128_args()
+    g.flags = da.FLAG_GENERIC
+    assert da.ds4attn_workspace_bytes(g, False) == 0
+    w = _ratio128_args()
+    w.window = 128
+    w.r0.n_rows = 4096                      # 128-row window: at most 6 blocks reachable + 8
+    assert da.ds4attn_workspace_bytes(w, False) == 4 * 4 * rec
+    e = _ratio128_args()
+    e.batch = 0
+    assert da.ds4attn_workspace_bytes(e, False) == 0
+    lib = da.lib()
+    n = ctypes.c_int64()
+    assert lib.ds4attn_workspace_bytes(None, 0, ctypes.byref(n)) == da.E_INVAL
+    assert lib.ds4attn_workspace_bytes(ctypes.byref(_ratio128_args()), 0, None) == da.E_INVAL
+    bad = _ratio128_args()
+    bad.head_dim = 96
+    assert lib.ds4attn_workspace_bytes(ctypes.byref(bad), 0, ctypes.byref(n)) == da.E_UNSUPPORTED
+
+
+def test_decode_workspace_checked_before_launch():
+    a = _ratio128_args()
+    need = da.ds4attn_workspace_bytes(a, False)
+    ws = FAKE + (1 << 32)
+    assert _decode(a, ws=ws, ws_bytes=need - 16) == da.E_WORKSPACE
+    assert _decode(a, ws=ws + 8, ws_bytes=need) == da.E_INVAL      # misaligned
+    assert _decode(a, ws=FAKE, ws_bytes=need) == da.E_INVAL        # overlaps o
+    assert _decode(a, ws=ws, ws_bytes=-1) == da.E_INVAL
+
+
+def test_tile_larger_than_the_chunk():
+    """bq is clamped to the chunk: any bq >= n_tok is one tile (no 32-bit overflow)."""
+    a = _good_args()
+    a.n_tok = 2048
+    assert da.ds4attn_blockmap_dims(a, 2 ** 31 - 1) == (1, 4)
+    a.batch = 0
+    assert _decode(a, q=None, o=None, blk=FAKE, bq=2 ** 31 - 1) == da.OK

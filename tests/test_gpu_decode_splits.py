@@ -18,6 +18,7 @@ import torch
 from oracle import reference as ref
 from query_flashattention_amd import ds4attn as da
 from query_flashattention_amd import pipeline, workloads as wl
+from tests.parity_util import compare as _compare, oracle_full
 
 pytestmark = pytest.mark.gpu
 
@@ -31,14 +32,6 @@ def _need_gpu():
     if not torch.cuda.is_available():
         pytest.fail("GPU tests need an MI355X; none is visible")
     da.lib()  # fail loudly if the HIP library is missing
-
-
-def _compare(out, want, label):
-    err = np.abs(np.asarray(out, dtype=np.float64) - want)
-    mx, mean = float(err.max()) if err.size else 0.0, float(err.mean()) if err.size else 0.0
-    print(f"{label}: max abs {mx:.3e} mean abs {mean:.3e} over {err.size} values")
-    assert np.isfinite(out).all(), label
-    assert mx <= MAX_ABS and mean <= MEAN_ABS, (label, mx, mean)
 
 
 def _run(w, flags, use_map=True, splits=1):
@@ -55,7 +48,7 @@ def _run(w, flags, use_map=True, splits=1):
             ws = torch.empty(da.ds4attn_decode_workspace_bytes(a, splits), dtype=torch.uint8, device=DEV)
             da.ds4attn_decode_split(a, dp.q, None, 1, dp.o, splits, ws)
         else:
-            da.ds4attn_decode(a, dp.q, None, 1, dp.o)
+            da.ds4attn_decode(a, dp.q, None, 1, dp.o)   # no workspace: unsplit
         out = dp.o
     torch.cuda.synchronize()
     return out.cpu().double().numpy()
@@ -69,12 +62,9 @@ def test_workload_full(name, split):
 
 
 @pytest.mark.parametrize("split", list(SPLITS))
-def test_ratio4_sampled(split):
+def test_ratio4_full(split):
     w = wl.named("decode_r4")
-    out = _run(w, SPLITS[split])
-    seqs = [0, 5, 31, 32, 63]
-    want = ref.attention(ref.from_workload(w), tokens=[(b, 0) for b in seqs])
-    _compare(out[seqs, 0], want, f"decode_r4/{split}")
+    _compare(_run(w, SPLITS[split]), oracle_full("decode_r4"), f"decode_r4/{split}")
 
 
 CASES = [

@@ -24,6 +24,7 @@ from oracle import fp8 as ofp8
 from oracle import reference as ref
 from query_flashattention_amd import ds4attn as da
 from query_flashattention_amd import pipeline, workloads as wl
+from tests.parity_util import compare as _compare
 
 pytestmark = pytest.mark.gpu
 
@@ -36,14 +37,6 @@ def _need_gpu():
     if not torch.cuda.is_available():
         pytest.fail("GPU tests need an MI355X; none is visible")
     da.lib()  # fail loudly if the HIP library is missing
-
-
-def _compare(out, want, label):
-    err = np.abs(np.asarray(out, dtype=np.float64) - want)
-    mx, mean = float(err.max()) if err.size else 0.0, float(err.mean()) if err.size else 0.0
-    print(f"{label}: max abs {mx:.3e} mean abs {mean:.3e} over {err.size} values")
-    assert np.isfinite(out).all(), label
-    assert mx <= MAX_ABS and mean <= MEAN_ABS, (label, mx, mean)
 
 
 def _oracle_problem(w) -> ref.Problem:
@@ -63,9 +56,19 @@ def _oracle_problem(w) -> ref.Problem:
                        q_pos0=int(w.q_pos0), k_pos0=int(w.k_pos0), r1=region(w.r1), r1_index=idx)
 
 
+_FULL = {}
+
+
+def _oracle_full(name):
+    """The oracle over every token of a named FP8 workload, computed once."""
+    if name not in _FULL:
+        _FULL[name] = ref.attention(_oracle_problem(wl.named(name)))
+    return _FULL[name]
+
+
 def _run(w, entry, bq):
     dp = pipeline.to_device(w, DEV)
-    out = pipeline.step(dp, entry, bq)
+    out = pipeline.step(dp, entry, bq, splits=1)
     torch.cuda.synchronize()
     return out.cpu().double().numpy()
 
@@ -130,20 +133,16 @@ def test_attention_fp8_decode_full(name):
     _compare(out, ref.attention(_oracle_problem(w)), name)
 
 
-def test_attention_fp8_decode_ratio4_sampled():
+def test_attention_fp8_decode_ratio4_full():
     w = wl.named("decode_r4_fp8")
-    out = _run(w, "decode", 1)
-    seqs = [0, 1, 17, 31, 32, 50, 62, 63]
-    want = ref.attention(_oracle_problem(w), tokens=[(b, 0) for b in seqs])
-    _compare(out[seqs, 0], want, "decode_r4_fp8 sampled")
+    _compare(_run(w, "decode", 1), _oracle_full("decode_r4_fp8"), "decode_r4_fp8 full")
 
 
-def test_attention_fp8_prefill_ratio4_sampled():
+def test_attention_fp8_prefill_ratio4_full():
+    """The 2048-token ratio-4 chunk on FP8 rows, every token against the oracle."""
     w = wl.named("prefill_r4_fp8")
     out = _run(w, "prefill", da.ds4attn_prefill_bq())
-    toks = [0, 1, 31, 32, 127, 128, 129, 700, 1023, 1024, 1500, 2046, 2047]
-    want = ref.attention(_oracle_problem(w), tokens=[(0, t) for t in toks])
-    _compare(out[0, toks], want, "prefill_r4_fp8 sampled")
+    _compare(out, _oracle_full("prefill_r4_fp8"), "prefill_r4_fp8 full")
 
 
 FP8_CASES = [
@@ -225,7 +224,7 @@ FP8_DECODE_CASES = [(c[0], c[1]) for c in FP8_CASES] + [
 def _run_flags(w, flags, splits=1):
     dp = pipeline.to_device(w, DEV)
     dp.flags = flags
-    out = pipeline.step(dp, "decode", 1, splits=splits)
+    out = pipeline.step(dp, "decode", 1, splits=splits)   # splits=1: unsplit
     torch.cuda.synchronize()
     return out.cpu().double().numpy()
 
@@ -250,10 +249,7 @@ def test_attention_fp8_workloads_splits(split):
     w = wl.named("decode_r128_fp8")
     _compare(_run_flags(w, FP8_SPLITS[split]), ref.attention(_oracle_problem(w)), f"decode_r128_fp8/{split}")
     w = wl.named("decode_r4_fp8")
-    out = _run_flags(w, FP8_SPLITS[split])
-    seqs = [0, 9, 33, 63]
-    want = ref.attention(_oracle_problem(w), tokens=[(b, 0) for b in seqs])
-    _compare(out[seqs, 0], want, f"decode_r4_fp8/{split}")
+    _compare(_run_flags(w, FP8_SPLITS[split]), _oracle_full("decode_r4_fp8"), f"decode_r4_fp8/{split}")
 
 
 @pytest.mark.parametrize("split", list(FP8_SPLITS))
