@@ -25,7 +25,9 @@
  * Conventions shared by every entry point:
  *   - Pointers marked "device" are HIP device addresses; the caller owns every
  *     buffer.  The library allocates nothing, frees nothing, keeps no pointer past
- *     the call and has no mutable global state; calls are thread-safe.
+ *     the call and has no mutable global state; calls are thread-safe.  (One
+ *     exception: ds4attn_decode_noalloc keeps its scratch in a static per-device
+ *     array, see there.)
  *   - All work is enqueued on `stream` (a hipStream_t, NULL = the null stream)
  *     and runs asynchronously; the library never synchronises.
  *   - Arguments are checked before anything is enqueued.  On any nonzero
@@ -257,6 +259,28 @@ int ds4attn_prefill(const ds4attn_args *a, const void *q, const uint8_t *blk, in
  * the same *a before looking at q, blk and o (DS4ATTN_OK, DS4ATTN_E_INVAL or
  * DS4ATTN_E_UNSUPPORTED). */
 int ds4attn_workspace_bytes(const ds4attn_args *a, int32_t is_prefill, int64_t *bytes);
+
+/*
+ * ds4attn_decode_noalloc -- ds4attn_decode for callers that cannot allocate device
+ * memory: code under HIP graph capture, tight serving loops, harnesses that forbid
+ * allocation.  Same arguments without the workspace, same result and the same
+ * work split: the split's records go to a static scratch array of the library
+ * (8,421,376 bytes = 256 records, enough for every split the plan picks), of
+ * which each device the library runs on holds its own copy until the process
+ * ends.  Nothing is allocated, freed or cleared: every record is written before
+ * it is read.
+ *   - Calls on one device share that device's array and keep no result in it; two
+ *     calls whose work overlaps in time on one device (different streams, or
+ *     different host threads without ordering) race on it and may return wrong
+ *     outputs.  Calls in order on one stream are safe.
+ *   - `stream` must belong to the current device (NULL = its null stream), else
+ *     DS4ATTN_E_INVAL.  The first call on a device looks up the array's address
+ *     there (DS4ATTN_E_HIP if that fails).
+ * Returns what ds4attn_decode returns, and DS4ATTN_E_WORKSPACE if a split needed
+ * more than the array holds (the plan never does).
+ */
+int ds4attn_decode_noalloc(const ds4attn_args *a, const void *q, const uint8_t *blk, int32_t bq,
+                           float *o, void *stream);
 
 /* The query-tile size the prefill kernel is tuned for (a map built with any
  * bq >= 1 is accepted). */

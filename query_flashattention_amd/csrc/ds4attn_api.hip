@@ -7,6 +7,7 @@
 #include "mfma_common.h"
 
 #include <cmath>
+#include <mutex>
 
 using namespace ds4attn;
 
@@ -226,6 +227,33 @@ int launch_resolved(const ds4attn_args *a, Resolved &R, const void *q, const uin
   return e == hipSuccess ? DS4ATTN_OK : DS4ATTN_E_HIP;
 }
 
+// ---------------------------------------------------------------------------- static scratch
+// The split records of ds4attn_decode_noalloc live in this array: each device the
+// library runs on holds its own copy until the process ends.  The decode plan
+// splits only batches of fewer than 128 groups of 16 heads, into at most 256 /
+// groups parts, so a call never needs more than 256 records.
+constexpr int64_t kScratchRecords = 256;
+constexpr int64_t kScratchBytes = kScratchRecords * kSplitRecord;
+static __device__ __align__(256) char scratch[kScratchBytes];
+
+// The device address of this device's `scratch`, looked up once per device (the
+// array's name is a host-side stand-in; only this address may reach a kernel).
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void *g_scratch_ptr[kMaxDevices] = {};
+
+int scratch_of_device(int dev, void **out) {
+  if (dev < 0 || dev >= kMaxDevices) return DS4ATTN_E_UNSUPPORTED;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void *ptr = nullptr;
+    if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || !ptr) return DS4ATTN_E_HIP;
+    g_scratch_ptr[dev] = ptr;
+  }
+  *out = g_scratch_ptr[dev];
+  return DS4ATTN_OK;
+}
+
 // ds4attn_decode / ds4attn_prefill: the library's plan, run in the caller's workspace.
 int run_planned(const ds4attn_args *a, const void *q, const uint8_t *blk, int32_t bq, float *o, void *ws,
                 int64_t ws_bytes, void *stream, bool prefill) {
@@ -336,6 +364,27 @@ int ds4attn_decode(const ds4attn_args *a, const void *q, const uint8_t *blk, int
 int ds4attn_prefill(const ds4attn_args *a, const void *q, const uint8_t *blk, int32_t bq, float *o,
                     void *workspace, int64_t workspace_bytes, void *stream) {
   return run_planned(a, q, blk, bq, o, workspace, workspace_bytes, stream, true);
+}
+
+int ds4attn_decode_noalloc(const ds4attn_args *a, const void *q, const uint8_t *blk, int32_t bq, float *o,
+                           void *stream) {
+  Resolved R;
+  int st = resolve_args(a, false, R);
+  if (st) return st;
+  const int splits = plan_splits(R, false);
+  if (splits <= 1) return launch_resolved(a, R, q, blk, bq, o, false, 1, nullptr, 0, stream);
+  if (split_workspace_bytes(a, splits) > kScratchBytes) return DS4ATTN_E_WORKSPACE;
+  // the array of the device the kernels run on, which must be the current device
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess) return DS4ATTN_E_HIP;
+  if (stream) {
+    hipDevice_t sdev = -1;
+    if (hipStreamGetDevice((hipStream_t)stream, &sdev) != hipSuccess) return DS4ATTN_E_HIP;
+    if (sdev != dev) return DS4ATTN_E_INVAL;
+  }
+  void *ws = nullptr;
+  if ((st = scratch_of_device(dev, &ws))) return st;
+  return launch_resolved(a, R, q, blk, bq, o, false, splits, ws, kScratchBytes, stream);
 }
 
 int ds4attn_workspace_bytes(const ds4attn_args *a, int32_t is_prefill, int64_t *bytes) {

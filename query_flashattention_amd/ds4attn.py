@@ -49,7 +49,8 @@ class Args(ctypes.Structure):
 
 
 EXPORTS = ("ds4attn_pad", "ds4attn_blockmap", "ds4attn_blockmap_dims", "ds4attn_decode",
-           "ds4attn_prefill", "ds4attn_workspace_bytes", "ds4attn_prefill_bq", "ds4attn_topk",
+           "ds4attn_prefill", "ds4attn_workspace_bytes", "ds4attn_decode_noalloc", "ds4attn_prefill_bq",
+           "ds4attn_topk",
            "ds4attn_quantize_fp8", "ds4attn_decode_split", "ds4attn_decode_workspace_bytes",
            "ds4attn_compress", "ds4attn_status_string")
 
@@ -72,6 +73,8 @@ def lib() -> ctypes.CDLL:
             getattr(h, name).argtypes = [ctypes.POINTER(Args), _c_void_p, _c_void_p, _i32,
                                          _c_void_p, _c_void_p, _i64, _c_void_p]
         h.ds4attn_workspace_bytes.argtypes = [ctypes.POINTER(Args), _i32, ctypes.POINTER(_i64)]
+        h.ds4attn_decode_noalloc.argtypes = [ctypes.POINTER(Args), _c_void_p, _c_void_p, _i32, _c_void_p,
+                                             _c_void_p]
         h.ds4attn_topk.argtypes = [_c_void_p, _i64, _i32, _i64, _i32, _c_void_p, _i64, _c_void_p]
         h.ds4attn_decode_split.argtypes = [ctypes.POINTER(Args), _c_void_p, _c_void_p, _i32, _c_void_p,
                                            _i32, _c_void_p, _i64, _c_void_p]
@@ -206,6 +209,14 @@ def ds4attn_prefill(a: Args, q: torch.Tensor, blk: Optional[torch.Tensor], bq: i
                     workspace: Optional[torch.Tensor] = None, stream=None) -> None:
     _check(lib().ds4attn_prefill(ctypes.byref(a), q.data_ptr(), _ptr(blk), bq, o.data_ptr(),
                                  _ptr(workspace), _nbytes(workspace), _stream(stream)), "ds4attn_prefill")
+
+
+def ds4attn_decode_noalloc(a: Args, q: torch.Tensor, blk: Optional[torch.Tensor], bq: int, o: torch.Tensor,
+                           stream=None) -> None:
+    """Decode with the split's scratch in the library's static per-device array
+    (no allocation anywhere); calls that overlap in time on one device race."""
+    _check(lib().ds4attn_decode_noalloc(ctypes.byref(a), q.data_ptr(), _ptr(blk), bq, o.data_ptr(),
+                                        _stream(stream)), "ds4attn_decode_noalloc")
 
 
 def ds4attn_workspace_bytes(a: Args, is_prefill: bool) -> int:

@@ -446,3 +446,16 @@ def test_tile_larger_than_the_chunk():
     assert da.ds4attn_blockmap_dims(a, 2 ** 31 - 1) == (1, 4)
     a.batch = 0
     assert _decode(a, q=None, o=None, blk=FAKE, bq=2 ** 31 - 1) == da.OK
+
+
+def test_noalloc_decode_checks_before_launch():
+    """The no-allocation decode entry point validates like ds4attn_decode before any
+    HIP call; an empty problem succeeds without touching a device."""
+    lib = da.lib()
+    assert lib.ds4attn_decode_noalloc(None, FAKE, None, 1, FAKE, None) == da.E_INVAL
+    a = _ratio128_args()
+    a.head_dim = 96
+    assert lib.ds4attn_decode_noalloc(ctypes.byref(a), FAKE, None, 1, FAKE, None) == da.E_UNSUPPORTED
+    a = _ratio128_args()
+    a.batch = 0
+    assert lib.ds4attn_decode_noalloc(ctypes.byref(a), None, None, 1, None, None) == da.OK
