@@ -274,3 +274,20 @@ def test_tile_longer_than_the_chunk():
     want = _oracle(w)
     compare(_run(w, "prefill", bq=big), want, "prefill bq = 2^31 - 1")
     compare(_run(w, "dims", bq=big), want, "decode bq = 2^31 - 1")
+
+
+# --------------------------------------------------------------------------- large score jumps
+
+@pytest.mark.parametrize("mode", ["prefill", "dims", "keys", "split3"])
+def test_score_jump_after_the_first_block(mode):
+    """Keys of a later block scaled by 16: the scores there exceed the first block's
+    maximum by far more than 2^8 in the base-2 softmax, so every kernel must move
+    its reference max and rescale the output after weights exist.  Compared with
+    the oracle."""
+    w = wl.random_problem(125, batch=1, tokens=19, heads=64, head_dim=512, n0=160, q_std=2.0, window=96,
+                          q_pos0=140, k_pos0=0)
+    k = w.r0.k.clone()
+    k[:, 96:128] = (k[:, 96:128].float() * 16).half()
+    w = dataclasses.replace(w, r0=dataclasses.replace(w.r0, k=k))
+    want = _oracle(w)
+    compare(_run(w, mode), want, f"score jump/{mode}")
