@@ -71,7 +71,14 @@ enum { DS4ATTN_F16 = 0, DS4ATTN_F32 = 1, DS4ATTN_E4M3 = 2 };
  *              This is the cache format ds4attn_quantize_fp8 writes ([P-DS4]
  *              "Architecture Deep Dive", Whole-Model Graph Execution: K/V rows are
  *              quantized to FP8 before they are stored; the element format and the
- *              per-row scale are this library's choice, the pages give none). */
+ *              per-row scale are this library's choice, the pages give none).
+ *              In the attention a K row's scale multiplies its scores in float32;
+ *              a V row's values are formed in float16 as decode(code) times half
+ *              the row scale (rounded to float16), the output doubled in float32.
+ *              V values therefore keep float16's range (any row whose values lie
+ *              within +-65504, the range ds4attn_quantize_fp8 accepts from float16
+ *              rows) and its absolute resolution near zero (2^-25 on the halved
+ *              value). */
 enum { DS4ATTN_KV_PLAIN = 0, DS4ATTN_KV_FP8_E4M3 = 1 };
 
 /* Status byte values of the block map ([P-Metal] "Mask Handling and Block Skipping":

@@ -80,6 +80,11 @@ __global__ __launch_bounds__(256, MODE == kSplitHeads ? 2 : 1) void attn_staged_
   // the waves at the end of the block
   constexpr bool SPLITKV = MODE == kSplitDims && !FP8;
   constexpr int KPD = KEYS ? 4 : 2;   // K operand reads in flight (k-steps)
+  // FP8 V rows are multiplied by half their row scale in float16, so that a row
+  // whose values reach the float16 maximum cannot overflow when its scale is
+  // rounded to float16 (448 * fp16(65504 / 448) rounds to inf, 224 * fp16(32752 /
+  // 448) does not); the output (or a split part's record) gets the factor 2 back.
+  constexpr float kOut = FP8 ? 2.f : 1.f;
   // V operand reads in flight (output tiles); FP8 rows in HEADS take one fewer,
   // which keeps their conversions within 256 registers without spilling
   constexpr int VPD = KEYS ? 8 : (MODE == kSplitHeads && FP8 ? 3 : 4);
@@ -871,8 +876,9 @@ __global__ __launch_bounds__(256, MODE == kSplitHeads ? 2 : 1) void attn_staged_
                                f8_row_off(trow) + 8 * (lane & 1);
         const float4 vlo = *(const float4 *)(sct + 32 + 4 * g);
         const float4 vhi = *(const float4 *)(sct + 48 + 4 * g);
-        const half8 vsc = {(_Float16)vlo.x, (_Float16)vlo.y, (_Float16)vlo.z, (_Float16)vlo.w,
-                           (_Float16)vhi.x, (_Float16)vhi.y, (_Float16)vhi.z, (_Float16)vhi.w};
+        const half8 vsc = {(_Float16)(0.5f * vlo.x), (_Float16)(0.5f * vlo.y), (_Float16)(0.5f * vlo.z),
+                           (_Float16)(0.5f * vlo.w), (_Float16)(0.5f * vhi.x), (_Float16)(0.5f * vhi.y),
+                           (_Float16)(0.5f * vhi.z), (_Float16)(0.5f * vhi.w)};
         auto vload = [&](int dt) __attribute__((always_inline)) -> uint2 {
           const int2v rv = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
               (__attribute__((address_space(3))) int2v *)(vsrc + 16 * dt));
@@ -975,7 +981,7 @@ __global__ __launch_bounds__(256, MODE == kSplitHeads ? 2 : 1) void attn_staged_
       const float mw = mlw[ww * 16 + c16];
       lall += (mw == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(mw - mall)) * mlw[64 + ww * 16 + c16];
     }
-    const float f = m == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m - mall);
+    const float f = m == -INFINITY ? 0.f : kOut * __builtin_amdgcn_exp2f(m - mall);
     // wave w finishes output tiles 8w .. 8w+7 (dims 128w .. 128w+127); the others
     // hand it theirs through LDS: xo[wave][tile][lane].  Instantiated per wave
     // index, so that the tile selection is resolved at compile time.
@@ -1180,12 +1186,13 @@ __global__ __launch_bounds__(256, MODE == kSplitHeads ? 2 : 1) void attn_staged_
       const int trow = trk < 4 ? 4 * g + trk : 16 + 4 * g + (trk - 4);
       const lds_char *vsrc = (const lds_char *)(__attribute__((address_space(3))) const void *)vtc +
                              f8_row_off(trow) + d0 + 8 * (lane & 1);
-      // V row scales of the slot rows, in float16
+      // half the V row scales of the slot rows, in float16 (see kOut)
       const float *sc = stile(buf);
       const float4 vlo = *(const float4 *)(sc + 16 * g + 8);
       const float4 vhi = *(const float4 *)(sc + 16 * (g ^ 2) + 12);
-      const half8 vsc = {(_Float16)vlo.x, (_Float16)vlo.y, (_Float16)vlo.z, (_Float16)vlo.w,
-                         (_Float16)vhi.x, (_Float16)vhi.y, (_Float16)vhi.z, (_Float16)vhi.w};
+      const half8 vsc = {(_Float16)(0.5f * vlo.x), (_Float16)(0.5f * vlo.y), (_Float16)(0.5f * vlo.z),
+                         (_Float16)(0.5f * vlo.w), (_Float16)(0.5f * vhi.x), (_Float16)(0.5f * vhi.y),
+                         (_Float16)(0.5f * vhi.z), (_Float16)(0.5f * vhi.w)};
       auto vload = [&](int dt) __attribute__((always_inline)) -> uint2 {
         const int2v r = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
             (__attribute__((address_space(3))) int2v *)(vsrc + 16 * dt));
@@ -1279,7 +1286,7 @@ __global__ __launch_bounds__(256, MODE == kSplitHeads ? 2 : 1) void attn_staged_
       return (sl < RPT ? kts : vts) + (sl % RPT) * kORow;
     };
     constexpr bool part = PARTS;
-    const float sc = part ? 1.f : inv;
+    const float sc = (part ? 1.f : inv) * kOut;
     lds_w *row = slot(c16) + 4 * d0 + 16 * g;
 #pragma unroll
     for (int dt = 0; dt < NDT; ++dt) *(__attribute__((address_space(3))) floatx4 *)(row + 64 * dt) = o[dt] * sc;
@@ -1330,7 +1337,8 @@ __global__ __launch_bounds__(256, MODE == kSplitHeads ? 2 : 1) void attn_staged_
       if (wj >= 0 && wj < WPP) {
         lds_w *row = slot(16 * wj + c16) + 16 * g;
 #pragma unroll
-        for (int dt = 0; dt < NDT; ++dt) *(__attribute__((address_space(3))) floatx4 *)(row + 64 * dt) = o[dt] * inv;
+        for (int dt = 0; dt < NDT; ++dt)
+          *(__attribute__((address_space(3))) floatx4 *)(row + 64 * dt) = o[dt] * (inv * kOut);
       }
       lds_barrier();
 #pragma unroll
@@ -1346,7 +1354,7 @@ __global__ __launch_bounds__(256, MODE == kSplitHeads ? 2 : 1) void attn_staged_
   }
   float *ob = (float *)(p.o + b * p.o_sb + t * p.o_st + (int64_t)h * p.o_sh) + d0 + 4 * g;
 #pragma unroll
-  for (int dt = 0; dt < NDT; ++dt) *(floatx4 *)(ob + 16 * dt) = o[dt] * inv;
+  for (int dt = 0; dt < NDT; ++dt) *(floatx4 *)(ob + 16 * dt) = o[dt] * (inv * kOut);
 }
 
 template <int MODE>

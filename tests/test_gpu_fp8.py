@@ -259,3 +259,36 @@ def test_attention_fp8_split_over_workgroups(split):
     w = wl.fp8_variant(wl.random_problem(77, **kw), 78)
     want = ref.attention(_oracle_problem(w))
     _compare(_run_flags(w, FP8_SPLITS[split], splits=3), want, f"fp8 index/{split} x3")
+
+
+@pytest.mark.parametrize("mode", ["prefill", "dims", "keys"])
+def test_attention_fp8_values_at_the_float16_maximum(mode):
+    """V rows quantized (by the oracle's quantizer) from float16 rows that reach
+    +-65504, so their scale is 65504/448: no value may overflow to inf in any
+    kernel.  Every V row is scaled alike (standard deviation 8000), so O scales with
+    them; errors are compared after dividing both sides by 65504."""
+    tokens = 16 if mode == "prefill" else 1
+    w = wl.random_problem(141, batch=2, tokens=tokens, heads=64, head_dim=512, n0=70, window=48, q_pos0=60,
+                          k_pos0=0)
+    g = torch.Generator().manual_seed(142)
+    v = torch.randn(w.r0.v.shape, generator=g) * 8000
+    v[:, ::3, 5] = 65504.0
+    v[:, 1::3, 9] = -65504.0
+    v = v.clamp(-65504, 65504).half()
+    kc, ks = ofp8.quantize_rows(w.r0.k.numpy())
+    vc, vs = ofp8.quantize_rows(v.numpy())
+    assert float(vs.max()) == float(np.float32(65504.0) / np.float32(448.0))
+    r0 = wl.RegionInputs(torch.from_numpy(kc), torch.from_numpy(vc), w.r0.n_rows, None, None,
+                         torch.from_numpy(ks), torch.from_numpy(vs))
+    w8 = dataclasses.replace(w, r0=r0)
+    want = ref.attention(_oracle_problem(w8))
+    dp = pipeline.to_device(w8, DEV)
+    if mode == "prefill":
+        out = pipeline.step(dp, "prefill", da.ds4attn_prefill_bq(), splits=1)
+    else:
+        dp.flags = da.FLAG_DECODE_DIMS if mode == "dims" else da.FLAG_DECODE_KEYS
+        out = pipeline.step(dp, "decode", 1, splits=1)
+    torch.cuda.synchronize()
+    out = out.cpu().double().numpy()
+    assert np.isfinite(out).all()
+    _compare(out / 65504.0, want / 65504.0, f"fp8 V rows at +-65504/{mode}")
