@@ -121,7 +121,7 @@ def counts(w):
 class Runner:
     """Resident input sets, graphs of whole steps and timing helpers for one workload."""
 
-    def __init__(self, name, n_sets, device="cuda:0", splits=1):
+    def __init__(self, name, n_sets, device="cuda:0", splits=None):
         import torch
         from query_flashattention_amd import ds4attn as da, pipeline, workloads
 
@@ -135,10 +135,23 @@ class Runner:
         for dp in self.sets:
             nt, nb = da.ds4attn_blockmap_dims(dp.args(), self.bq)
             self.blks.append(torch.empty((dp.q.shape[0], nt, nb), dtype=torch.uint8, device=device))
-        # split decode: each token's blocks over `splits` workgroups, partials in a workspace
+        # the workspace of the library's own split plan (splits=None: ds4attn_decode
+        # picks it) or of a chosen split (ds4attn_decode_split); None when unsplit
         self.splits = splits
-        self.ws = [torch.empty(max(1, da.ds4attn_decode_workspace_bytes(dp.args(), splits)), dtype=torch.uint8,
-                               device=device) for dp in self.sets]
+
+        def ws_bytes(a):
+            if splits is None:
+                return da.ds4attn_workspace_bytes(a, self.kind == "prefill")
+            return da.ds4attn_decode_workspace_bytes(a, splits)
+
+        self.ws = []
+        for dp in self.sets:
+            n = ws_bytes(dp.args())
+            self.ws.append(torch.empty(n, dtype=torch.uint8, device=device) if n else None)
+        # parts per token: the workspace holds one record set per part
+        a = self.sets[0].args()
+        per_part = da.ds4attn_decode_workspace_bytes(a, 2) // 2
+        self.parts = max(1, ws_bytes(a) // per_part) if per_part and self.kind == "decode" else 1
         torch.cuda.synchronize()
 
     def step(self, i):
@@ -148,12 +161,12 @@ class Runner:
     def attention_only(self, i):
         dp = self.sets[i]
         blk = self.blks[i]
-        if self.splits > 1:
+        if self.splits is not None and self.splits > 1:
             self.da.ds4attn_decode_split(dp.args(), dp.q, blk if blk.numel() else None, self.bq, dp.o,
                                          self.splits, self.ws[i])
             return
         fn = self.da.ds4attn_decode if self.kind == "decode" else self.da.ds4attn_prefill
-        fn(dp.args(), dp.q, blk if blk.numel() else None, self.bq, dp.o)
+        fn(dp.args(), dp.q, blk if blk.numel() else None, self.bq, dp.o, self.ws[i])
 
     def capture(self):
         """One graph per full rotation of the input sets and one per single set."""
@@ -260,6 +273,21 @@ def _oracle_rate(p, seconds):
             return reps, el
 
 
+def host_cpu():
+    """The host the CPU baseline ran on: the cores in the process's affinity mask
+    and the CPU model (from /proc/cpuinfo)."""
+    model = "unknown"
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    return {"affinity_cores": len(os.sched_getaffinity(0)), "cpu_model": model}
+
+
 def cpu_baseline(w, kv_bytes_per_step, seconds):
     """The float64 oracle on the host, over whole batches of the same workload,
     repeated until `seconds` of CPU work; K/V GB/s on the same algorithmic bytes.
@@ -275,7 +303,8 @@ def cpu_baseline(w, kv_bytes_per_step, seconds):
     out = {"value": round(kv_bytes_per_step * reps / el / 1e9, 3), "unit": "GB/s", "cores": threads,
            "kind": "oracle",
            "sample": f"float64 NumPy oracle over the whole batch ({w.q.shape[0]} sequences), "
-                     f"{reps} repetitions in {el:.1f} s"}
+                     f"{reps} repetitions in {el:.1f} s",
+           **host_cpu()}
     if threadpool_limits is not None:
         with threadpool_limits(1):
             reps1, el1 = _oracle_rate(p, seconds / 2)
@@ -332,18 +361,17 @@ def measured_peaks(torch):
                       f"{mgrid} workgroups x 4 waves x {iters} x 8 independent v_mfma_f32_16x16x32_f16"}
 
 
-def decode_kernel_label(w):
-    """The decode kernel the library picks for a workload (the same rule as its
-    dispatch: the KEYS split when a token's list can hold at least 8 blocks)."""
+def decode_kernel_label(w, parts=1):
+    """The decode kernel the library picks for a workload split into `parts` (the
+    same rule as its dispatch: the KEYS split when each part's share of the longest
+    possible block list holds at least 8 blocks)."""
     nb0 = -(-w.r0.n_rows // 32)
-    indexed = w.r1_index is not None
+    if w.window > 0:
+        nb0 = min(nb0, w.window // 32 + 2)
     nb1 = 0
     if w.r1 is not None and w.r1.n_rows > 0:
-        nb1 = -(-w.r1_index.shape[-1] // 32) if indexed else -(-w.r1.n_rows // 32)
-    nbd = nb0 + (0 if indexed else nb1)
-    dense = min(nbd, w.window // 32 + 2) if w.window > 0 else nbd
-    mode = 2 if dense + (nb1 if indexed else 0) >= 8 else 1
-    return mode
+        nb1 = -(-w.r1_index.shape[-1] // 32) if w.r1_index is not None else -(-w.r1.n_rows // 32)
+    return 2 if (nb0 + nb1) // max(1, parts) >= 8 else 1
 
 
 def prefill_cpu_tflops(w, n_tokens, seconds):
@@ -495,7 +523,7 @@ def quantize_timing(b, n, d=512, n_sets=4, reps=25):
             "gbs_kernel": round(nbytes / (ms * 1e-3) / 1e9, 1)}
 
 
-def run_workload(name, steps, warmup, n_sets, launches, splits=1):
+def run_workload(name, steps, warmup, n_sets, launches, splits=None):
     r = Runner(name, n_sets, splits=splits)
     for k in range(warmup):
         r.step(k % n_sets)
@@ -616,7 +644,8 @@ def main():
                      "single_launch_ms_p10": round(k["single_launch_p10"], 5),
                      "single_launch_ms_p90": round(k["single_launch_p90"], 5)}
             if not other.startswith("prefill"):
-                entry["kernel_split"] = {1: "DIMS", 2: "KEYS"}[decode_kernel_label(r.w)]
+                entry["kernel_split"] = {1: "DIMS", 2: "KEYS"}[decode_kernel_label(r.w, r.parts)]
+                entry["split_parts"] = r.parts
             if other.startswith("prefill"):
                 entry["tflops_step"] = round(cc["flops"] / (ms * 1e-3) / 1e12, 2)
                 entry["tflops_kernel"] = round(cc["flops"] / (k["mean"] * 1e-3) / 1e12, 2)
@@ -630,14 +659,15 @@ def main():
             extra[other] = entry
             del r
             torch.cuda.empty_cache()
-        # one sequence of the ratio-128 layer (12 key blocks): each token's blocks over
-        # 4 workgroups per head group, then the combine pass
-        r, s_, k = run_workload("decode_r128", 200, 3, 64, 100, splits=4)
-        extra["decode_r128_split4"] = {"ms_per_step": round(s_ * 1e3 / 200, 5),
-                                        "kernel_ms_mean": round(k["mean"], 5),
-                                        "single_launch_ms_median": round(k["single_launch_median"], 5),
-                                        "kernel_us_mean": round(k["mean"] * 1e3, 2),
-                                        "note": "partial pass + combine pass, both in the timed launches"}
+        # one sequence of the ratio-128 layer (12 key blocks) without the split that
+        # ds4attn_decode picks for it (the decode_r128 line above: 4 parts per head
+        # group plus the combine pass)
+        r, s_, k = run_workload("decode_r128", 200, 3, 64, 100, splits=1)
+        extra["decode_r128_unsplit"] = {"ms_per_step": round(s_ * 1e3 / 200, 5),
+                                         "kernel_ms_mean": round(k["mean"], 5),
+                                         "single_launch_ms_median": round(k["single_launch_median"], 5),
+                                         "kernel_us_mean": round(k["mean"] * 1e3, 2),
+                                         "note": "one workgroup per 16 heads walks all 12 blocks"}
         del r
         torch.cuda.empty_cache()
         # top-k index selection feeding the ratio-4 layers: the prefill chunk's 2048
@@ -658,7 +688,7 @@ def main():
         else:
             tf = prefill_cpu_tflops(w, 64, args.cpu_seconds)
             out["cpu_baseline"] = {"value": round(tf, 4), "unit": "TFLOP/s", "kind": "oracle",
-                                   "sample": "64 sampled tokens of the chunk"}
+                                   "sample": "64 sampled tokens of the chunk", **host_cpu()}
     print(json.dumps(out))
 
 
