@@ -60,7 +60,8 @@ enum : int { kSplitHeads = 0, kSplitDims = 1, kSplitKeys = 2 };
 // PARTS (decode only): the launch is a split decode; each workgroup takes one part
 // of its token's block list and leaves a record for the combine pass.
 template <int MODE, bool INDEXED, bool FP8, bool PARTS = false>
-__global__ __launch_bounds__(256, MODE == kSplitHeads ? 2 : 1) void attn_staged_kernel(const AttnParams p) {
+__global__ __launch_bounds__(MODE == kSplitDims && !FP8 ? 512 : 256, MODE == kSplitHeads ? 2 : 1)
+void attn_staged_kernel(const AttnParams p) {
   constexpr bool KEYS = MODE == kSplitKeys;
   // KEYS units: float16 rows go in half-blocks of 16 rows, FP8 rows in whole blocks
   // (the FP8 tiles of a block take the space of a float16 half-block, and the
@@ -74,10 +75,16 @@ __global__ __launch_bounds__(256, MODE == kSplitHeads ? 2 : 1) void attn_staged_
   // computes while the other's transfers are in flight.
   // (FP8 tiles are half the size: DIMS keeps four blocks in flight)
   constexpr int NBUF = MODE == kSplitHeads ? 1 : (FP8 ? 4 : 2);
-  // DIMS with float16 rows stages a block's K rows as soon as the score exchange
-  // has freed the K tile and its V rows after P.V, so the transfer issue (bound by
-  // the CU's vector-memory path) overlaps the softmax and P.V instead of stalling
-  // the waves at the end of the block
+  // DIMS with float16 rows runs eight waves: waves 0-3 compute, waves 4-7
+  // ("producers") only move key blocks into the tiles.  A wave that issues a block
+  // transfer stalls while the vector-memory path drains (about 0.6 us per 64 KiB
+  // block and CU), so the computing waves no longer issue any: they meet the
+  // producers only at the workgroup barriers.  The producers stage a block's K rows
+  // as soon as the score exchange has freed the K tile and its V rows once P.V has
+  // freed the V tile, and publish each block at the barrier that ends the block
+  // before it.  Only the producers' counters see the transfers, so the computing
+  // waves' waits for their own loads (Q, the map row, validity bytes) wait for
+  // nothing else.
   constexpr bool SPLITKV = MODE == kSplitDims && !FP8;
   constexpr int KPD = KEYS ? 4 : 2;   // K operand reads in flight (k-steps)
   // FP8 V rows are multiplied by half their row scale in float16, so that a row
@@ -96,7 +103,9 @@ __global__ __launch_bounds__(256, MODE == kSplitHeads ? 2 : 1) void attn_staged_
   asm volatile("" ::"s"(p.q), "s"(p.B), "s"(p.valid0), "s"(p.valid1_sb), "s"(p.vs1), "s"(p.nbd));
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave index (uniform)
+  // wave index (uniform); SPLITKV: 0-3 within the computing or the producing waves
+  const int w = __builtin_amdgcn_readfirstlane((tid >> 6) & 3);
+  const bool producer = SPLITKV && tid >= 256;
   const int g = lane >> 4;       // lane group: operand k-slots 8g..8g+7
   const int c16 = lane & 15;     // MFMA row/column of this lane
   const uint32_t lane16 = 16u * lane;   // this lane's byte offset in a transferred row
@@ -142,6 +151,7 @@ __global__ __launch_bounds__(256, MODE == kSplitHeads ? 2 : 1) void attn_staged_
   __shared__ floatx4 xs[MODE == kSplitDims ? 4 * 2 * 64 : 1];   // partial S^T exchange
   __shared__ uint16_t blist[kListCap];
   __shared__ int cnt[4];
+  __shared__ int nd_s;   // SPLITKV: the list length, for the producers
   __shared__ __attribute__((aligned(16))) int idx_s[INDEXED ? kIdxCap : 4];
   __shared__ uint32_t vmask[kMaskRing];   // bit r: row r of the entry's block is visible
   __shared__ uint32_t dmask[kTable];      // the same for dense blocks 0..kTable-1
@@ -168,6 +178,57 @@ __global__ __launch_bounds__(256, MODE == kSplitHeads ? 2 : 1) void attn_staged_
       f(std::integral_constant<int, 2>{});
       f(std::integral_constant<int, 3>{});
     }
+  };
+
+  // Float16 rows of key block j (uniform) for this wave's transfers: the region's K
+  // and V rows of this sequence, the row stride, the wave's eight rows 8w..8w+7 (a
+  // gathered entry reads its row from the list; unused entries read row 0) and the
+  // visibility mask `vm`.  issue_row starts the transfer of one of them (K or V):
+  // rows whose bit in `vm` is clear arrive as zeros and are not read from memory.
+  struct RowSet {
+    const char *kb, *vb;
+    int64_t sr;
+    int rows[8];
+    uint32_t vm;
+  };
+  auto row_set = [&](int j, uint32_t vm) __attribute__((always_inline)) -> RowSet {
+    RowSet rs;
+    rs.vm = vm;
+    int base;
+    if (j < p.nb0) {
+      rs.kb = p.k0 + b * p.kv0_sb;
+      rs.vb = p.v0 + b * p.kv0_sb;
+      rs.sr = p.kv0_sr;
+      base = j * kRowsPerBlock;
+    } else {
+      rs.kb = p.k1 + b * p.kv1_sb;
+      rs.vb = p.v1 + b * p.kv1_sb;
+      rs.sr = p.kv1_sr;
+      base = (j - p.nb0) * kRowsPerBlock;
+    }
+    if (INDEXED && j >= p.nb0) {
+      // the wave's eight list entries in two 16-byte LDS reads (entries past r1_k
+      // hold -1)
+      const int4 *src = (const int4 *)&idx_s[base + 8 * w];
+      const int4 c0 = src[0], c1 = src[1];
+      const int cs[8] = {c0.x, c0.y, c0.z, c0.w, c1.x, c1.y, c1.z, c1.w};
+#pragma unroll
+      for (int q = 0; q < 8; ++q) {
+        const int c = __builtin_amdgcn_readfirstlane(cs[q]);
+        rs.rows[q] = (c >= 0 && c < p.n1) ? c : 0;
+      }
+    } else {
+#pragma unroll
+      for (int q = 0; q < 8; ++q) rs.rows[q] = base + 8 * w + q;
+    }
+    return rs;
+  };
+  auto issue_row = [&](const RowSet &rs, int q, uint32_t tile, int stride, auto is_v)
+      __attribute__((always_inline)) {
+    const int rr = 8 * w + q;
+    const bool shown = (rs.vm >> rr) & 1u;
+    const char *src = decltype(is_v)::value ? rs.vb : rs.kb;
+    dma16(shown ? src + rs.rows[q] * rs.sr : kZeroRow, lane16, tile + rr * stride);
   };
 
   // Start the transfers of key block j (uniform) into buffer pair `buf`: wave w
@@ -239,29 +300,11 @@ __global__ __launch_bounds__(256, MODE == kSplitHeads ? 2 : 1) void attn_staged_
                    lds_addr(stile(buf)) + 64u * w);
       }
     } else {
-      int rows[8];
-      if (INDEXED && j >= p.nb0) {
-        // the wave's eight list entries in two 16-byte LDS reads (entries past r1_k
-        // hold -1); unused entries read row 0, they are masked
-        const int4 *src = (const int4 *)&idx_s[base + 8 * w];
-        const int4 c0 = src[0], c1 = src[1];
-        const int cs[8] = {c0.x, c0.y, c0.z, c0.w, c1.x, c1.y, c1.z, c1.w};
-#pragma unroll
-        for (int q = 0; q < 8; ++q) {
-          const int c = __builtin_amdgcn_readfirstlane(cs[q]);
-          rows[q] = (c >= 0 && c < p.n1) ? c : 0;
-        }
-      } else {
-#pragma unroll
-        for (int q = 0; q < 8; ++q) rows[q] = base + 8 * w + q;
-      }
+      const RowSet rs = row_set(j, vm);
 #pragma unroll
       for (int q = 0; q < 8; ++q) {
-        const int rr = 8 * w + q;
-        const int row = rows[q];
-        const bool shown = (vm >> rr) & 1u;
-        if (PART != 2) dma16(shown ? kb + row * sr : kZeroRow, lane16, kbase + rr * kKRow);
-        if (PART != 1) dma16(shown ? vb + row * sr : kZeroRow, lane16, vbase + rr * kVRow);
+        if (PART != 2) issue_row(rs, q, kbase, kKRow, std::false_type{});
+        if (PART != 1) issue_row(rs, q, vbase, kVRow, std::true_type{});
       }
     }
   };
@@ -459,10 +502,141 @@ __global__ __launch_bounds__(256, MODE == kSplitHeads ? 2 : 1) void attn_staged_
   if constexpr (KEYS) {
     const int sraw = buf_load_u8(make_rsrc(blkrow, blkrow ? (uint32_t)p.nbd : 0u), (uint32_t)tid);
     s_first = tid < p.nbd ? (blkrow ? sraw : kPartial) : 0;
-  } else {
+  } else if (!SPLITKV || producer) {
     for_bufs([&](auto E) {
       if (spec(E) >= 0) stage_rows(spec(E), 0xffffffffu, E, BothParts{});
     });
+  }
+
+  // This workgroup's part of the list, entries [e0, e1), once the list has been
+  // built (ndense dense entries).
+  int ndense = 0, e0 = 0, e1 = 0;
+  auto part_bounds = [&](int nd) __attribute__((always_inline)) {
+    const int nlist = nd + (INDEXED ? p.nb1 : 0);
+    // (nlist <= kListCap + kIdxCap / 32 and split < kMaxSplits: 32-bit products)
+    e0 = (int)((uint32_t)(nlist * split) / (uint32_t)nsplit);
+    e1 = (int)((uint32_t)(nlist * (split + 1)) / (uint32_t)nsplit);
+  };
+  // List entry i: key block j (dense blocks of both regions, then the gathered
+  // blocks of an indexed region) and its map status.
+  auto entry_at = [&](int i, int &j, int &status) {
+    if (i < ndense) {
+      const int e = blist[i];
+      j = e & 0x3fff;
+      status = e >> 14;
+    } else {
+      j = p.nb0 + (i - ndense);
+      status = kPartial;
+    }
+  };
+
+  // Start the transfers of list entry i (< nlist) into buffer pair `buf`, with the
+  // entry's mask (MASKED) or unmasked.
+  auto stage = [&](int i, auto buf, auto masked, auto part) __attribute__((always_inline)) {
+    constexpr bool MASKED = decltype(masked)::value;
+    int j, status;
+    entry_at(i, j, status);
+    const uint32_t vm = MASKED ? __builtin_amdgcn_readfirstlane(vmask[i & (kMaskRing - 1)]) : 0xffffffffu;
+    stage_rows(__builtin_amdgcn_readfirstlane(j), vm, buf, part);
+  };
+
+  // Clear the V rows of entry i that its mask hides, among this wave's own rows
+  // 8w..8w+7 (its own completed transfers wrote them).
+  auto clear_masked = [&](int i, auto buf) __attribute__((always_inline)) {
+    if (i >= e1) return;
+    const uint32_t vmi = vmask[i & (kMaskRing - 1)];
+    char *vt = vtile(buf);
+    if constexpr (FP8) {
+      // this wave's rows are the rows of its pairs 4w..4w+3: slot q < 4 the first
+      // row of pair 4w + q, slot q >= 4 the second row of pair 4w + q - 4
+#pragma unroll
+      for (int q = 0; q < 8; ++q) {
+        const int pr = 4 * w + (q & 3);
+        const int rr = q < 4 ? pr : f8_second_row(pr);
+        if (!((vmi >> rr) & 1u)) {
+          // the row's 512 bytes, and its V scale
+          if (lane < 32) *(uint4 *)(vt + f8_row_off(rr) + 16 * lane) = make_uint4(0u, 0u, 0u, 0u);
+          if (lane == 0) stile(buf)[16 * w + 8 + q] = 0.f;
+        }
+      }
+    } else {
+      uint32_t hidden = (~vmi >> (8 * w)) & 0xffu;
+      while (hidden) {
+        const int rr = 8 * w + __ffs(hidden) - 1;
+        hidden &= hidden - 1;
+        *(uint4 *)(vt + rr * kVRow + 16 * lane) = make_uint4(0u, 0u, 0u, 0u);
+      }
+    }
+  };
+
+  // The guessed first entries against the list: a wrong guess is staged again,
+  // unmasked (its hidden rows are cleared once it has landed).  Returns whether any
+  // entry was staged again.
+  auto check_guesses = [&]() __attribute__((always_inline)) -> bool {
+    bool hit[NBUF], all = true;
+    for_bufs([&](auto E) {
+      int j = -1, st;
+      if (e1 > e0 + E) entry_at(e0 + E, j, st);
+      j = __builtin_amdgcn_readfirstlane(j);
+      hit[E] = e1 <= e0 + E || j == spec(E);
+      all = all && hit[E];
+    });
+    if (!all) {
+      wait_vmcnt<0>();   // the guessed transfers land before their buffers are refilled
+      for_bufs([&](auto E) {
+        if (!hit[E]) stage(e0 + E, E, Unmasked{}, BothParts{});
+      });
+    }
+    return !all;
+  };
+
+  // SPLITKV producers: their whole program.  It meets the computing waves' barriers
+  // in the same order: the block list's (two per 256 map entries and a final one),
+  // the first-block mask table's, the masks', entry e0's, then per entry i the
+  // score exchange, a mask refill when entry i + NBUF starts a chunk, the end of the
+  // entry while another follows, and the epilogue's.  It branches off before the
+  // computing waves load anything through the compiler, so that no wait of theirs
+  // (nor one for registers their loads would write) lands in this path.
+  if constexpr (SPLITKV) {
+    if (producer) {
+      auto produce = [&](int i, auto buf) __attribute__((always_inline)) {
+        constexpr int B = decltype(buf)::value;
+        const int nx = i + NBUF;
+        lds_barrier();   // score exchange of entry i: K tile B is free
+        if (nx < e1 && (nx & (kMaskChunk - 1)) == 0) lds_barrier();   // masks of entries nx..
+        if (nx < e1) stage(nx, buf, Masked{}, KPart{});
+        if (i + 1 < e1) {
+          // entry i + 1 landed: only the K rows of entry nx may be in flight
+          if (nx < e1) wait_vmcnt<kStageOps / 2>();
+          else wait_vmcnt<0>();
+          // (entry e0 + 1 was staged unmasked, as guessed)
+          if (i == e0) clear_masked(i + 1, std::integral_constant<int, (B + 1) % NBUF>{});
+          lds_barrier();   // end of entry i: publishes entry i + 1, V tile B is free
+          if (nx < e1) stage(nx, buf, Masked{}, VPart{});
+        }
+      };
+      const int nbar = 2 * ((p.nbd + 255) / 256) + 1;
+      for (int k = 0; k < nbar; ++k) lds_barrier();   // the block list
+      lds_barrier();                                  // the first-block mask table
+      ndense = nd_s;
+      part_bounds(ndense);
+      const bool redo = check_guesses();
+      lds_barrier();   // masks visible
+      // entry e0 landed: only entry e0 + 1's guessed transfers may be in flight
+      // (after a redo the order is not known: wait for everything)
+      if (!redo && spec(1) >= 0) wait_vmcnt<kStageOps>();
+      else wait_vmcnt<0>();
+      clear_masked(e0, std::integral_constant<int, 0>{});
+      lds_barrier();   // entry e0 ready
+      for (int i = e0; i < e1; i += NBUF) {
+        for_bufs([&](auto E) {
+          if (i + E < e1) produce(i + E, E);
+        });
+      }
+      wait_vmcnt<0>();   // nothing in flight when the workgroup ends
+      lds_barrier();     // the epilogue's barrier
+      return;
+    }
   }
 
   // validity arrays of this sequence (size 0 when absent: every load out of range)
@@ -558,31 +732,16 @@ __global__ __launch_bounds__(256, MODE == kSplitHeads ? 2 : 1) void attn_staged_
       for (int e = tid; e < padded; e += 256) idx_s[e] = e < p.r1_k ? src[e] : -1;
     }
   }
-  const int ndense = build_block_list<256>(blkrow, p.nbd, blist, cnt, s_first);   // ends with a barrier
-  const int nlist = ndense + (INDEXED ? p.nb1 : 0);
-  // this workgroup's part of the list: entries [e0, e1)
-  // (nlist <= kListCap + kIdxCap / 32 and split < kMaxSplits: 32-bit products)
-  const int e0 = (int)((uint32_t)(nlist * split) / (uint32_t)nsplit);
-  const int e1 = (int)((uint32_t)(nlist * (split + 1)) / (uint32_t)nsplit);
+  ndense = build_block_list<256>(blkrow, p.nbd, blist, cnt, s_first);   // ends with a barrier
   {
     const bool vis = tok && (toff0 == kOutOfRange || tv0 != 0) && (toff1 == kOutOfRange || tv1 != 0);
     const uint64_t bal = __ballot(vis);
     if ((lane & 31) == 0) dmask[tj] = (uint32_t)(bal >> (lane & 32));
   }
+  if (SPLITKV && tid == 0) nd_s = ndense;
   lds_barrier();
+  part_bounds(ndense);
 
-  // List entry i: key block j (dense blocks of both regions, then the gathered
-  // blocks of an indexed region) and its map status.
-  auto entry_at = [&](int i, int &j, int &status) {
-    if (i < ndense) {
-      const int e = blist[i];
-      j = e & 0x3fff;
-      status = e >> 14;
-    } else {
-      j = p.nb0 + (i - ndense);
-      status = kPartial;
-    }
-  };
   // Visibility masks of list entries [c0, c0 + n) into the ring, K rounds of 8
   // entries per batch of loads: half-wave (w, lane >> 5) takes entry 8k + 2w + (lane >> 5)
   // of a round, lane & 31 its row.  Dense blocks below kTable come from the table.
@@ -651,44 +810,7 @@ __global__ __launch_bounds__(256, MODE == kSplitHeads ? 2 : 1) void attn_staged_
     else build_masks(e0, n, std::integral_constant<int, 8>{});
   };
 
-  // Start the transfers of list entry i (< nlist) into buffer pair `buf`, with the
-  // entry's mask (MASKED) or unmasked.
-  auto stage = [&](int i, auto buf, auto masked, auto part) __attribute__((always_inline)) {
-    constexpr bool MASKED = decltype(masked)::value;
-    int j, status;
-    entry_at(i, j, status);
-    const uint32_t vm = MASKED ? __builtin_amdgcn_readfirstlane(vmask[i & (kMaskRing - 1)]) : 0xffffffffu;
-    stage_rows(__builtin_amdgcn_readfirstlane(j), vm, buf, part);
-  };
 
-  // Clear the V rows of entry i that its mask hides, among this wave's own rows
-  // 8w..8w+7 (its own completed transfers wrote them).
-  auto clear_masked = [&](int i, auto buf) __attribute__((always_inline)) {
-    if (i >= e1) return;
-    const uint32_t vmi = vmask[i & (kMaskRing - 1)];
-    char *vt = vtile(buf);
-    if constexpr (FP8) {
-      // this wave's rows are the rows of its pairs 4w..4w+3: slot q < 4 the first
-      // row of pair 4w + q, slot q >= 4 the second row of pair 4w + q - 4
-#pragma unroll
-      for (int q = 0; q < 8; ++q) {
-        const int pr = 4 * w + (q & 3);
-        const int rr = q < 4 ? pr : f8_second_row(pr);
-        if (!((vmi >> rr) & 1u)) {
-          // the row's 512 bytes, and its V scale
-          if (lane < 32) *(uint4 *)(vt + f8_row_off(rr) + 16 * lane) = make_uint4(0u, 0u, 0u, 0u);
-          if (lane == 0) stile(buf)[16 * w + 8 + q] = 0.f;
-        }
-      }
-    } else {
-      uint32_t hidden = (~vmi >> (8 * w)) & 0xffu;
-      while (hidden) {
-        const int rr = 8 * w + __ffs(hidden) - 1;
-        hidden &= hidden - 1;
-        *(uint4 *)(vt + rr * kVRow + 16 * lane) = make_uint4(0u, 0u, 0u, 0u);
-      }
-    }
-  };
 
   floatx4 o[NDT];
 #pragma unroll
@@ -1032,27 +1154,22 @@ __global__ __launch_bounds__(256, MODE == kSplitHeads ? 2 : 1) void attn_staged_
   //   block i (buffer B = i mod NBUF): consume from B; barrier (B free); stage
   //             i+NBUF -> B masked; wait for this wave's transfers of i+1; barrier
   //             (publishes i+1)
-  {
-    bool hit[NBUF], all = true;
-    for_bufs([&](auto E) {
-      int j = -1, st;
-      if (e1 > e0 + E) entry_at(e0 + E, j, st);
-      j = __builtin_amdgcn_readfirstlane(j);
-      hit[E] = e1 <= e0 + E || j == spec(E);
-      all = all && hit[E];
-    });
-    if (!all) {
-      wait_vmcnt<0>();   // the guessed transfers land before their buffers are refilled
-      for_bufs([&](auto E) {
-        if (!hit[E]) stage(e0 + E, E, Unmasked{}, BothParts{});
-      });
-    }
+  // SPLITKV: the producers stage; the computing waves only meet them at barriers,
+  //   the score exchange of block i (after which its K tile takes entry i + 2) and
+  //   the end of block i (which publishes entry i + 1, and after which block i's V
+  //   tile takes entry i + 2).  Block e0 is published as soon as it has landed.
+  if constexpr (SPLITKV) {
+    build_masks_first(kMaskChunk);
+    lds_barrier();   // masks visible
+    lds_barrier();   // entry e0 ready (the producers publish it)
+  } else {
+    check_guesses();
+    build_masks_first(kMaskChunk);
+    wait_vmcnt<0>();
+    lds_barrier();   // masks visible
+    for_bufs([&](auto E) { clear_masked(e0 + E, E); });
+    lds_barrier();   // blocks 0 and 1 ready
   }
-  build_masks_first(kMaskChunk);
-  wait_vmcnt<0>();
-  lds_barrier();   // masks visible
-  for_bufs([&](auto E) { clear_masked(e0 + E, E); });
-  lds_barrier();   // blocks 0 and 1 ready
 
   auto iteration = [&](int i, auto buf) __attribute__((always_inline)) {
     constexpr int B = decltype(buf)::value;
@@ -1113,15 +1230,13 @@ __global__ __launch_bounds__(256, MODE == kSplitHeads ? 2 : 1) void attn_staged_
     }
     const int nx = i + NBUF;   // the entry buffer B takes next
     if constexpr (SPLITKV) {
-      // the exchange barrier ended every wave's K reads: the K tile takes entry nx
-      if (nx < e1) {
-        if ((nx & (kMaskChunk - 1)) == 0) {
-          // next chunk of masks (entries i and i + 1 sit in the other half of the ring)
-          const int n = e1 - nx;
-          build_masks(nx, n < kMaskChunk ? n : kMaskChunk, std::integral_constant<int, 1>{});
-          lds_barrier();
-        }
-        stage(nx, buf, Masked{}, KPart{});
+      // the exchange barrier ended every wave's K reads: the producers stage entry
+      // nx into the K tile, after the next chunk of masks when nx starts one
+      // (entries i and i + 1 sit in the other half of the ring)
+      if (nx < e1 && (nx & (kMaskChunk - 1)) == 0) {
+        const int n = e1 - nx;
+        build_masks(nx, n < kMaskChunk ? n : kMaskChunk, std::integral_constant<int, 1>{});
+        lds_barrier();
       }
     }
     // ---- online softmax: this lane holds rows slot_row(g, 0..7) of head h
@@ -1231,19 +1346,16 @@ __global__ __launch_bounds__(256, MODE == kSplitHeads ? 2 : 1) void attn_staged_
       }
     }
 
+    if constexpr (SPLITKV) {
+      // every read of buffer B is done; the producers publish entry i + 1
+      if (i + 1 < e1) lds_barrier();
+      return;
+    }
     lds_barrier();   // every wave is done with buffer B
     // HEADS (two workgroups per CU): a wave issuing its block's transfers runs at
     // raised priority, so the other workgroup's MFMA phase yields issue slots to it
     if constexpr (MODE == kSplitHeads) __builtin_amdgcn_s_setprio(1);
-    if constexpr (SPLITKV) {
-      if (nx < e1) {
-        stage(nx, buf, Masked{}, VPart{});
-        // block i+1 landed: only the stage of entry nx may be in flight
-        wait_vmcnt<(NBUF - 1) * kStageOps>();
-      } else {
-        wait_vmcnt<0>();
-      }
-    } else if (nx < e1) {
+    if (nx < e1) {
       if ((nx & (kMaskChunk - 1)) == 0) {
         // next chunk of masks (one batch of loads per 8 entries; drains the transfers)
         const int n = e1 - nx;
@@ -1362,7 +1474,8 @@ static hipError_t launch_staged(const AttnParams &p, hipStream_t s) {
   constexpr int HG = MODE == kSplitHeads ? 64 : 16;
   const int64_t n = (int64_t)p.B * p.T * (p.H / HG) * (MODE == kSplitHeads ? 1 : p.nsplit);
   if (n == 0) return hipSuccess;
-  const dim3 grid((unsigned)n), block(256);
+  // (DIMS on float16 rows: four computing and four producing waves)
+  const dim3 grid((unsigned)n), block(MODE == kSplitDims && !p.fp8 ? 512 : 256);
   auto go = [&](auto parts) {
     constexpr bool P = decltype(parts)::value;
     if (p.fp8) {
@@ -1382,11 +1495,14 @@ static hipError_t launch_staged(const AttnParams &p, hipStream_t s) {
 // Decode: lists that can be long take the KEYS split; short lists (a few blocks:
 // each wave would see one or two units, and the merge of the four partial results
 // would cost more than the overlap gains) take the DIMS split.  The list length
-// is bounded by list_bound, per split part.
-constexpr int64_t kKeysMinEntries = 8;
+// is bounded by list_bound, per split part.  FP8 rows go to KEYS from four blocks
+// on (a KEYS unit is then a whole block, one per wave, and DIMS would convert the
+// codes of every block in all four waves): measured on 64 sequences x 4 blocks,
+// KEYS 11.96 us against DIMS 13.03 us.
+constexpr int64_t kKeysMinEntries = 8, kKeysMinEntriesFp8 = 4;
 static bool use_keys(const AttnParams &p) {
   if (p.decode_split) return p.decode_split == 2;
-  return list_bound(p) / (p.nsplit > 0 ? p.nsplit : 1) >= kKeysMinEntries;
+  return list_bound(p) / (p.nsplit > 0 ? p.nsplit : 1) >= (p.fp8 ? kKeysMinEntriesFp8 : kKeysMinEntries);
 }
 hipError_t launch_attn_decode(const AttnParams &p, hipStream_t s) {
   return use_keys(p) ? launch_staged<kSplitKeys>(p, s) : launch_staged<kSplitDims>(p, s);
