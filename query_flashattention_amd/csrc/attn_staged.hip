@@ -81,8 +81,8 @@ void attn_staged_kernel(const AttnParams p) {
   // block and CU), so the computing waves no longer issue any: they meet the
   // producers only at the workgroup barriers.  The producers stage a block's K rows
   // as soon as the score exchange has freed the K tile and its V rows once P.V has
-  // freed the V tile, and publish each block at the barrier that ends the block
-  // before it.  Only the producers' counters see the transfers, so the computing
+  // freed the V tile; they publish its K rows at the barrier that ends the block
+  // before it and its V rows, which only P.V reads, at its own score exchange.  Only the producers' counters see the transfers, so the computing
   // waves' waits for their own loads (Q, the map row, validity bytes) wait for
   // nothing else.
   constexpr bool SPLITKV = MODE == kSplitDims && !FP8;
@@ -104,8 +104,11 @@ void attn_staged_kernel(const AttnParams p) {
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   // wave index (uniform); SPLITKV: 0-3 within the computing or the producing waves
-  const int w = __builtin_amdgcn_readfirstlane((tid >> 6) & 3);
   const bool producer = SPLITKV && tid >= 256;
+  const int w = __builtin_amdgcn_readfirstlane((tid >> 6) & 3);
+  // float16 rows a wave transfers per key block, K and V each (also the transfers
+  // it issues per part)
+  constexpr int RPW = 8;
   const int g = lane >> 4;       // lane group: operand k-slots 8g..8g+7
   const int c16 = lane & 15;     // MFMA row/column of this lane
   const uint32_t lane16 = 16u * lane;   // this lane's byte offset in a transferred row
@@ -181,14 +184,14 @@ void attn_staged_kernel(const AttnParams p) {
   };
 
   // Float16 rows of key block j (uniform) for this wave's transfers: the region's K
-  // and V rows of this sequence, the row stride, the wave's eight rows 8w..8w+7 (a
+  // and V rows of this sequence, the row stride, the wave's RPW rows RPW w .. (a
   // gathered entry reads its row from the list; unused entries read row 0) and the
   // visibility mask `vm`.  issue_row starts the transfer of one of them (K or V):
   // rows whose bit in `vm` is clear arrive as zeros and are not read from memory.
   struct RowSet {
     const char *kb, *vb;
     int64_t sr;
-    int rows[8];
+    int rows[RPW];
     uint32_t vm;
   };
   auto row_set = [&](int j, uint32_t vm) __attribute__((always_inline)) -> RowSet {
@@ -207,33 +210,39 @@ void attn_staged_kernel(const AttnParams p) {
       base = (j - p.nb0) * kRowsPerBlock;
     }
     if (INDEXED && j >= p.nb0) {
-      // the wave's eight list entries in two 16-byte LDS reads (entries past r1_k
-      // hold -1)
-      const int4 *src = (const int4 *)&idx_s[base + 8 * w];
-      const int4 c0 = src[0], c1 = src[1];
-      const int cs[8] = {c0.x, c0.y, c0.z, c0.w, c1.x, c1.y, c1.z, c1.w};
+      // the wave's list entries in 16-byte LDS reads (entries past r1_k hold -1)
+      const int4 *src = (const int4 *)&idx_s[base + RPW * w];
+      int cs[RPW];
 #pragma unroll
-      for (int q = 0; q < 8; ++q) {
+      for (int q4 = 0; q4 < RPW / 4; ++q4) {
+        const int4 c4 = src[q4];
+        cs[4 * q4] = c4.x;
+        cs[4 * q4 + 1] = c4.y;
+        cs[4 * q4 + 2] = c4.z;
+        cs[4 * q4 + 3] = c4.w;
+      }
+#pragma unroll
+      for (int q = 0; q < RPW; ++q) {
         const int c = __builtin_amdgcn_readfirstlane(cs[q]);
         rs.rows[q] = (c >= 0 && c < p.n1) ? c : 0;
       }
     } else {
 #pragma unroll
-      for (int q = 0; q < 8; ++q) rs.rows[q] = base + 8 * w + q;
+      for (int q = 0; q < RPW; ++q) rs.rows[q] = base + RPW * w + q;
     }
     return rs;
   };
   auto issue_row = [&](const RowSet &rs, int q, uint32_t tile, int stride, auto is_v)
       __attribute__((always_inline)) {
-    const int rr = 8 * w + q;
+    const int rr = RPW * w + q;
     const bool shown = (rs.vm >> rr) & 1u;
     const char *src = decltype(is_v)::value ? rs.vb : rs.kb;
     dma16(shown ? src + rs.rows[q] * rs.sr : kZeroRow, lane16, tile + rr * stride);
   };
 
   // Start the transfers of key block j (uniform) into buffer pair `buf`: wave w
-  // moves rows 8w..8w+7 of K and of V, one 1 KiB row per instruction, kStageOps
-  // instructions in all.  Rows whose bit in `vm` is clear arrive as zeros (and are
+  // moves rows RPW w .. RPW w + RPW - 1 of K and of V (FP8: pairs 4w..4w+3), one
+  // 1 KiB row per instruction.  Rows whose bit in `vm` is clear arrive as zeros (and are
   // not read from memory); with vm = all ones every row is transferred (gathered
   // entries that are unused read row 0) and hidden rows are cleared afterwards.
   // `part` (float16 rows): 0 = K and V rows, 1 = K rows only, 2 = V rows only.
@@ -302,7 +311,7 @@ void attn_staged_kernel(const AttnParams p) {
     } else {
       const RowSet rs = row_set(j, vm);
 #pragma unroll
-      for (int q = 0; q < 8; ++q) {
+      for (int q = 0; q < RPW; ++q) {
         if (PART != 2) issue_row(rs, q, kbase, kKRow, std::false_type{});
         if (PART != 1) issue_row(rs, q, vbase, kVRow, std::true_type{});
       }
@@ -502,9 +511,18 @@ void attn_staged_kernel(const AttnParams p) {
   if constexpr (KEYS) {
     const int sraw = buf_load_u8(make_rsrc(blkrow, blkrow ? (uint32_t)p.nbd : 0u), (uint32_t)tid);
     s_first = tid < p.nbd ? (blkrow ? sraw : kPartial) : 0;
-  } else if (!SPLITKV || producer) {
+  }
+  if (!KEYS && (!SPLITKV || producer)) {
     for_bufs([&](auto E) {
-      if (spec(E) >= 0) stage_rows(spec(E), 0xffffffffu, E, BothParts{});
+      if (spec(E) >= 0) {
+        if constexpr (SPLITKV) {
+          // (K rows first: an entry's K rows are published before its V rows)
+          stage_rows(spec(E), 0xffffffffu, E, KPart{});
+          stage_rows(spec(E), 0xffffffffu, E, VPart{});
+        } else {
+          stage_rows(spec(E), 0xffffffffu, E, BothParts{});
+        }
+      }
     });
   }
 
@@ -541,7 +559,7 @@ void attn_staged_kernel(const AttnParams p) {
   };
 
   // Clear the V rows of entry i that its mask hides, among this wave's own rows
-  // 8w..8w+7 (its own completed transfers wrote them).
+  // (its own completed transfers wrote them).
   auto clear_masked = [&](int i, auto buf) __attribute__((always_inline)) {
     if (i >= e1) return;
     const uint32_t vmi = vmask[i & (kMaskRing - 1)];
@@ -560,9 +578,9 @@ void attn_staged_kernel(const AttnParams p) {
         }
       }
     } else {
-      uint32_t hidden = (~vmi >> (8 * w)) & 0xffu;
+      uint32_t hidden = (~vmi >> (RPW * w)) & ((1u << RPW) - 1u);
       while (hidden) {
-        const int rr = 8 * w + __ffs(hidden) - 1;
+        const int rr = RPW * w + __ffs(hidden) - 1;
         hidden &= hidden - 1;
         *(uint4 *)(vt + rr * kVRow + 16 * lane) = make_uint4(0u, 0u, 0u, 0u);
       }
@@ -599,19 +617,27 @@ void attn_staged_kernel(const AttnParams p) {
   // (nor one for registers their loads would write) lands in this path.
   if constexpr (SPLITKV) {
     if (producer) {
+      // An entry's K rows are published by the barrier that ends the entry before
+      // it, its V rows (needed only from P.V on) by its own score exchange.  In
+      // issue order: K rows of entry nx after the exchange of entry i, its V rows
+      // after the end of entry i.
       auto produce = [&](int i, auto buf) __attribute__((always_inline)) {
-        constexpr int B = decltype(buf)::value;
         const int nx = i + NBUF;
-        lds_barrier();   // score exchange of entry i: K tile B is free
+        // entry i's V rows landed: only entry i + 1's transfers may be in flight;
+        // the first two entries were staged unmasked, as guessed: clear their
+        // hidden V rows
+        if (i + 1 < e1) wait_vmcnt<2 * RPW>();
+        else wait_vmcnt<0>();
+        if (i <= e0 + 1) clear_masked(i, buf);
+        lds_barrier();   // score exchange of entry i: its V rows ready, K tile B free
         if (nx < e1 && (nx & (kMaskChunk - 1)) == 0) lds_barrier();   // masks of entries nx..
         if (nx < e1) stage(nx, buf, Masked{}, KPart{});
         if (i + 1 < e1) {
-          // entry i + 1 landed: only the K rows of entry nx may be in flight
-          if (nx < e1) wait_vmcnt<kStageOps / 2>();
-          else wait_vmcnt<0>();
-          // (entry e0 + 1 was staged unmasked, as guessed)
-          if (i == e0) clear_masked(i + 1, std::integral_constant<int, (B + 1) % NBUF>{});
-          lds_barrier();   // end of entry i: publishes entry i + 1, V tile B is free
+          // entry i + 1's K rows landed: only its V rows and the K rows of entry nx
+          // may be in flight
+          if (nx < e1) wait_vmcnt<2 * RPW>();
+          else wait_vmcnt<RPW>();
+          lds_barrier();   // end of entry i: entry i + 1's K rows ready, V tile B free
           if (nx < e1) stage(nx, buf, Masked{}, VPart{});
         }
       };
@@ -622,12 +648,13 @@ void attn_staged_kernel(const AttnParams p) {
       part_bounds(ndense);
       const bool redo = check_guesses();
       lds_barrier();   // masks visible
-      // entry e0 landed: only entry e0 + 1's guessed transfers may be in flight
-      // (after a redo the order is not known: wait for everything)
-      if (!redo && spec(1) >= 0) wait_vmcnt<kStageOps>();
-      else wait_vmcnt<0>();
-      clear_masked(e0, std::integral_constant<int, 0>{});
-      lds_barrier();   // entry e0 ready
+      // entry e0's K rows landed: only its V rows and entry e0 + 1's guessed
+      // transfers may be in flight (after a redo the order is not known: wait for
+      // everything)
+      if (redo) wait_vmcnt<0>();
+      else if (spec(1) >= 0) wait_vmcnt<3 * RPW>();
+      else wait_vmcnt<RPW>();
+      lds_barrier();   // entry e0's K rows ready
       for (int i = e0; i < e1; i += NBUF) {
         for_bufs([&](auto E) {
           if (i + E < e1) produce(i + E, E);
@@ -1155,13 +1182,14 @@ void attn_staged_kernel(const AttnParams p) {
   //             i+NBUF -> B masked; wait for this wave's transfers of i+1; barrier
   //             (publishes i+1)
   // SPLITKV: the producers stage; the computing waves only meet them at barriers,
-  //   the score exchange of block i (after which its K tile takes entry i + 2) and
-  //   the end of block i (which publishes entry i + 1, and after which block i's V
-  //   tile takes entry i + 2).  Block e0 is published as soon as it has landed.
+  //   the score exchange of block i (which publishes its V rows, and after which
+  //   its K tile takes entry i + 2) and the end of block i (which publishes entry
+  //   i + 1's K rows, and after which block i's V tile takes entry i + 2).  Block
+  //   e0's K rows are published as soon as they have landed.
   if constexpr (SPLITKV) {
     build_masks_first(kMaskChunk);
     lds_barrier();   // masks visible
-    lds_barrier();   // entry e0 ready (the producers publish it)
+    lds_barrier();   // entry e0's K rows ready (the producers publish them)
   } else {
     check_guesses();
     build_masks_first(kMaskChunk);
@@ -1492,14 +1520,15 @@ static hipError_t launch_staged(const AttnParams &p, hipStream_t s) {
   return hipGetLastError();
 }
 
-// Decode: lists that can be long take the KEYS split; short lists (a few blocks:
-// each wave would see one or two units, and the merge of the four partial results
-// would cost more than the overlap gains) take the DIMS split.  The list length
-// is bounded by list_bound, per split part.  FP8 rows go to KEYS from four blocks
-// on (a KEYS unit is then a whole block, one per wave, and DIMS would convert the
-// codes of every block in all four waves): measured on 64 sequences x 4 blocks,
-// KEYS 11.96 us against DIMS 13.03 us.
-constexpr int64_t kKeysMinEntries = 8, kKeysMinEntriesFp8 = 4;
+// Decode: lists that can be long take the KEYS split; shorter ones take the DIMS
+// split.  The list length is bounded by list_bound, per split part.  Measured per
+// launch (float16 rows): DIMS, with its producer waves, is faster up to 16 blocks
+// (64 sequences x 8 blocks 16.1 us against 19.8 us, x 16 blocks 28.2 against
+// 30.1), even at 32, and slower at 64 blocks (16 sequences: 81.5 against 75.6).
+// FP8 rows go to KEYS from four blocks on (a KEYS unit is then a whole block, one
+// per wave, and DIMS converts the codes of every block in all four waves): 64
+// sequences x 4 blocks, KEYS 11.96 us against DIMS 13.03 us.
+constexpr int64_t kKeysMinEntries = 40, kKeysMinEntriesFp8 = 4;
 static bool use_keys(const AttnParams &p) {
   if (p.decode_split) return p.decode_split == 2;
   return list_bound(p) / (p.nsplit > 0 ? p.nsplit : 1) >= (p.fp8 ? kKeysMinEntriesFp8 : kKeysMinEntries);
