@@ -364,14 +364,14 @@ def measured_peaks(torch):
 def decode_kernel_label(w, parts=1):
     """The decode kernel the library picks for a workload split into `parts` (the
     same rule as its dispatch: the KEYS split when each part's share of the longest
-    possible block list holds at least 40 blocks, 4 for FP8 rows)."""
+    possible block list holds at least 40 blocks, 8 for FP8 rows)."""
     nb0 = -(-w.r0.n_rows // 32)
     if w.window > 0:
         nb0 = min(nb0, w.window // 32 + 2)
     nb1 = 0
     if w.r1 is not None and w.r1.n_rows > 0:
         nb1 = -(-w.r1_index.shape[-1] // 32) if w.r1_index is not None else -(-w.r1.n_rows // 32)
-    least = 4 if w.r0.k_scale is not None else 40
+    least = 8 if w.r0.k_scale is not None else 40
     return 2 if (nb0 + nb1) // max(1, parts) >= least else 1
 
 

@@ -95,8 +95,9 @@ enum {
   /* Decode on the matrix-core kernel only, with a chosen split of the work over a
    * workgroup's four waves (by default the library picks one from the length a
    * token's block list can reach).  DIMS: the waves share each key block and split
-   * the head dimension.  KEYS: the waves take different key rows (16-row halves of
-   * float16 blocks, whole FP8 blocks) and merge their partial results at the end.
+   * the head dimension, while four more waves move the blocks into LDS.  KEYS: the
+   * waves take different key rows (16-row halves of float16 blocks, whole FP8
+   * blocks) and merge their partial results at the end.
    * Setting both is DS4ATTN_E_INVAL; with
    * DS4ATTN_FLAG_GENERIC, or where the matrix-core kernel does not apply, either
    * is DS4ATTN_E_UNSUPPORTED.  Results agree within rounding; they exist for

@@ -60,7 +60,7 @@ enum : int { kSplitHeads = 0, kSplitDims = 1, kSplitKeys = 2 };
 // PARTS (decode only): the launch is a split decode; each workgroup takes one part
 // of its token's block list and leaves a record for the combine pass.
 template <int MODE, bool INDEXED, bool FP8, bool PARTS = false>
-__global__ __launch_bounds__(MODE == kSplitDims && !FP8 ? 512 : 256, MODE == kSplitHeads ? 2 : 1)
+__global__ __launch_bounds__(MODE == kSplitDims ? 512 : 256, MODE == kSplitHeads ? 2 : 1)
 void attn_staged_kernel(const AttnParams p) {
   constexpr bool KEYS = MODE == kSplitKeys;
   // KEYS units: float16 rows go in half-blocks of 16 rows, FP8 rows in whole blocks
@@ -75,17 +75,20 @@ void attn_staged_kernel(const AttnParams p) {
   // computes while the other's transfers are in flight.
   // (FP8 tiles are half the size: DIMS keeps four blocks in flight)
   constexpr int NBUF = MODE == kSplitHeads ? 1 : (FP8 ? 4 : 2);
-  // DIMS with float16 rows runs eight waves: waves 0-3 compute, waves 4-7
-  // ("producers") only move key blocks into the tiles.  A wave that issues a block
+  // DIMS runs eight waves: waves 0-3 compute, waves 4-7 ("producers") only move
+  // key blocks into the tiles.  A wave that issues a block
   // transfer stalls while the vector-memory path drains (about 0.6 us per 64 KiB
   // block and CU), so the computing waves no longer issue any: they meet the
   // producers only at the workgroup barriers.  The producers stage a block's K rows
   // as soon as the score exchange has freed the K tile and its V rows once P.V has
   // freed the V tile; they publish its K rows at the barrier that ends the block
-  // before it and its V rows, which only P.V reads, at its own score exchange.  Only the producers' counters see the transfers, so the computing
+  // before it and its V rows, which only P.V reads, at its own score exchange.
+  // FP8 rows (half the bytes, four buffers) are staged a whole block at a time once
+  // the end of the block four before has freed its buffer, and published whole by
+  // the end of the block before it.  Only the producers' counters see the transfers, so the computing
   // waves' waits for their own loads (Q, the map row, validity bytes) wait for
   // nothing else.
-  constexpr bool SPLITKV = MODE == kSplitDims && !FP8;
+  constexpr bool SPLITKV = MODE == kSplitDims;
   constexpr int KPD = KEYS ? 4 : 2;   // K operand reads in flight (k-steps)
   // FP8 V rows are multiplied by half their row scale in float16, so that a row
   // whose values reach the float16 maximum cannot overflow when its scale is
@@ -515,7 +518,7 @@ void attn_staged_kernel(const AttnParams p) {
   if (!KEYS && (!SPLITKV || producer)) {
     for_bufs([&](auto E) {
       if (spec(E) >= 0) {
-        if constexpr (SPLITKV) {
+        if constexpr (SPLITKV && !FP8) {
           // (K rows first: an entry's K rows are published before its V rows)
           stage_rows(spec(E), 0xffffffffu, E, KPart{});
           stage_rows(spec(E), 0xffffffffu, E, VPart{});
@@ -621,7 +624,7 @@ void attn_staged_kernel(const AttnParams p) {
       // it, its V rows (needed only from P.V on) by its own score exchange.  In
       // issue order: K rows of entry nx after the exchange of entry i, its V rows
       // after the end of entry i.
-      auto produce = [&](int i, auto buf) __attribute__((always_inline)) {
+      auto produce16 = [&](int i, auto buf) __attribute__((always_inline)) {
         const int nx = i + NBUF;
         // entry i's V rows landed: only entry i + 1's transfers may be in flight;
         // the first two entries were staged unmasked, as guessed: clear their
@@ -641,6 +644,31 @@ void attn_staged_kernel(const AttnParams p) {
           if (nx < e1) stage(nx, buf, Masked{}, VPart{});
         }
       };
+      // FP8 rows: entry nx is staged whole (kF8StageOps transfers) after the end of
+      // entry i, and entry i + 1 is published whole by the end of entry i.  Entries
+      // i + 2 and i + 3, where they exist, were staged after entry i + 1 (by the
+      // prologue's guesses or after the ends of entries i - 2 and i - 1); counting
+      // only those keeps the wait safe when a guessed entry past the list is in
+      // flight too.
+      auto produce8 = [&](int i, auto buf) __attribute__((always_inline)) {
+        constexpr int B = decltype(buf)::value;
+        const int nx = i + NBUF;
+        // before the last entry's exchange nothing may remain in flight (a guessed
+        // entry past a short list): the epilogue writes the K tiles after it
+        if (i + 1 >= e1) wait_vmcnt<0>();
+        lds_barrier();   // score exchange of entry i
+        if (nx < e1 && (nx & (kMaskChunk - 1)) == 0) lds_barrier();   // masks of entries nx..
+        if (i + 1 < e1) {
+          const int later = (i + 3 < e1 - 1 ? i + 3 : e1 - 1) - (i + 1);
+          if (later >= 2) wait_vmcnt<2 * kF8StageOps>();
+          else if (later == 1) wait_vmcnt<kF8StageOps>();
+          else wait_vmcnt<0>();
+          // (the first NBUF entries were staged unmasked, as guessed)
+          if (i + 1 < e0 + NBUF) clear_masked(i + 1, std::integral_constant<int, (B + 1) % NBUF>{});
+          lds_barrier();   // end of entry i: entry i + 1 ready, buffer B free
+          if (nx < e1) stage(nx, buf, Masked{}, BothParts{});
+        }
+      };
       const int nbar = 2 * ((p.nbd + 255) / 256) + 1;
       for (int k = 0; k < nbar; ++k) lds_barrier();   // the block list
       lds_barrier();                                  // the first-block mask table
@@ -648,16 +676,32 @@ void attn_staged_kernel(const AttnParams p) {
       part_bounds(ndense);
       const bool redo = check_guesses();
       lds_barrier();   // masks visible
-      // entry e0's K rows landed: only its V rows and entry e0 + 1's guessed
-      // transfers may be in flight (after a redo the order is not known: wait for
-      // everything)
-      if (redo) wait_vmcnt<0>();
-      else if (spec(1) >= 0) wait_vmcnt<3 * RPW>();
-      else wait_vmcnt<RPW>();
-      lds_barrier();   // entry e0's K rows ready
+      if constexpr (FP8) {
+        // entry e0 landed: only the guessed entries after it may be in flight (after
+        // a redo the order is not known, and an empty list goes to the epilogue
+        // next: wait for everything)
+        if (redo || e0 >= e1) wait_vmcnt<0>();
+        else if (spec(3) >= 0) wait_vmcnt<3 * kF8StageOps>();
+        else if (spec(2) >= 0) wait_vmcnt<2 * kF8StageOps>();
+        else if (spec(1) >= 0) wait_vmcnt<kF8StageOps>();
+        else wait_vmcnt<0>();
+        clear_masked(e0, std::integral_constant<int, 0>{});
+        lds_barrier();   // entry e0 ready
+      } else {
+        // entry e0's K rows landed: only its V rows and entry e0 + 1's guessed
+        // transfers may be in flight (after a redo the order is not known: wait for
+        // everything)
+        if (redo) wait_vmcnt<0>();
+        else if (spec(1) >= 0) wait_vmcnt<3 * RPW>();
+        else wait_vmcnt<RPW>();
+        lds_barrier();   // entry e0's K rows ready
+      }
       for (int i = e0; i < e1; i += NBUF) {
         for_bufs([&](auto E) {
-          if (i + E < e1) produce(i + E, E);
+          if (i + E < e1) {
+            if constexpr (FP8) produce8(i + E, E);
+            else produce16(i + E, E);
+          }
         });
       }
       wait_vmcnt<0>();   // nothing in flight when the workgroup ends
@@ -1416,14 +1460,17 @@ void attn_staged_kernel(const AttnParams p) {
     // DIMS: the workgroup's 16 x 512 float32 outputs (or, for a split part, its
     // unnormalised partial record) leave through the free tile buffers, so that
     // every store writes 1 KiB of one row instead of 16 rows x 64 bytes
+    // (the K tiles: every wave's K reads ended at the last score exchange, while
+    // the V tile of the last entry may still be read by slower waves, since that
+    // entry ends without a barrier)
     typedef __attribute__((address_space(3))) char lds_w;
     lds_w *kts = (lds_w *)(__attribute__((address_space(3))) void *)kt0;
-    lds_w *vts = (lds_w *)(__attribute__((address_space(3))) void *)vt0;
+    lds_w *kts1 = (lds_w *)(__attribute__((address_space(3))) void *)kt1;
     constexpr int kORow = 2064;                          // 512 float32, padded
     constexpr int RPT = KT / kORow < 16 ? KT / kORow : 16;   // rows per tile buffer
-    static_assert(2 * RPT >= 16 && RPT * kORow <= VT, "the 16 output rows fit the tiles");
+    static_assert(NBUF >= 2 && 2 * RPT >= 16 && RPT * kORow <= KT, "the 16 output rows fit the K tiles");
     auto slot = [&](int sl) __attribute__((always_inline)) -> lds_w * {
-      return (sl < RPT ? kts : vts) + (sl % RPT) * kORow;
+      return (sl < RPT ? kts : kts1) + (sl % RPT) * kORow;
     };
     constexpr bool part = PARTS;
     const float sc = (part ? 1.f : inv) * kOut;
@@ -1502,8 +1549,8 @@ static hipError_t launch_staged(const AttnParams &p, hipStream_t s) {
   constexpr int HG = MODE == kSplitHeads ? 64 : 16;
   const int64_t n = (int64_t)p.B * p.T * (p.H / HG) * (MODE == kSplitHeads ? 1 : p.nsplit);
   if (n == 0) return hipSuccess;
-  // (DIMS on float16 rows: four computing and four producing waves)
-  const dim3 grid((unsigned)n), block(MODE == kSplitDims && !p.fp8 ? 512 : 256);
+  // (DIMS: four computing and four producing waves)
+  const dim3 grid((unsigned)n), block(MODE == kSplitDims ? 512 : 256);
   auto go = [&](auto parts) {
     constexpr bool P = decltype(parts)::value;
     if (p.fp8) {
@@ -1522,13 +1569,11 @@ static hipError_t launch_staged(const AttnParams &p, hipStream_t s) {
 
 // Decode: lists that can be long take the KEYS split; shorter ones take the DIMS
 // split.  The list length is bounded by list_bound, per split part.  Measured per
-// launch (float16 rows): DIMS, with its producer waves, is faster up to 16 blocks
-// (64 sequences x 8 blocks 16.1 us against 19.8 us, x 16 blocks 28.2 against
-// 30.1), even at 32, and slower at 64 blocks (16 sequences: 81.5 against 75.6).
-// FP8 rows go to KEYS from four blocks on (a KEYS unit is then a whole block, one
-// per wave, and DIMS converts the codes of every block in all four waves): 64
-// sequences x 4 blocks, KEYS 11.96 us against DIMS 13.03 us.
-constexpr int64_t kKeysMinEntries = 40, kKeysMinEntriesFp8 = 4;
+// launch, DIMS with its producer waves against KEYS: float16 rows, 64 sequences x
+// 8 blocks 16.1 us against 19.8 us, x 16 blocks 28.2 against 30.1, about even at
+// 32, slower at 64 (16 sequences: 81.5 against 75.6); FP8 rows, 64 sequences x 4
+// blocks 11.1 against 11.8 us, x 12 blocks 23.8 against 20.5.
+constexpr int64_t kKeysMinEntries = 40, kKeysMinEntriesFp8 = 8;
 static bool use_keys(const AttnParams &p) {
   if (p.decode_split) return p.decode_split == 2;
   return list_bound(p) / (p.nsplit > 0 ? p.nsplit : 1) >= (p.fp8 ? kKeysMinEntriesFp8 : kKeysMinEntries);
