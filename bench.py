@@ -218,8 +218,9 @@ class Runner:
 
     def kernel_ms(self, launches):
         """Average duration (ms) of the attention kernel: HIP events on the launch
-        stream around graph replays that hold only attention launches (one per input
-        set, maps and padding prepared beforehand), so the figure is the kernel's
+        stream around graph replays that hold only attention launches (the input sets
+        in turn, at least 20 launches per graph; maps and padding prepared
+        beforehand), so the figure is the kernel's
         own time plus the short gap between back-to-back dispatches.  Also the
         latency of single launches (one event pair each) for context."""
         torch = self.torch
@@ -231,13 +232,18 @@ class Runner:
                 dp.r1.pad_in_place()
             self.da.ds4attn_blockmap(dp.args(), self.bq, self.blks[i] if self.blks[i].numel() else None)
         torch.cuda.synchronize()
+        # (at least 20 launches per graph, the sets in turn: with few large input sets
+        # a graph of one round would time its own launch overhead with every replay)
+        rounds = max(1, 20 // r)
         g = torch.cuda.CUDAGraph()
         with torch.cuda.graph(g):
-            for i in range(r):
-                self.attention_only(i)
+            for _ in range(rounds):
+                for i in range(r):
+                    self.attention_only(i)
         g.replay()
         torch.cuda.synchronize()
-        reps = max(1, launches // r)
+        per_graph = rounds * r
+        reps = max(1, launches // per_graph)
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         self.spin_ms(20.0)
         e0.record()
@@ -245,7 +251,7 @@ class Runner:
             g.replay()
         e1.record()
         torch.cuda.synchronize()
-        mean = e0.elapsed_time(e1) / (reps * r)
+        mean = e0.elapsed_time(e1) / (reps * per_graph)
         evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
                for _ in range(launches)]
         self.spin_ms(20.0)
@@ -255,7 +261,7 @@ class Runner:
             evs[k][1].record()
         torch.cuda.synchronize()
         d = sorted(a.elapsed_time(b) for a, b in evs)
-        return {"mean": mean, "launches": reps * r, "single_launch_median": d[len(d) // 2],
+        return {"mean": mean, "launches": reps * per_graph, "single_launch_median": d[len(d) // 2],
                 "single_launch_p10": d[len(d) // 10], "single_launch_p90": d[(9 * len(d)) // 10]}
 
 
