@@ -149,9 +149,11 @@ class Runner:
             n = ws_bytes(dp.args())
             self.ws.append(torch.empty(n, dtype=torch.uint8, device=device) if n else None)
         # parts per token: the workspace holds one record set per part
-        a = self.sets[0].args()
-        per_part = da.ds4attn_decode_workspace_bytes(a, 2) // 2
-        self.parts = max(1, ws_bytes(a) // per_part) if per_part and self.kind == "decode" else 1
+        self.parts = 1
+        if self.kind == "decode":
+            a = self.sets[0].args()
+            per_part = da.ds4attn_decode_workspace_bytes(a, 2) // 2
+            self.parts = max(1, ws_bytes(a) // per_part) if per_part else 1
         torch.cuda.synchronize()
 
     def step(self, i):
