@@ -83,6 +83,10 @@ CASES = [
     ("masked_tokens", dict(batch=1, tokens=5, heads=16, head_dim=512, n0=40, window=4, q_pos0=0, k_pos0=3)),
     ("index_all_unused", dict(batch=1, tokens=2, heads=16, head_dim=512, n0=10, n1=20, r1_mode="index",
                               r1_k=32, idx_invalid_frac=1.0)),
+    # a window that reaches one or two blocks of a ten-block region: a block guessed
+    # past the end of the list is in flight while the list is consumed
+    ("short_window", dict(batch=2, tokens=3, heads=32, head_dim=512, n0=320, window=20, q_pos0=300,
+                          k_pos0=0)),
     # long lists: more than one chunk of 64 list entries (the visibility masks are
     # rebuilt as the waves go) and more than one chunk of 512 index entries
     ("long_dense", dict(batch=1, tokens=1, heads=16, head_dim=512, n0=4500, valid0_frac=0.9)),
@@ -110,7 +114,9 @@ def test_random(label, kw, split):
                    n1=900, r1_mode="index", r1_k=300, idx_invalid_frac=0.1), 3),
     ("masked_tokens", dict(batch=1, tokens=5, heads=16, head_dim=512, n0=40, window=4, q_pos0=0,
                            k_pos0=3), 2),
-], ids=["valid", "index", "masked_tokens"])
+    ("short_window", dict(batch=2, tokens=3, heads=32, head_dim=512, n0=320, window=70, q_pos0=290,
+                          k_pos0=0), 3),
+], ids=["valid", "index", "masked_tokens", "short_window"])
 def test_split_over_workgroups(label, kw, splits, split):
     w = wl.random_problem(zlib.crc32(label.encode()) % 1000 + 7, **kw)
     want = ref.attention(ref.from_workload(w))

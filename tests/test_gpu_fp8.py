@@ -218,6 +218,11 @@ FP8_DECODE_CASES = [(c[0], c[1]) for c in FP8_CASES] + [
     ("f8_long_dense", dict(batch=1, tokens=1, heads=16, head_dim=512, n0=4500, valid0_frac=0.9)),
     ("f8_long_index", dict(batch=1, tokens=2, heads=16, head_dim=512, n0=128, n1=3000, r1_mode="index",
                            r1_k=1500, idx_invalid_frac=0.05)),
+    # lists shorter than the four blocks DIMS stages before the map arrives: the blocks
+    # guessed past the end of the list are in flight while the list is consumed
+    ("f8_one_block", dict(batch=2, tokens=2, heads=16, head_dim=512, n0=20)),
+    ("f8_short_window", dict(batch=2, tokens=3, heads=32, head_dim=512, n0=320, window=70, q_pos0=290,
+                             k_pos0=0)),
 ]
 
 
