@@ -380,7 +380,11 @@ def decode_kernel_label(w, parts=1):
     if w.r1 is not None and w.r1.n_rows > 0:
         nb1 = -(-w.r1_index.shape[-1] // 32) if w.r1_index is not None else -(-w.r1.n_rows // 32)
     least = 8 if w.r0.k_scale is not None else 40
-    return 2 if (nb0 + nb1) // max(1, parts) >= least else 1
+    if (nb0 + nb1) // max(1, parts) >= least:
+        return 2
+    groups = w.q.shape[0] * w.q.shape[1] * (w.q.shape[2] // 16)
+    wide = parts == 1 and w.r1_index is None and w.q.shape[2] % 32 == 0 and groups > 256
+    return 3 if wide else 1
 
 
 def prefill_cpu_tflops(w, n_tokens, seconds):
@@ -653,7 +657,7 @@ def main():
                      "single_launch_ms_p10": round(k["single_launch_p10"], 5),
                      "single_launch_ms_p90": round(k["single_launch_p90"], 5)}
             if not other.startswith("prefill"):
-                entry["kernel_split"] = {1: "DIMS", 2: "KEYS"}[decode_kernel_label(r.w, r.parts)]
+                entry["kernel_split"] = {1: "DIMS", 2: "KEYS", 3: "WIDE"}[decode_kernel_label(r.w, r.parts)]
                 entry["split_parts"] = r.parts
             if other.startswith("prefill"):
                 entry["tflops_step"] = round(cc["flops"] / (ms * 1e-3) / 1e12, 2)

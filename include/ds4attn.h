@@ -98,12 +98,17 @@ enum {
    * the head dimension, while four more waves move the blocks into LDS.  KEYS: the
    * waves take different key rows (16-row halves of float16 blocks, whole FP8
    * blocks) and merge their partial results at the end.
-   * Setting both is DS4ATTN_E_INVAL; with
-   * DS4ATTN_FLAG_GENERIC, or where the matrix-core kernel does not apply, either
-   * is DS4ATTN_E_UNSUPPORTED.  Results agree within rounding; they exist for
-   * cross-checks and measurement. */
+   * WIDE: DIMS over 32 heads per workgroup (two 16-head tiles per wave sharing
+   * each operand read, half the workgroups), for n_head a multiple of 32 and no
+   * index list; the library picks it when a batch has more groups of 16 heads
+   * than the chip has CUs (256).  Setting more than one is DS4ATTN_E_INVAL; with
+   * DS4ATTN_FLAG_GENERIC, or where the matrix-core kernel (or, for WIDE, its
+   * conditions) does not apply, DS4ATTN_E_UNSUPPORTED, and ds4attn_decode_split
+   * refuses WIDE.  Results agree within rounding; they exist for cross-checks and
+   * measurement. */
   DS4ATTN_FLAG_DECODE_DIMS = 2,
-  DS4ATTN_FLAG_DECODE_KEYS = 4
+  DS4ATTN_FLAG_DECODE_KEYS = 4,
+  DS4ATTN_FLAG_DECODE_WIDE = 8
 };
 
 /* One KV region.  Row r of sequence b starts at  k + b*stride_b + r*stride_row

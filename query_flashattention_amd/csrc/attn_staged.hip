@@ -50,7 +50,8 @@
 
 namespace ds4attn {
 
-enum : int { kSplitHeads = 0, kSplitDims = 1, kSplitKeys = 2 };
+// (kDimsWide: DIMS over 32 heads per workgroup, see DIMS below)
+enum : int { kSplitHeads = 0, kSplitDims = 1, kSplitKeys = 2, kDimsWide = 3 };
 
 // FP8 rows (E4M3 codes, a float32 scale per row): the rows travel to LDS as codes
 // (half the bytes), two rows per transfer, and are converted where the operands
@@ -60,16 +61,22 @@ enum : int { kSplitHeads = 0, kSplitDims = 1, kSplitKeys = 2 };
 // PARTS (decode only): the launch is a split decode; each workgroup takes one part
 // of its token's block list and leaves a record for the combine pass.
 template <int MODE, bool INDEXED, bool FP8, bool PARTS = false>
-__global__ __launch_bounds__(MODE == kSplitDims ? 512 : 256, MODE == kSplitHeads ? 2 : 1)
+__global__ __launch_bounds__(MODE == kSplitDims || MODE == kDimsWide ? 512 : 256, MODE == kSplitHeads ? 2 : 1)
 void attn_staged_kernel(const AttnParams p) {
   constexpr bool KEYS = MODE == kSplitKeys;
+  // DIMS over 16 heads, or over 32 (kDimsWide: each computing wave carries two
+  // 16-head tiles, which share every K and V operand read; half the workgroups
+  // per token, so a large batch pulls each key block into half as many CUs)
+  constexpr bool DIMS = MODE == kSplitDims || MODE == kDimsWide;
+  constexpr int HT = MODE == kDimsWide ? 2 : 1;   // 16-head tiles per computing wave
+  static_assert(!(MODE == kDimsWide && (PARTS || INDEXED)), "wide DIMS: no split parts, no index list");
   // KEYS units: float16 rows go in half-blocks of 16 rows, FP8 rows in whole blocks
   // (the FP8 tiles of a block take the space of a float16 half-block, and the
   // 8-bit transpose read hands out 8 keys per lane)
   constexpr int UPE = FP8 ? 1 : 2;   // KEYS units per list entry
-  constexpr int HG = MODE == kSplitHeads ? 64 : 16;   // heads per workgroup
-  constexpr int NKS = MODE == kSplitDims ? 4 : 16;    // 32-dim k-steps of S per wave
-  constexpr int NDT = MODE == kSplitDims ? 8 : 32;    // 16-dim output tiles per wave
+  constexpr int HG = MODE == kSplitHeads ? 64 : 16 * HT;   // heads per workgroup
+  constexpr int NKS = DIMS ? 4 : 16;    // 32-dim k-steps of S per wave
+  constexpr int NDT = DIMS ? 8 : 32;    // 16-dim output tiles per wave (and head tile)
   // Tile buffers: DIMS double-buffers (block i+1 and i+2 in flight while block i
   // is consumed); HEADS keeps one block so that two workgroups share a CU and one
   // computes while the other's transfers are in flight.
@@ -88,7 +95,7 @@ void attn_staged_kernel(const AttnParams p) {
   // the end of the block before it.  Only the producers' counters see the transfers, so the computing
   // waves' waits for their own loads (Q, the map row, validity bytes) wait for
   // nothing else.
-  constexpr bool SPLITKV = MODE == kSplitDims;
+  constexpr bool SPLITKV = DIMS;
   constexpr int KPD = KEYS ? 4 : 2;   // K operand reads in flight (k-steps)
   // FP8 V rows are multiplied by half their row scale in float16, so that a row
   // whose values reach the float16 maximum cannot overflow when its scale is
@@ -127,7 +134,7 @@ void attn_staged_kernel(const AttnParams p) {
   const int split = (int)(L0 % (uint32_t)nsplit);
   const uint32_t L = L0 / (uint32_t)nsplit;
   // (indices below 2^31: multiply-shift divisions by the run-time H/HG and T)
-  const uint32_t bt = fast_div(L, HG == 16 ? p.div_g16 : p.div_g64);
+  const uint32_t bt = fast_div(L, HG == 16 ? p.div_g16 : (HG == 32 ? p.div_g32 : p.div_g64));
   const int hg = (int)(L - bt * (uint32_t)ngroups);
   const uint32_t bb = fast_div(bt, p.div_t);
   const int t = (int)(bt - bb * (uint32_t)p.T);
@@ -135,7 +142,7 @@ void attn_staged_kernel(const AttnParams p) {
   const int tile = (int)fast_div((uint32_t)t, p.div_bq);   // the token's query tile in the map
   // this lane's head and the first head dim of this wave's operands
   const int h = hg * HG + (MODE == kSplitHeads ? 16 * w : 0) + c16;
-  const int d0 = MODE == kSplitDims ? 128 * w : 0;
+  const int d0 = DIMS ? 128 * w : 0;
 
   // Two tile buffers as separate LDS objects (FP8: codes, plus the blocks' row scales).
   constexpr int KT = KEYS ? 16 : (FP8 ? kF8Tile : kKTile), VT = KEYS ? 16 : (FP8 ? kF8Tile : kVTile);
@@ -154,7 +161,7 @@ void attn_staged_kernel(const AttnParams p) {
   // scales of block rows 8w'..8w'+7: K at [16w' + q], V at [16w' + 8 + q]
   __shared__ __attribute__((aligned(16))) float sc0[FP8 ? 64 : 4], sc1[FP8 && NBUF >= 2 ? 64 : 4];
   __shared__ __attribute__((aligned(16))) float sc2[FP8 && NBUF >= 4 ? 64 : 4], sc3[FP8 && NBUF >= 4 ? 64 : 4];
-  __shared__ floatx4 xs[MODE == kSplitDims ? 4 * 2 * 64 : 1];   // partial S^T exchange
+  __shared__ floatx4 xs[DIMS ? 4 * 2 * HT * 64 : 1];   // partial S^T exchange
   __shared__ uint16_t blist[kListCap];
   __shared__ int cnt[4];
   __shared__ int nd_s;   // SPLITKV: the list length, for the producers
@@ -762,6 +769,7 @@ void attn_staged_kernel(const AttnParams p) {
 
   // Q^T operand fragments: head h, dims d0 + 32ks + 8g .. +7
   half8 qf[NKS];
+  half8 qf2[HT == 2 ? NKS : 1];   // kDimsWide: Q^T fragments of heads h + 16
   u32x4 qst[KEYS ? 4 : 1];
   if constexpr (KEYS) {
     // Q rows of heads 16hg + 4w .. +3, one contiguous 1 KiB row per load (they reach
@@ -789,6 +797,11 @@ void attn_staged_kernel(const AttnParams p) {
     const char *qrow = p.q + b * p.q_sb + t * p.q_st + (int64_t)h * p.q_sh;
 #pragma unroll
     for (int ks = 0; ks < NKS; ++ks) qf[ks] = *(const half8 *)(qrow + 2 * (d0 + 32 * ks + 8 * g));
+    if constexpr (HT == 2) {
+      const char *qrow2 = qrow + 16 * p.q_sh;
+#pragma unroll
+      for (int ks = 0; ks < NKS; ++ks) qf2[ks] = *(const half8 *)(qrow2 + 2 * (d0 + 32 * ks + 8 * g));
+    }
   }
   if (INDEXED) {
     // the token's index list; entries up to the end of its last 32-entry block
@@ -887,6 +900,11 @@ void attn_staged_kernel(const AttnParams p) {
 #pragma unroll
   for (int dt = 0; dt < NDT; ++dt) o[dt] = floatx4{0.f, 0.f, 0.f, 0.f};
   float m = -INFINITY, l = 0.f;
+  // kDimsWide: output, running max and sum of the second head tile
+  floatx4 o2[HT == 2 ? NDT : 1];
+#pragma unroll
+  for (int dt = 0; dt < (HT == 2 ? NDT : 1); ++dt) o2[dt] = floatx4{0.f, 0.f, 0.f, 0.f};
+  float m2 = -INFINITY, l2 = 0.f;
 
   // transpose-read roles: this lane points at row slot_row(g, e) of the V tile,
   // 4 dims starting at 16dt + 4a, for the lanes 16g + 4a + (0..3) to receive
@@ -1246,7 +1264,9 @@ void attn_staged_kernel(const AttnParams p) {
   auto iteration = [&](int i, auto buf) __attribute__((always_inline)) {
     constexpr int B = decltype(buf)::value;
     // ---- S^T = K Q^T over this wave's head dims; operand reads run KPD steps ahead
+    // (kDimsWide: t0, t1 for the second head tile, from the same K operands)
     floatx4 s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
+    floatx4 t0 = {0.f, 0.f, 0.f, 0.f}, t1 = {0.f, 0.f, 0.f, 0.f};
     const char *ktc = ktile(buf), *vtc = vtile(buf);
     if constexpr (FP8) {
       // rows c16 and 16 + c16, dims d0 + 32ks + 8g .. +7: 8 codes
@@ -1260,8 +1280,13 @@ void attn_staged_kernel(const AttnParams p) {
       }
 #pragma unroll
       for (int ks = 0; ks < NKS; ++ks) {
-        s0 = mfma16(e4m3x8_to_half8(ka[ks % KPD]), qf[ks], s0);
-        s1 = mfma16(e4m3x8_to_half8(kb[ks % KPD]), qf[ks], s1);
+        const half8 kah = e4m3x8_to_half8(ka[ks % KPD]), kbh = e4m3x8_to_half8(kb[ks % KPD]);
+        s0 = mfma16(kah, qf[ks], s0);
+        s1 = mfma16(kbh, qf[ks], s1);
+        if constexpr (HT == 2) {
+          t0 = mfma16(kah, qf2[ks], t0);
+          t1 = mfma16(kbh, qf2[ks], t1);
+        }
         if (ks + KPD < NKS) {
           ka[ks % KPD] = *(const uint2 *)(krow0 + 32 * (ks + KPD));
           kb[ks % KPD] = *(const uint2 *)(krow1 + 32 * (ks + KPD));
@@ -1280,6 +1305,10 @@ void attn_staged_kernel(const AttnParams p) {
       for (int ks = 0; ks < NKS; ++ks) {
         s0 = mfma16(*(const half8 *)&ka[ks % KPD], qf[ks], s0);
         s1 = mfma16(*(const half8 *)&kb[ks % KPD], qf[ks], s1);
+        if constexpr (HT == 2) {
+          t0 = mfma16(*(const half8 *)&ka[ks % KPD], qf2[ks], t0);
+          t1 = mfma16(*(const half8 *)&kb[ks % KPD], qf2[ks], t1);
+        }
         if (ks + KPD < NKS) {
           ka[ks % KPD] = *(const uint4 *)(krow0 + 64 * (ks + KPD));
           kb[ks % KPD] = *(const uint4 *)(krow1 + 64 * (ks + KPD));
@@ -1287,17 +1316,30 @@ void attn_staged_kernel(const AttnParams p) {
         __builtin_amdgcn_sched_barrier(0);   // keep this order: MFMAs, then the reads they free
       }
     }
-    if (MODE == kSplitDims) {
+    if constexpr (DIMS) {
       // partial tiles meet in LDS; every wave adds them in the same order
-      xs[(w * 2 + 0) * 64 + lane] = s0;
-      xs[(w * 2 + 1) * 64 + lane] = s1;
+      constexpr int XT = 2 * HT;   // partial tiles per wave
+      xs[(w * XT + 0) * 64 + lane] = s0;
+      xs[(w * XT + 1) * 64 + lane] = s1;
+      if constexpr (HT == 2) {
+        xs[(w * XT + 2) * 64 + lane] = t0;
+        xs[(w * XT + 3) * 64 + lane] = t1;
+      }
       lds_barrier();
       s0 = xs[0 * 64 + lane];
       s1 = xs[1 * 64 + lane];
+      if constexpr (HT == 2) {
+        t0 = xs[2 * 64 + lane];
+        t1 = xs[3 * 64 + lane];
+      }
 #pragma unroll
       for (int ww = 1; ww < 4; ++ww) {
-        s0 += xs[(ww * 2 + 0) * 64 + lane];
-        s1 += xs[(ww * 2 + 1) * 64 + lane];
+        s0 += xs[(ww * XT + 0) * 64 + lane];
+        s1 += xs[(ww * XT + 1) * 64 + lane];
+        if constexpr (HT == 2) {
+          t0 += xs[(ww * XT + 2) * 64 + lane];
+          t1 += xs[(ww * XT + 3) * 64 + lane];
+        }
       }
     }
     const int nx = i + NBUF;   // the entry buffer B takes next
@@ -1311,57 +1353,66 @@ void attn_staged_kernel(const AttnParams p) {
         lds_barrier();
       }
     }
-    // ---- online softmax: this lane holds rows slot_row(g, 0..7) of head h
-    float sv[8];
+    // ---- online softmax: this lane holds rows slot_row(g, 0..7) of head h (and,
+    // kDimsWide, of head h + 16): the scores' factors (softmax scale, and FP8: the
+    // K rows' scales), then one pass per head tile
+    float kq[8];
     if constexpr (FP8) {
       // K row scales of slot rows 4g..4g+3 (first rows of wave g's pairs) and
       // 16+4g..16+4g+3 (second rows of wave (g ^ 2)'s pairs)
       const float *sc = stile(buf);
       const float4 klo = *(const float4 *)(sc + 16 * g);
       const float4 khi = *(const float4 *)(sc + 16 * (g ^ 2) + 4);
-      const float kq[8] = {klo.x, klo.y, klo.z, klo.w, khi.x, khi.y, khi.z, khi.w};
+      const float kr[8] = {klo.x, klo.y, klo.z, klo.w, khi.x, khi.y, khi.z, khi.w};
 #pragma unroll
-      for (int i2 = 0; i2 < 4; ++i2) {
-        sv[i2] = s0[i2] * (p.scale_log2 * kq[i2]);
-        sv[4 + i2] = s1[i2] * (p.scale_log2 * kq[4 + i2]);
-      }
+      for (int i2 = 0; i2 < 8; ++i2) kq[i2] = p.scale_log2 * kr[i2];
     } else {
 #pragma unroll
-      for (int i2 = 0; i2 < 4; ++i2) {
-        sv[i2] = s0[i2] * p.scale_log2;
-        sv[4 + i2] = s1[i2] * p.scale_log2;
-      }
+      for (int i2 = 0; i2 < 8; ++i2) kq[i2] = p.scale_log2;
     }
     const uint32_t vis = __builtin_amdgcn_readfirstlane(vmask[i & (kMaskRing - 1)]);
-    if (vis != 0xffffffffu) {
-      const uint32_t sm = slot_mask(vis, g);
+    const uint32_t sm = slot_mask(vis, g);
+    auto softmax = [&](const floatx4 &a0, const floatx4 &a1, float &mm, float &ll, floatx4 *oo)
+        __attribute__((always_inline)) -> half8 {
+      float sv[8];
 #pragma unroll
-      for (int i2 = 0; i2 < 8; ++i2)
-        if (!((sm >> i2) & 1u)) sv[i2] = -INFINITY;
-    }
-    float mx = sv[0];
+      for (int i2 = 0; i2 < 4; ++i2) {
+        sv[i2] = a0[i2] * kq[i2];
+        sv[4 + i2] = a1[i2] * kq[4 + i2];
+      }
+      if (vis != 0xffffffffu) {
 #pragma unroll
-    for (int i2 = 1; i2 < 8; ++i2) mx = fmaxf(mx, sv[i2]);
-    mx = xor_max(mx, 16);
-    mx = xor_max(mx, 32);
-    const bool grow = mx > m + kRescaleSlack;
-    const float mref = grow ? mx : m;
-    const float msafe = (mref == -INFINITY) ? 0.f : mref;
-    const float alpha = __builtin_amdgcn_exp2f(m - msafe);
-    half8 pf;
-    float psum = 0.f;
+        for (int i2 = 0; i2 < 8; ++i2)
+          if (!((sm >> i2) & 1u)) sv[i2] = -INFINITY;
+      }
+      float mx = sv[0];
 #pragma unroll
-    for (int i2 = 0; i2 < 8; ++i2) {
-      const _Float16 ph = (_Float16)__builtin_amdgcn_exp2f(sv[i2] - msafe);
-      pf[i2] = ph;
-      psum += (float)ph;
-    }
-    l = alpha * l + psum;
-    m = mref;
-    if (__ballot(grow)) {
+      for (int i2 = 1; i2 < 8; ++i2) mx = fmaxf(mx, sv[i2]);
+      mx = xor_max(mx, 16);
+      mx = xor_max(mx, 32);
+      const bool grow = mx > mm + kRescaleSlack;
+      const float mref = grow ? mx : mm;
+      const float msafe = (mref == -INFINITY) ? 0.f : mref;
+      const float alpha = __builtin_amdgcn_exp2f(mm - msafe);
+      half8 pp;
+      float psum = 0.f;
 #pragma unroll
-      for (int dt = 0; dt < NDT; ++dt) o[dt] *= alpha;
-    }
+      for (int i2 = 0; i2 < 8; ++i2) {
+        const _Float16 ph = (_Float16)__builtin_amdgcn_exp2f(sv[i2] - msafe);
+        pp[i2] = ph;
+        psum += (float)ph;
+      }
+      ll = alpha * ll + psum;
+      mm = mref;
+      if (__ballot(grow)) {
+#pragma unroll
+        for (int dt = 0; dt < NDT; ++dt) oo[dt] *= alpha;
+      }
+      return pp;
+    };
+    const half8 pf = softmax(s0, s1, m, l, o);
+    half8 pf2 = pf;
+    if constexpr (HT == 2) pf2 = softmax(t0, t1, m2, l2, o2);
     // ---- O^T += V^T P^T; V^T operand = two transpose reads (slots 0-3, 4-7), VPD
     // output tiles ahead
     if constexpr (FP8) {
@@ -1390,7 +1441,9 @@ void attn_staged_kernel(const AttnParams p) {
       for (int u = 0; u < VPD; ++u) vq[u] = vload(u);
 #pragma unroll
       for (int dt = 0; dt < NDT; ++dt) {
-        o[dt] = mfma16(e4m3x8_to_half8(vq[dt % VPD]) * vsc, pf, o[dt]);
+        const half8 vop = e4m3x8_to_half8(vq[dt % VPD]) * vsc;
+        o[dt] = mfma16(vop, pf, o[dt]);
+        if constexpr (HT == 2) o2[dt] = mfma16(vop, pf2, o2[dt]);
         if (dt + VPD < NDT) vq[dt % VPD] = vload(dt + VPD);
         __builtin_amdgcn_sched_barrier(0);   // keep this order: MFMA, then the reads it frees
       }
@@ -1413,6 +1466,7 @@ void attn_staged_kernel(const AttnParams p) {
 #pragma unroll
       for (int dt = 0; dt < NDT; ++dt) {
         o[dt] = mfma16(vq[dt % VPD], pf, o[dt]);
+        if constexpr (HT == 2) o2[dt] = mfma16(vq[dt % VPD], pf2, o2[dt]);
         if (dt + VPD < NDT) vq[dt % VPD] = vload(dt + VPD);
         __builtin_amdgcn_sched_barrier(0);   // keep this order: MFMA, then the reads it frees
       }
@@ -1456,27 +1510,39 @@ void attn_staged_kernel(const AttnParams p) {
   lt = xor_sum(lt, 16);
   lt = xor_sum(lt, 32);
   const float inv = lt > 0.f ? 1.f / lt : 0.f;
-  if constexpr (MODE == kSplitDims) {
-    // DIMS: the workgroup's 16 x 512 float32 outputs (or, for a split part, its
-    // unnormalised partial record) leave through the free tile buffers, so that
-    // every store writes 1 KiB of one row instead of 16 rows x 64 bytes
-    // (the K tiles: every wave's K reads ended at the last score exchange, while
-    // the V tile of the last entry may still be read by slower waves, since that
-    // entry ends without a barrier)
+  if constexpr (DIMS) {
+    // DIMS: the workgroup's 16 (kDimsWide: 32) x 512 float32 outputs (or, for a
+    // split part, its unnormalised partial record) leave through the free tile
+    // buffers, so that every store writes 1 KiB of one row instead of 16 rows x 64
+    // bytes (the K tiles: every wave's K reads ended at the last score exchange,
+    // while the V tile of the last entry may still be read by slower waves, since
+    // that entry ends without a barrier)
     typedef __attribute__((address_space(3))) char lds_w;
     lds_w *kts = (lds_w *)(__attribute__((address_space(3))) void *)kt0;
     lds_w *kts1 = (lds_w *)(__attribute__((address_space(3))) void *)kt1;
+    lds_w *kts2 = (lds_w *)(__attribute__((address_space(3))) void *)kt2;
+    lds_w *kts3 = (lds_w *)(__attribute__((address_space(3))) void *)kt3;
     constexpr int kORow = 2064;                          // 512 float32, padded
     constexpr int RPT = KT / kORow < 16 ? KT / kORow : 16;   // rows per tile buffer
-    static_assert(NBUF >= 2 && 2 * RPT >= 16 && RPT * kORow <= KT, "the 16 output rows fit the K tiles");
+    static_assert(NBUF * RPT >= 16 * HT && RPT * kORow <= KT, "the output rows fit the K tiles");
     auto slot = [&](int sl) __attribute__((always_inline)) -> lds_w * {
-      return (sl < RPT ? kts : kts1) + (sl % RPT) * kORow;
+      const int tb = sl / RPT;
+      return (tb == 0 ? kts : (tb == 1 ? kts1 : (tb == 2 ? kts2 : kts3))) + (sl % RPT) * kORow;
     };
     constexpr bool part = PARTS;
     const float sc = (part ? 1.f : inv) * kOut;
     lds_w *row = slot(c16) + 4 * d0 + 16 * g;
 #pragma unroll
     for (int dt = 0; dt < NDT; ++dt) *(__attribute__((address_space(3))) floatx4 *)(row + 64 * dt) = o[dt] * sc;
+    if constexpr (HT == 2) {
+      float lt2 = l2;
+      lt2 = xor_sum(lt2, 16);
+      lt2 = xor_sum(lt2, 32);
+      const float sc2 = (lt2 > 0.f ? 1.f / lt2 : 0.f) * kOut;
+      lds_w *row2 = slot(16 + c16) + 4 * d0 + 16 * g;
+#pragma unroll
+      for (int dt = 0; dt < NDT; ++dt) *(__attribute__((address_space(3))) floatx4 *)(row2 + 64 * dt) = o2[dt] * sc2;
+    }
     lds_barrier();
     char *rec = part ? p.ws + ((int64_t)L * nsplit + split) * kSplitRecord : nullptr;
     if constexpr (part) {
@@ -1488,9 +1554,10 @@ void attn_staged_kernel(const AttnParams p) {
         *(floatx4 *)((float *)rec + r * 512 + 256 * half + 4 * lane) = v;
       }
     } else {
+      // wave w stores rows 4 HT w .. 4 HT w + 4 HT - 1, 1 KiB per store
 #pragma unroll
-      for (int k = 0; k < 8; ++k) {
-        const int r = 4 * w + (k >> 1), half = k & 1;
+      for (int k = 0; k < 8 * HT; ++k) {
+        const int r = 4 * HT * w + (k >> 1), half = k & 1;
         const floatx4 v = *(const __attribute__((address_space(3))) floatx4 *)(slot(r) + 1024 * half + lane16);
         float *dst = (float *)(p.o + b * p.o_sb + t * p.o_st + (int64_t)(hg * HG + r) * p.o_sh);
         __builtin_nontemporal_store(v, (floatx4 *)(dst + 256 * half + 4 * lane));
@@ -1578,8 +1645,30 @@ static bool use_keys(const AttnParams &p) {
   if (p.decode_split) return p.decode_split == 2;
   return list_bound(p) / (p.nsplit > 0 ? p.nsplit : 1) >= (p.fp8 ? kKeysMinEntriesFp8 : kKeysMinEntries);
 }
+// Wide DIMS (32 heads per workgroup) once the 16-head grid has more workgroups than
+// the chip has CUs: it then fits in half the rounds.  Below that its extra work per
+// block lengthens every workgroup (measured on the sliding-window decode: 8 / 32 / 64
+// sequences 10.8 / 11.4 / 13.0 us wide against 8.2 / 8.9 / 10.6 us; 128 sequences,
+// 512 workgroups of 16 heads, 14.8 us against 20.0 us).  No index lists (their LDS
+// does not fit beside the wider score exchange), no split parts.
+constexpr int64_t kWideAboveGroups = kNumCus;
+static bool use_wide(const AttnParams &p) {
+  if (p.indexed || p.nsplit > 1 || p.H % 32 != 0) return false;
+  if (p.decode_split) return p.decode_split == 3;
+  return (int64_t)p.B * p.T * (p.H / 16) > kWideAboveGroups;
+}
+static hipError_t launch_wide(const AttnParams &p, hipStream_t s) {
+  const int64_t n = (int64_t)p.B * p.T * (p.H / 32);
+  if (n == 0) return hipSuccess;
+  const dim3 grid((unsigned)n), block(512);
+  if (p.fp8) hipLaunchKernelGGL((attn_staged_kernel<kDimsWide, false, true, false>), grid, block, 0, s, p);
+  else hipLaunchKernelGGL((attn_staged_kernel<kDimsWide, false, false, false>), grid, block, 0, s, p);
+  return hipGetLastError();
+}
 hipError_t launch_attn_decode(const AttnParams &p, hipStream_t s) {
-  return use_keys(p) ? launch_staged<kSplitKeys>(p, s) : launch_staged<kSplitDims>(p, s);
+  if (use_keys(p)) return launch_staged<kSplitKeys>(p, s);
+  if (use_wide(p)) return launch_wide(p, s);
+  return launch_staged<kSplitDims>(p, s);
 }
 // Combine the split partials of one (token, head group): 16 heads x 512 dims over
 // 1024 threads, thread = (head, 8 consecutive dims).  The partials were accumulated

@@ -152,11 +152,14 @@ int resolve_args(const ds4attn_args *a, bool prefill, Resolved &R) {
   // FP8 rows are dequantized inside the matrix-core kernels only
   if (fp8 && !R.mfma) return DS4ATTN_E_UNSUPPORTED;
   const bool want_dims = a->flags & DS4ATTN_FLAG_DECODE_DIMS, want_keys = a->flags & DS4ATTN_FLAG_DECODE_KEYS;
-  if (want_dims && want_keys) return DS4ATTN_E_INVAL;
-  if (want_dims || want_keys) {
+  const bool want_wide = a->flags & DS4ATTN_FLAG_DECODE_WIDE;
+  if ((int)want_dims + (int)want_keys + (int)want_wide > 1) return DS4ATTN_E_INVAL;
+  if (want_dims || want_keys || want_wide) {
     // a chosen decode split: the matrix-core decode kernel
     if (!R.mfma || (prefill && a->n_head % 64 == 0)) return DS4ATTN_E_UNSUPPORTED;
-    P.decode_split = want_keys ? 2 : 1;
+    // the wide split: 32 heads per workgroup, no index list
+    if (want_wide && (P.indexed || a->n_head % 32 != 0)) return DS4ATTN_E_UNSUPPORTED;
+    P.decode_split = want_keys ? 2 : (want_wide ? 3 : 1);
   }
   return DS4ATTN_OK;
 }
@@ -169,7 +172,8 @@ int resolve_args(const ds4attn_args *a, bool prefill, Resolved &R) {
 // blocks per part (measured: one sequence of the ratio-128 layer at 32K, 12
 // blocks, runs fastest in 4 parts; 64-sequence batches only lose from splitting).
 int plan_splits(const Resolved &R, bool prefill) {
-  if (prefill || R.empty || !R.mfma) return 1;
+  // (a chosen wide split has no split parts)
+  if (prefill || R.empty || !R.mfma || R.P.decode_split == 3) return 1;
   const AttnParams &P = R.P;
   const int64_t groups = (int64_t)P.B * P.T * (P.H / 16);
   if (groups >= 128) return 1;
@@ -200,14 +204,15 @@ int launch_resolved(const ds4attn_args *a, Resolved &R, const void *q, const uin
   P.bq = blk ? (int)std::min<int64_t>(bq, std::max(1, a->n_tok)) : 1;
   P.ntiles = ((int64_t)a->n_tok + P.bq - 1) / P.bq;
   P.div_g16 = make_fast_div((uint32_t)std::max(1, a->n_head / 16));
+  P.div_g32 = make_fast_div((uint32_t)std::max(1, a->n_head / 32));
   P.div_g64 = make_fast_div((uint32_t)std::max(1, a->n_head / 64));
   P.div_t = make_fast_div((uint32_t)std::max(1, a->n_tok));
   P.div_bq = make_fast_div((uint32_t)P.bq);
   hipStream_t s = (hipStream_t)stream;
   hipError_t e;
   if (splits > 1) {
-    // split decode runs on the matrix-core decode kernel only
-    if (!R.mfma || prefill) return DS4ATTN_E_UNSUPPORTED;
+    // split decode runs on the matrix-core decode kernel only, 16 heads per part
+    if (!R.mfma || prefill || R.P.decode_split == 3) return DS4ATTN_E_UNSUPPORTED;
     const int64_t work = (int64_t)a->batch * a->n_tok;
     if (work * (a->n_head / 16) * splits > 0x7fffffffLL) return DS4ATTN_E_UNSUPPORTED;
     const int64_t need = split_workspace_bytes(a, splits);

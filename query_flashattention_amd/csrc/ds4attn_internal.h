@@ -13,6 +13,7 @@ namespace ds4attn {
 
 constexpr int kRowsPerBlock = 32;   // [P-Metal] KV-Cache Management: 32-row padding
 constexpr int kNumXcd = 8;          // MI355X: 8 accelerator dies, workgroups dealt round-robin
+constexpr int kNumCus = 256;        // compute units (32 per die)
 constexpr int kIdxCap = 2048;       // largest index list held in LDS by the matrix-core kernel
 
 enum : int { kSkip = 0, kPartial = 1, kFull = 2 };
@@ -68,7 +69,8 @@ struct AttnParams {
   // split decode: each token's block list divided over nsplit workgroups per head
   // group, partial results in ws (one kSplitRecord per (b, t, head group, split))
   int nsplit;              // 1 = no split
-  int decode_split;        // decode work split: 0 = chosen by list length, 1 = DIMS, 2 = KEYS
+  int decode_split;        // decode work split: 0 = chosen by the library, 1 = DIMS, 2 = KEYS,
+                           // 3 = DIMS over 32 heads per workgroup
   char *ws;
   // block map
   const uint8_t *blk;      // [B][ntiles][nbd] or null (every block treated as PARTIAL)
@@ -76,8 +78,8 @@ struct AttnParams {
   int64_t ntiles;
   int nbd;                 // blocks covered by the map: nb0 (+ nb1 when not indexed)
   // the matrix-core kernels' index divisions by run-time values, as multiply and
-  // shift (see fast_div): by H/16, H/64, T and bq
-  FastDiv div_g16, div_g64, div_t, div_bq;
+  // shift (see fast_div): by H/16, H/32, H/64, T and bq
+  FastDiv div_g16, div_g32, div_g64, div_t, div_bq;
 };
 
 // Bound on the length of a token's block list: the dense blocks of region 0 its

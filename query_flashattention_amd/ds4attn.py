@@ -25,6 +25,7 @@ BLK_SKIP, BLK_PARTIAL, BLK_FULL = 0, 1, 2
 FLAG_GENERIC = 1
 FLAG_DECODE_DIMS = 2
 FLAG_DECODE_KEYS = 4
+FLAG_DECODE_WIDE = 8
 
 _c_void_p = ctypes.c_void_p
 _i32, _i64 = ctypes.c_int32, ctypes.c_int64

@@ -389,6 +389,44 @@ def test_decode_split_flags_need_the_matrix_core_kernel():
     assert _decode(a) == da.E_UNSUPPORTED
 
 
+@pytest.mark.parametrize("flags,expect", [
+    (da.FLAG_DECODE_WIDE | da.FLAG_DECODE_DIMS, da.E_INVAL),
+    (da.FLAG_DECODE_WIDE | da.FLAG_DECODE_KEYS, da.E_INVAL),
+    (da.FLAG_DECODE_WIDE | da.FLAG_GENERIC, da.E_UNSUPPORTED),
+])
+def test_wide_decode_flag_rejected(flags, expect):
+    a = _good_args()
+    a.flags = flags
+    assert _decode(a) == expect
+
+
+def test_wide_decode_needs_32_heads_and_no_index_list():
+    a = _good_args(heads=48)
+    a.flags = da.FLAG_DECODE_WIDE
+    assert _decode(a) == da.E_UNSUPPORTED
+    a = _good_args()
+    a.flags = da.FLAG_DECODE_WIDE
+    a.r1.k = a.r1.v = FAKE + (1 << 30)
+    a.r1.n_rows = 256
+    a.r1.stride_row = 1024
+    a.r1.stride_b = 256 * 1024
+    a.r1_index = FAKE
+    a.r1_k = 64
+    assert _decode(a) == da.E_UNSUPPORTED
+
+
+def test_wide_decode_is_never_split():
+    """A chosen wide split plans no parts (no workspace), and the split entry point
+    refuses it before anything is enqueued."""
+    lib = da.lib()
+    a = _good_args()
+    a.flags = da.FLAG_DECODE_WIDE
+    assert da.ds4attn_workspace_bytes(a, False) == 0
+    ws = FAKE + (1 << 32)
+    need = 1 * 1 * 4 * 2 * (16 * 512 * 4 + 128)
+    assert lib.ds4attn_decode_split(ctypes.byref(a), FAKE, None, 1, FAKE, 2, ws, need, None) == da.E_UNSUPPORTED
+
+
 def _ratio128_args(batch=1):
     """One decode token of a ratio-128 layer at 32K: 128 raw rows + 256 compressed slots."""
     a = _good_args()

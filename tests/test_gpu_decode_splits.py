@@ -1,7 +1,8 @@
-"""GPU parity of the two ways the matrix-core decode kernel divides a workgroup's
+"""GPU parity of the ways the matrix-core decode kernel divides a workgroup's
 work over its four waves, each forced with its flag: DIMS (the waves share every
-key block and split the head dimension) and KEYS (the waves take different 16-row
-halves of the key blocks and merge their partial results).  Both against the
+key block and split the head dimension; also WIDE, the same over 32 heads per
+workgroup) and KEYS (the waves take different 16-row halves of the key blocks and
+merge their partial results).  Both against the
 float64 oracle within the attention tolerance (max-abs 1e-2, mean-abs 1e-3), on
 the decode workloads at full size and on general cases (windows, validity masks,
 two regions, index lists with unused entries, empty regions, tokens that see no
@@ -25,6 +26,8 @@ pytestmark = pytest.mark.gpu
 MAX_ABS, MEAN_ABS = 1e-2, 1e-3
 DEV = "cuda:0"
 SPLITS = {"dims": da.FLAG_DECODE_DIMS, "keys": da.FLAG_DECODE_KEYS}
+# DIMS over 32 heads per workgroup: head counts that are multiples of 32, no index lists
+WIDE = da.FLAG_DECODE_WIDE
 
 
 @pytest.fixture(scope="module", autouse=True)
@@ -122,6 +125,31 @@ def test_split_over_workgroups(label, kw, splits, split):
     want = ref.attention(ref.from_workload(w))
     _compare(_run(w, SPLITS[split], splits=splits), want, f"{label}/{split} x{splits}")
     _compare(_run(w, SPLITS[split], use_map=False, splits=splits), want, f"{label}/{split} x{splits} no map")
+
+
+@pytest.mark.parametrize("name", ["decode_swa", "decode_r128", "decode_r128_b64"])
+def test_wide_workload_full(name):
+    w = wl.named(name)
+    _compare(_run(w, WIDE), ref.attention(ref.from_workload(w)), f"{name}/wide")
+
+
+WIDE_CASES = [(label, kw) for label, kw in CASES if kw["heads"] % 32 == 0 and kw.get("r1_mode") != "index"] + [
+    ("wide_one_row", dict(batch=2, tokens=1, heads=64, head_dim=512, n0=1)),
+    ("wide_masked_tokens", dict(batch=1, tokens=5, heads=32, head_dim=512, n0=40, window=4, q_pos0=0, k_pos0=3)),
+    ("wide_long_dense", dict(batch=1, tokens=1, heads=32, head_dim=512, n0=4500, valid0_frac=0.9)),
+    ("wide_ragged", dict(batch=3, tokens=2, heads=96, head_dim=512, n0=77)),
+]
+
+
+@pytest.mark.parametrize("label,kw", WIDE_CASES, ids=[c[0] for c in WIDE_CASES])
+def test_wide_random(label, kw):
+    w = wl.random_problem(zlib.crc32(label.encode()) % 1000 + 3, **kw)
+    want = ref.attention(ref.from_workload(w))
+    out = _run(w, WIDE)
+    _compare(out, want, f"{label}/wide")
+    _compare(_run(w, WIDE, use_map=False), want, f"{label}/wide no map")
+    if label == "wide_masked_tokens":
+        assert (out[0, :3] == 0).all()   # tokens 0..2 see no row: exact zeros
 
 
 def test_both_splits_agree_on_ratio128_single_sequence():

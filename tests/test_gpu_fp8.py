@@ -249,6 +249,31 @@ def test_attention_fp8_decode_splits(label, kw, split):
         assert (out[0, :3] == 0).all()
 
 
+@pytest.mark.parametrize("name", ["decode_swa_fp8", "decode_r128_fp8"])
+def test_attention_fp8_wide_workloads(name):
+    """The wide DIMS split (32 heads per workgroup) on the FP8 batches without index
+    lists, every output element."""
+    w = wl.named(name)
+    _compare(_run_flags(w, da.FLAG_DECODE_WIDE), _oracle_full(name), f"{name}/wide")
+
+
+FP8_WIDE_CASES = [(label, kw) for label, kw in FP8_DECODE_CASES
+                  if kw["heads"] % 32 == 0 and kw.get("r1_mode") != "index"] + [
+    ("f8_wide_one_block", dict(batch=2, tokens=2, heads=32, head_dim=512, n0=20)),
+    ("f8_wide_masked_tokens", dict(batch=1, tokens=5, heads=64, head_dim=512, n0=40, window=4, q_pos0=0,
+                                   k_pos0=3)),
+]
+
+
+@pytest.mark.parametrize("label,kw", FP8_WIDE_CASES, ids=[c[0] for c in FP8_WIDE_CASES])
+def test_attention_fp8_decode_wide(label, kw):
+    """Hidden rows hold NaN codes and NaN scales, as in the other split tests."""
+    w = wl.fp8_variant(wl.random_problem(zlib.crc32(label.encode()) % 1000 + 5, **kw), 7)
+    want = ref.attention(_oracle_problem(w))
+    _poison_hidden_rows(w)
+    _compare(_run_flags(w, da.FLAG_DECODE_WIDE), want, f"{label}/wide")
+
+
 @pytest.mark.parametrize("split", list(FP8_SPLITS))
 def test_attention_fp8_workloads_splits(split):
     w = wl.named("decode_r128_fp8")

@@ -12,8 +12,8 @@ tolerance alone (max-abs 1e-2, mean-abs 1e-3) could let through.
 * Wrong speculative starts: the kernels fetch their first list entries from the
   window arithmetic before the block map arrives.  A window whose reach ends in
   one raw block followed by a dense region 1, and leading raw blocks that are all
-  invalid, make those guesses wrong in every kernel (HEADS prefill, DIMS and KEYS
-  decode, split parts, FP8 rows), while the guessed rows hold NaN.
+  invalid, make those guesses wrong in every kernel (HEADS prefill, DIMS, wide DIMS
+  and KEYS decode, split parts, FP8 rows), while the guessed rows hold NaN.
 * A query tile longer than the chunk (bq = 2^31 - 1) is one tile.
 
 Every case runs through the C ABI and is compared with the float64 oracle.
@@ -51,7 +51,14 @@ MODES = {
     "keys": ("decode", da.FLAG_DECODE_KEYS, 1),
     "split3": ("decode", 0, 3),
     "plan": ("decode", 0, None),
+    # DIMS over 32 heads per workgroup: no index lists
+    "wide": ("decode", da.FLAG_DECODE_WIDE, 1),
 }
+KERNEL_MODES = ["prefill", "dims", "keys", "split3", "wide"]
+
+
+def _indexed(kw):
+    return kw.get("r1_mode") == "index"
 
 
 def _run(w, mode, use_map=True, pad=True, bq=None):
@@ -120,8 +127,11 @@ POISON_CASES = [
 ]
 
 
-@pytest.mark.parametrize("mode", ["prefill", "dims", "keys", "split3"])
-@pytest.mark.parametrize("label,kw", POISON_CASES, ids=[c[0] for c in POISON_CASES])
+POISON_PARAMS = [(label, kw, mode) for label, kw in POISON_CASES for mode in KERNEL_MODES
+                 if not (mode == "wide" and _indexed(kw))]
+
+
+@pytest.mark.parametrize("label,kw,mode", POISON_PARAMS, ids=[f"{c[0]}-{c[2]}" for c in POISON_PARAMS])
 def test_poisoned_hidden_rows(label, kw, mode):
     w = free_row0(wl.random_problem(zlib.crc32(label.encode()) % 1000 + 31, **kw))
     w, n = poison_hidden(w)
@@ -131,7 +141,7 @@ def test_poisoned_hidden_rows(label, kw, mode):
     compare(_run(w, mode, use_map=False), want, f"{label}/{mode} no map")
 
 
-@pytest.mark.parametrize("mode", ["prefill", "dims", "keys", "split3"])
+@pytest.mark.parametrize("mode", KERNEL_MODES)
 @pytest.mark.parametrize("fp8", [False, True], ids=["f16", "fp8"])
 def test_unpadded_tail_stays_hidden(mode, fp8):
     """The rows between the live count and the block end hold NaN (the pad stage
@@ -155,6 +165,13 @@ def test_poisoned_decode_workloads(mode):
         compare(_run(w, mode), _oracle(w), f"{name}/{mode} ({n} NaN rows)")
 
 
+def test_poisoned_decode_workloads_wide():
+    """The same for the wide DIMS split on the batches without index lists."""
+    for name in ("decode_r128_b64", "decode_swa"):
+        w, n = poison_hidden(wl.named(name))
+        compare(_run(w, "wide"), _oracle(w), f"{name}/wide ({n} NaN rows)")
+
+
 # --------------------------------------------------------------------------- one-hot values
 
 def _decode_r4_onehot(topk=384):
@@ -170,13 +187,15 @@ def _decode_r4_onehot(topk=384):
     return poison_hidden(w)[0]
 
 
-@pytest.mark.parametrize("mode", ["dims", "keys", "plan", "split3"])
+@pytest.mark.parametrize("mode", ["dims", "keys", "plan", "split3", "wide"])
 def test_onehot_decode_workloads(mode):
     w = wl.named("decode_r128_b64")
     w = poison_hidden(onehot_values(w, lambda b, j: j, lambda b, c: 128 + c))[0]
     out, want = _run(w, mode), _oracle(w)
     compare(out, want, f"decode_r128_b64 one-hot/{mode}")
     check_onehot(out, want, f"decode_r128_b64 one-hot/{mode}")
+    if mode == "wide":
+        return   # (the ratio-4 batch has index lists)
     w = _decode_r4_onehot()
     out, want = _run(w, mode), _oracle(w)
     compare(out, want, f"decode_r4 top-384 one-hot/{mode}")
@@ -237,9 +256,12 @@ SPEC_CASES = [
 ]
 
 
+SPEC_PARAMS = [(label, make, mode) for label, make in SPEC_CASES for mode in KERNEL_MODES
+               if not (mode == "wide" and label.endswith("indexed"))]
+
+
 @pytest.mark.parametrize("fp8", [False, True], ids=["f16", "fp8"])
-@pytest.mark.parametrize("mode", ["prefill", "dims", "keys", "split3"])
-@pytest.mark.parametrize("label,make", SPEC_CASES, ids=[c[0] for c in SPEC_CASES])
+@pytest.mark.parametrize("label,make,mode", SPEC_PARAMS, ids=[f"{c[0]}-{c[2]}" for c in SPEC_PARAMS])
 def test_wrong_speculative_start(label, make, mode, fp8):
     tokens = 16 if mode == "prefill" else 1
     w = make(tokens, 64)
@@ -278,7 +300,7 @@ def test_tile_longer_than_the_chunk():
 
 # --------------------------------------------------------------------------- large score jumps
 
-@pytest.mark.parametrize("mode", ["prefill", "dims", "keys", "split3"])
+@pytest.mark.parametrize("mode", KERNEL_MODES)
 def test_score_jump_after_the_first_block(mode):
     """Keys of a later block scaled by 16: the scores there exceed the first block's
     maximum by far more than 2^8 in the base-2 softmax, so every kernel must move
