@@ -53,6 +53,33 @@ namespace ds4attn {
 // (kDimsWide: DIMS over 32 heads per workgroup, see DIMS below)
 enum : int { kSplitHeads = 0, kSplitDims = 1, kSplitKeys = 2, kDimsWide = 3 };
 
+// Stores a float32 tile of 16 heads x 16 N dims held in accumulator layout (lane
+// 16g + c16 holds head c16, dims 16dt + 4g .. +3 in acc[dt]), times `sc` (this
+// lane's head's factor), to the rows at `dst` (head c at dst + c * stride bytes).
+// A cross-lane permutation first gives lane l head l >> 2, dims 16dt + 4(l & 3),
+// so that four adjacent lanes write 64 contiguous bytes: the address path
+// coalesces adjacent lanes only, and 16-byte accesses in the accumulator's lane
+// order (a row per lane, a row's four pieces 16 lanes apart) cost it about 3.4
+// times as long (measured with loads of the same shape from L2).
+template <int N, bool NONTEMPORAL>
+__device__ __forceinline__ void store_acc_rows(char *dst, int64_t stride, const floatx4 *acc, float sc,
+                                               int lane) {
+  typedef int int4v __attribute__((ext_vector_type(4)));
+  const int src = 4 * (16 * (lane & 3) + (lane >> 2));   // byte address of the source lane
+  floatx4 *row = (floatx4 *)(dst + (int64_t)(lane >> 2) * stride) + (lane & 3);
+#pragma unroll
+  for (int dt = 0; dt < N; ++dt) {
+    // (whole-vector casts: a cast of one element of a vector value is not safe here)
+    const int4v v = __builtin_bit_cast(int4v, acc[dt] * sc);
+    int4v ri;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) ri[k] = __builtin_amdgcn_ds_bpermute(src, v[k]);
+    const floatx4 r = __builtin_bit_cast(floatx4, ri);
+    if constexpr (NONTEMPORAL) __builtin_nontemporal_store(r, row + 4 * dt);
+    else row[4 * dt] = r;
+  }
+}
+
 // FP8 rows (E4M3 codes, a float32 scale per row): the rows travel to LDS as codes
 // (half the bytes), two rows per transfer, and are converted where the operands
 // are read: K codes to float16 (exact), with the row's scale applied to the fp32
@@ -621,8 +648,8 @@ void attn_staged_kernel(const AttnParams p) {
   // SPLITKV producers: their whole program.  It meets the computing waves' barriers
   // in the same order: the block list's (two per 256 map entries and a final one),
   // the first-block mask table's, the masks', entry e0's, then per entry i the
-  // score exchange, a mask refill when entry i + NBUF starts a chunk, the end of the
-  // entry while another follows, and the epilogue's.  It branches off before the
+  // score exchange, a mask refill when entry i + NBUF starts a chunk, and the end of
+  // the entry while another follows.  It branches off before the
   // computing waves load anything through the compiler, so that no wait of theirs
   // (nor one for registers their loads would write) lands in this path.
   if constexpr (SPLITKV) {
@@ -660,9 +687,6 @@ void attn_staged_kernel(const AttnParams p) {
       auto produce8 = [&](int i, auto buf) __attribute__((always_inline)) {
         constexpr int B = decltype(buf)::value;
         const int nx = i + NBUF;
-        // before the last entry's exchange nothing may remain in flight (a guessed
-        // entry past a short list): the epilogue writes the K tiles after it
-        if (i + 1 >= e1) wait_vmcnt<0>();
         lds_barrier();   // score exchange of entry i
         if (nx < e1 && (nx & (kMaskChunk - 1)) == 0) lds_barrier();   // masks of entries nx..
         if (i + 1 < e1) {
@@ -685,8 +709,7 @@ void attn_staged_kernel(const AttnParams p) {
       lds_barrier();   // masks visible
       if constexpr (FP8) {
         // entry e0 landed: only the guessed entries after it may be in flight (after
-        // a redo the order is not known, and an empty list goes to the epilogue
-        // next: wait for everything)
+        // a redo the order is not known: wait for everything, as for an empty list)
         if (redo || e0 >= e1) wait_vmcnt<0>();
         else if (spec(3) >= 0) wait_vmcnt<3 * kF8StageOps>();
         else if (spec(2) >= 0) wait_vmcnt<2 * kF8StageOps>();
@@ -712,7 +735,6 @@ void attn_staged_kernel(const AttnParams p) {
         });
       }
       wait_vmcnt<0>();   // nothing in flight when the workgroup ends
-      lds_barrier();     // the epilogue's barrier
       return;
     }
   }
@@ -1220,9 +1242,7 @@ void attn_staged_kernel(const AttnParams p) {
     if constexpr (PARTS) {
       // partial record of this split: unnormalised O, then the maxima and the sums
       char *rec = p.ws + ((int64_t)L * nsplit + split) * kSplitRecord;
-      float *ob = (float *)rec + c16 * 512 + 128 * w + 4 * g;
-#pragma unroll
-      for (int k = 0; k < 8; ++k) *(floatx4 *)(ob + 16 * k) = acc[k];
+      store_acc_rows<8, false>(rec + 512 * w, 512 * 4, acc, 1.f, lane);
       if (w == 0 && g == 0) {
         ((float *)(rec + 16 * 512 * 4))[c16] = mall;
         ((float *)(rec + 16 * 512 * 4))[16 + c16] = lall;
@@ -1230,9 +1250,8 @@ void attn_staged_kernel(const AttnParams p) {
       return;
     }
     const float inv = lall > 0.f ? 1.f / lall : 0.f;
-    float *ob = (float *)(p.o + b * p.o_sb + t * p.o_st + (int64_t)h * p.o_sh) + 128 * w + 4 * g;
-#pragma unroll
-    for (int k = 0; k < 8; ++k) __builtin_nontemporal_store(acc[k] * inv, (floatx4 *)(ob + 16 * k));
+    store_acc_rows<8, true>(p.o + b * p.o_sb + t * p.o_st + (int64_t)(hg * HG) * p.o_sh + 512 * w, p.o_sh, acc,
+                            inv, lane);
     return;
   }
 
@@ -1511,70 +1530,35 @@ void attn_staged_kernel(const AttnParams p) {
   lt = xor_sum(lt, 32);
   const float inv = lt > 0.f ? 1.f / lt : 0.f;
   if constexpr (DIMS) {
-    // DIMS: the workgroup's 16 (kDimsWide: 32) x 512 float32 outputs (or, for a
-    // split part, its unnormalised partial record) leave through the free tile
-    // buffers, so that every store writes 1 KiB of one row instead of 16 rows x 64
-    // bytes (the K tiles: every wave's K reads ended at the last score exchange,
-    // while the V tile of the last entry may still be read by slower waves, since
-    // that entry ends without a barrier)
-    typedef __attribute__((address_space(3))) char lds_w;
-    lds_w *kts = (lds_w *)(__attribute__((address_space(3))) void *)kt0;
-    lds_w *kts1 = (lds_w *)(__attribute__((address_space(3))) void *)kt1;
-    lds_w *kts2 = (lds_w *)(__attribute__((address_space(3))) void *)kt2;
-    lds_w *kts3 = (lds_w *)(__attribute__((address_space(3))) void *)kt3;
-    constexpr int kORow = 2064;                          // 512 float32, padded
-    constexpr int RPT = KT / kORow < 16 ? KT / kORow : 16;   // rows per tile buffer
-    static_assert(NBUF * RPT >= 16 * HT && RPT * kORow <= KT, "the output rows fit the K tiles");
-    auto slot = [&](int sl) __attribute__((always_inline)) -> lds_w * {
-      const int tb = sl / RPT;
-      return (tb == 0 ? kts : (tb == 1 ? kts1 : (tb == 2 ? kts2 : kts3))) + (sl % RPT) * kORow;
-    };
-    constexpr bool part = PARTS;
-    const float sc = (part ? 1.f : inv) * kOut;
-    lds_w *row = slot(c16) + 4 * d0 + 16 * g;
-#pragma unroll
-    for (int dt = 0; dt < NDT; ++dt) *(__attribute__((address_space(3))) floatx4 *)(row + 64 * dt) = o[dt] * sc;
-    if constexpr (HT == 2) {
-      float lt2 = l2;
-      lt2 = xor_sum(lt2, 16);
-      lt2 = xor_sum(lt2, 32);
-      const float sc2 = (lt2 > 0.f ? 1.f / lt2 : 0.f) * kOut;
-      lds_w *row2 = slot(16 + c16) + 4 * d0 + 16 * g;
-#pragma unroll
-      for (int dt = 0; dt < NDT; ++dt) *(__attribute__((address_space(3))) floatx4 *)(row2 + 64 * dt) = o2[dt] * sc2;
-    }
-    lds_barrier();
-    char *rec = part ? p.ws + ((int64_t)L * nsplit + split) * kSplitRecord : nullptr;
-    if constexpr (part) {
-      // a split part's record is read back by the combine pass: cached stores
-#pragma unroll
-      for (int k = 0; k < 8; ++k) {
-        const int r = 4 * w + (k >> 1), half = k & 1;
-        const floatx4 v = *(const __attribute__((address_space(3))) floatx4 *)(slot(r) + 1024 * half + lane16);
-        *(floatx4 *)((float *)rec + r * 512 + 256 * half + 4 * lane) = v;
+    // DIMS: wave w writes dims 128w .. 128w + 127 of the workgroup's 16 (kDimsWide:
+    // 32) heads, or, for a split part, of its unnormalised partial record (read
+    // back by the combine pass: cached stores)
+    if constexpr (PARTS) {
+      char *rec = p.ws + ((int64_t)L * nsplit + split) * kSplitRecord;
+      store_acc_rows<NDT, false>(rec + 4 * d0, 512 * 4, o, kOut, lane);
+      if (w == 0 && g == 0) {
+        // then the maxima and the sums
+        ((float *)(rec + 16 * 512 * 4))[c16] = m;
+        ((float *)(rec + 16 * 512 * 4))[16 + c16] = lt;
       }
     } else {
-      // wave w stores rows 4 HT w .. 4 HT w + 4 HT - 1, 1 KiB per store
-#pragma unroll
-      for (int k = 0; k < 8 * HT; ++k) {
-        const int r = 4 * HT * w + (k >> 1), half = k & 1;
-        const floatx4 v = *(const __attribute__((address_space(3))) floatx4 *)(slot(r) + 1024 * half + lane16);
-        float *dst = (float *)(p.o + b * p.o_sb + t * p.o_st + (int64_t)(hg * HG + r) * p.o_sh);
-        __builtin_nontemporal_store(v, (floatx4 *)(dst + 256 * half + 4 * lane));
+      char *orow = p.o + b * p.o_sb + t * p.o_st + (int64_t)(hg * HG) * p.o_sh + 4 * d0;
+      store_acc_rows<NDT, true>(orow, p.o_sh, o, inv * kOut, lane);
+      if constexpr (HT == 2) {
+        float lt2 = l2;
+        lt2 = xor_sum(lt2, 16);
+        lt2 = xor_sum(lt2, 32);
+        store_acc_rows<NDT, true>(orow + 16 * p.o_sh, p.o_sh, o2, (lt2 > 0.f ? 1.f / lt2 : 0.f) * kOut, lane);
       }
-    }
-    if (part && w == 0 && g == 0) {
-      // then the maxima and the sums
-      ((float *)(rec + 16 * 512 * 4))[c16] = m;
-      ((float *)(rec + 16 * 512 * 4))[16 + c16] = lt;
     }
     return;
   }
   if constexpr (MODE == kSplitHeads) {
     // HEADS: the 64 x 512 float32 outputs leave through the free tile buffers, so
-    // that every store writes 1 KiB of one row (stores shaped like the accumulator,
-    // 16 rows x 64 bytes each, cost the vector-memory path about three times as
-    // much).  Per pass WPP waves write their 16 rows; then all four waves store them.
+    // that every store writes 1 KiB of one row.  Per pass WPP waves write their 16
+    // rows; then all four waves store them.  (Stored straight from the accumulators
+    // with store_acc_rows, 16 rows x 64 bytes per store, the 128 KiB per token made
+    // the prefill kernels slower, the sliding-window chunk 110 -> 119 us.)
     typedef __attribute__((address_space(3))) char lds_w;
     lds_w *kts = (lds_w *)(__attribute__((address_space(3))) void *)kt0;
     lds_w *vts = (lds_w *)(__attribute__((address_space(3))) void *)vt0;
@@ -1606,9 +1590,6 @@ void attn_staged_kernel(const AttnParams p) {
     }
     return;
   }
-  float *ob = (float *)(p.o + b * p.o_sb + t * p.o_st + (int64_t)h * p.o_sh) + d0 + 4 * g;
-#pragma unroll
-  for (int dt = 0; dt < NDT; ++dt) *(floatx4 *)(ob + 16 * dt) = o[dt] * (inv * kOut);
 }
 
 template <int MODE>
@@ -1671,7 +1652,7 @@ hipError_t launch_attn_decode(const AttnParams &p, hipStream_t s) {
   return launch_staged<kSplitDims>(p, s);
 }
 // Combine the split partials of one (token, head group): 16 heads x 512 dims over
-// 1024 threads, thread = (head, 8 consecutive dims).  The partials were accumulated
+// 1024 threads, thread = (head, 8 dims).  The partials were accumulated
 // against their own running maxima m_s (base 2); with M = max m_s the result is
 // sum_s 2^(m_s - M) O_s / sum_s 2^(m_s - M) l_s, zero when no split saw a row.  The
 // maxima and sums of all parts are staged in LDS first (one load per thread), and
@@ -1684,7 +1665,9 @@ __global__ __launch_bounds__(1024) void split_combine_kernel(const AttnParams p)
   const int hg = (int)(L % ngroups);
   const int64_t bt = L / ngroups;
   const int t = (int)(bt % p.T), b = (int)(bt / p.T);
-  const int tid = threadIdx.x, hh = tid >> 6, dq = (tid & 63) * 8;
+  // (lane l: dims 4l .. 4l + 3 and 256 + 4l .. 256 + 4l + 3, so that adjacent
+  // lanes read and write adjacent 16 bytes)
+  const int tid = threadIdx.x, hh = tid >> 6, dq = (tid & 63) * 4;
   const int ns = p.nsplit;
   const char *rec0 = p.ws + L * ns * kSplitRecord;
   for (int e = tid; e < 32 * ns; e += 1024) {   // e = part * 32 + (0..15 maxima, 16..31 sums)
@@ -1704,7 +1687,7 @@ __global__ __launch_bounds__(1024) void split_combine_kernel(const AttnParams p)
         if (s0 + u < ns) {
           const floatx4 *src = (const floatx4 *)((const float *)(rec0 + (s0 + u) * kSplitRecord) + hh * 512 + dq);
           v0[u] = src[0];
-          v1[u] = src[1];
+          v1[u] = src[64];
         }
       }
 #pragma unroll
@@ -1722,7 +1705,7 @@ __global__ __launch_bounds__(1024) void split_combine_kernel(const AttnParams p)
   const float inv = lsum > 0.f ? 1.f / lsum : 0.f;
   float *ob = (float *)(p.o + b * p.o_sb + t * p.o_st + (int64_t)(hg * 16 + hh) * p.o_sh) + dq;
   *(floatx4 *)ob = acc0 * inv;
-  *(floatx4 *)(ob + 4) = acc1 * inv;
+  *(floatx4 *)(ob + 256) = acc1 * inv;
 }
 
 hipError_t launch_attn_decode_split(const AttnParams &p, hipStream_t s) {
