@@ -123,6 +123,13 @@ void attn_staged_kernel(const AttnParams p) {
   // waves' waits for their own loads (Q, the map row, validity bytes) wait for
   // nothing else.
   constexpr bool SPLITKV = DIMS;
+  // List entries whose transfers start before the map row is read (guessed).  The
+  // float16 producers guess only the first: the prologue's barriers (block list,
+  // masks) would otherwise wait while they issue a second block, and with every CU
+  // busy the vector-memory path takes about 1 us per block.  They stage the second
+  // once the list is known (see the producers' prologue).
+  constexpr int kGuessed = SPLITKV && !FP8 ? 1 : NBUF;
+  constexpr int kLateVMaxEntries = 5;   // see the producers' prologue
   constexpr int KPD = KEYS ? 4 : 2;   // K operand reads in flight (k-steps)
   // FP8 V rows are multiplied by half their row scale in float16, so that a row
   // whose values reach the float16 maximum cannot overflow when its scale is
@@ -551,7 +558,7 @@ void attn_staged_kernel(const AttnParams p) {
   }
   if (!KEYS && (!SPLITKV || producer)) {
     for_bufs([&](auto E) {
-      if (spec(E) >= 0) {
+      if (E < kGuessed && spec(E) >= 0) {
         if constexpr (SPLITKV && !FP8) {
           // (K rows first: an entry's K rows are published before its V rows)
           stage_rows(spec(E), 0xffffffffu, E, KPart{});
@@ -633,7 +640,7 @@ void attn_staged_kernel(const AttnParams p) {
       int j = -1, st;
       if (e1 > e0 + E) entry_at(e0 + E, j, st);
       j = __builtin_amdgcn_readfirstlane(j);
-      hit[E] = e1 <= e0 + E || j == spec(E);
+      hit[E] = e1 <= e0 + E || E >= kGuessed || j == spec(E);
       all = all && hit[E];
     });
     if (!all) {
@@ -654,6 +661,9 @@ void attn_staged_kernel(const AttnParams p) {
   // (nor one for registers their loads would write) lands in this path.
   if constexpr (SPLITKV) {
     if (producer) {
+      // (float16: whether entry e0 + 1's V rows are staged late, and masked; set in
+      // the prologue below)
+      bool v_late = false;
       // An entry's K rows are published by the barrier that ends the entry before
       // it, its V rows (needed only from P.V on) by its own score exchange.  In
       // issue order: K rows of entry nx after the exchange of entry i, its V rows
@@ -661,11 +671,11 @@ void attn_staged_kernel(const AttnParams p) {
       auto produce16 = [&](int i, auto buf) __attribute__((always_inline)) {
         const int nx = i + NBUF;
         // entry i's V rows landed: only entry i + 1's transfers may be in flight;
-        // the first two entries were staged unmasked, as guessed: clear their
-        // hidden V rows
+        // entry e0 (guessed) and, unless staged masked, entry e0 + 1 arrived
+        // unmasked: clear their hidden V rows
         if (i + 1 < e1) wait_vmcnt<2 * RPW>();
         else wait_vmcnt<0>();
-        if (i <= e0 + 1) clear_masked(i, buf);
+        if (i == e0 || (i == e0 + 1 && !v_late)) clear_masked(i, buf);
         lds_barrier();   // score exchange of entry i: its V rows ready, K tile B free
         if (nx < e1 && (nx & (kMaskChunk - 1)) == 0) lds_barrier();   // masks of entries nx..
         if (nx < e1) stage(nx, buf, Masked{}, KPart{});
@@ -706,6 +716,22 @@ void attn_staged_kernel(const AttnParams p) {
       ndense = nd_s;
       part_bounds(ndense);
       const bool redo = check_guesses();
+      // Float16: entry e0 + 1, now known.  Its K rows go at once (unmasked; the
+      // mask hides them in the scores).  Its V rows go now too (unmasked, cleared
+      // once landed), except for a short list (a window's blocks) with every CU
+      // busy: there the prologue is a large part of the chain, and they go (masked)
+      // after entry e0's barrier, so that the barriers before it do not wait for
+      // them to be issued.  (Measured, 64 sequences: a 4-block window 10.6 -> 10.0
+      // us with the late V rows; 12-block lists 20.3 us with early, 20.6 with late
+      // V rows; a single sequence split in 48 workgroups 11.8 early, 12.0 late.)
+      const bool second = !FP8 && e0 + 1 < e1;
+      v_late = gridDim.x >= (uint32_t)kNumCus && e1 - e0 <= kLateVMaxEntries;
+      if constexpr (!FP8) {
+        if (second) {
+          stage(e0 + 1, std::integral_constant<int, 1>{}, Unmasked{}, KPart{});
+          if (!v_late) stage(e0 + 1, std::integral_constant<int, 1>{}, Unmasked{}, VPart{});
+        }
+      }
       lds_barrier();   // masks visible
       if constexpr (FP8) {
         // entry e0 landed: only the guessed entries after it may be in flight (after
@@ -718,13 +744,20 @@ void attn_staged_kernel(const AttnParams p) {
         clear_masked(e0, std::integral_constant<int, 0>{});
         lds_barrier();   // entry e0 ready
       } else {
-        // entry e0's K rows landed: only its V rows and entry e0 + 1's guessed
-        // transfers may be in flight (after a redo the order is not known: wait for
-        // everything)
-        if (redo) wait_vmcnt<0>();
-        else if (spec(1) >= 0) wait_vmcnt<3 * RPW>();
-        else wait_vmcnt<RPW>();
+        // entry e0's K rows landed: only its V rows (after a redo, which stages the
+        // entry whole: none of its rows) and entry e0 + 1's rows may be in flight
+        const int later = second ? (v_late ? RPW : 2 * RPW) : 0;   // e0 + 1's transfers
+        if (redo) {
+          if (later == 2 * RPW) wait_vmcnt<2 * RPW>();
+          else if (later == RPW) wait_vmcnt<RPW>();
+          else wait_vmcnt<0>();
+        } else {
+          if (later == 2 * RPW) wait_vmcnt<3 * RPW>();
+          else if (later == RPW) wait_vmcnt<2 * RPW>();
+          else wait_vmcnt<RPW>();
+        }
         lds_barrier();   // entry e0's K rows ready
+        if (second && v_late) stage(e0 + 1, std::integral_constant<int, 1>{}, Masked{}, VPart{});
       }
       for (int i = e0; i < e1; i += NBUF) {
         for_bufs([&](auto E) {
@@ -779,14 +812,22 @@ void attn_staged_kernel(const AttnParams p) {
   // conditional load makes the compiler wait for everything in flight)
   const int tv0 = (KEYS || p.valid0) ? buf_load_u8(rb0, toff0) : 0;
   const int tv1 = (KEYS || p.valid1) ? buf_load_u8(rb1, toff1) : 0;
-  // KEYS: the first 512 index entries into registers before the rows are loaded
+  // The first 512 index entries into registers before Q and the rows are loaded
+  // (loads complete in order: waiting for these then waits for nothing behind them)
   int ia = -1, ib = -1;
-  if (KEYS && INDEXED) {
+  if (INDEXED) {
     const rsrc_t ri = make_rsrc(p.idx + ((int64_t)b * p.T + t) * p.r1_k, 4u * (uint32_t)p.r1_k);
     const int va = (int)__builtin_amdgcn_raw_buffer_load_b32(ri, 4u * tid, 0, 0);
     const int vb = (int)__builtin_amdgcn_raw_buffer_load_b32(ri, 4u * (tid + 256), 0, 0);
     ia = tid < p.r1_k ? va : -1;
     ib = tid + 256 < p.r1_k ? vb : -1;
+  }
+
+  // The computing waves' map row (its first 256 entries), for the same reason
+  // (KEYS loaded it before its rows)
+  if constexpr (!KEYS) {
+    const int sraw = buf_load_u8(make_rsrc(blkrow, blkrow ? (uint32_t)p.nbd : 0u), (uint32_t)tid);
+    s_first = tid < p.nbd ? (blkrow ? sraw : kPartial) : 0;
   }
 
   // Q^T operand fragments: head h, dims d0 + 32ks + 8g .. +7
@@ -830,13 +871,9 @@ void attn_staged_kernel(const AttnParams p) {
     // that lie past r1_k read as unused (-1)
     const int32_t *src = p.idx + ((int64_t)b * p.T + t) * p.r1_k;
     const int padded = p.nb1 * kRowsPerBlock;
-    if constexpr (KEYS) {
-      if (tid < padded) idx_s[tid] = ia;
-      if (tid + 256 < padded) idx_s[tid + 256] = ib;
-      for (int e = tid + 512; e < padded; e += 256) idx_s[e] = e < p.r1_k ? src[e] : -1;
-    } else {
-      for (int e = tid; e < padded; e += 256) idx_s[e] = e < p.r1_k ? src[e] : -1;
-    }
+    if (tid < padded) idx_s[tid] = ia;
+    if (tid + 256 < padded) idx_s[tid + 256] = ib;
+    for (int e = tid + 512; e < padded; e += 256) idx_s[e] = e < p.r1_k ? src[e] : -1;
   }
   ndense = build_block_list<256>(blkrow, p.nbd, blist, cnt, s_first);   // ends with a barrier
   {

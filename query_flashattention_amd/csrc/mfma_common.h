@@ -70,11 +70,15 @@ constexpr float kRescaleSlack = 8.f;
 // entry = block | status << 14, in block order.  A null map lists every block as
 // PARTIAL.  All threads of the workgroup must call it; it always ends with a barrier.
 // `cnt` is LDS scratch of NT/64 ints.  `s_first` >= 0 is the status of block
-// `threadIdx.x` already loaded by the caller (0 past the end of the row).
+// `threadIdx.x` already loaded by the caller (0 past the end of the row).  The
+// barriers order LDS only (lgkmcnt, then s_barrier): a full __syncthreads would
+// also wait for every global load in flight, such as the query rows loaded after
+// the map row.
 template <int NT>
 __device__ __forceinline__ int build_block_list(const uint8_t *row, int nbd, uint16_t *list, int *cnt,
                                                 int s_first = -1) {
   constexpr int NW = NT / 64;
+  auto barrier = [] { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); };
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   int total = 0;
   for (int base = 0; base < nbd; base += NT) {
@@ -84,7 +88,7 @@ __device__ __forceinline__ int build_block_list(const uint8_t *row, int nbd, uin
     else if (j < nbd) s = row ? (int)row[j] : kPartial;
     const unsigned long long m = __ballot(s != 0);
     if (lane == 0) cnt[wv] = __popcll(m);
-    __syncthreads();
+    barrier();
     int off = total, sum = 0;
 #pragma unroll
     for (int k = 0; k < NW; ++k) {
@@ -97,9 +101,9 @@ __device__ __forceinline__ int build_block_list(const uint8_t *row, int nbd, uin
       list[off + rank] = (uint16_t)(j | (s << 14));
     }
     total += sum;
-    __syncthreads();
+    barrier();
   }
-  __syncthreads();  // also orders any LDS staging done before the call when the map is empty
+  barrier();  // also orders any LDS writes made before the call when the map is empty
   return total;
 }
 
