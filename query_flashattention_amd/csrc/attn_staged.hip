@@ -529,9 +529,10 @@ void attn_staged_kernel(const AttnParams p) {
   using Set0 = std::integral_constant<int, 0>;
   using Set1 = std::integral_constant<int, 1>;
 
-  // The first NBUF list entries are guessed before the map row arrives, and their
-  // transfers start at once: without a map (or for the token's own tile) the list
-  // starts at the first block the window reaches.  A wrong guess is redone below.
+  // The first kGuessed list entries are guessed before the map row arrives, and
+  // their transfers start at once: without a map (or for the token's own tile) the
+  // list starts at the first block the window reaches.  A wrong guess is redone
+  // below.
   int jlo = 0;
   if (p.blk && p.window > 0) {
     const int64_t lo = p.qk_delta + (int64_t)tile * p.bq - p.window + 1;   // tile's first row
@@ -704,7 +705,7 @@ void attn_staged_kernel(const AttnParams p) {
           if (later >= 2) wait_vmcnt<2 * kF8StageOps>();
           else if (later == 1) wait_vmcnt<kF8StageOps>();
           else wait_vmcnt<0>();
-          // (the first NBUF entries were staged unmasked, as guessed)
+          // (the first NBUF entries were staged unmasked, as guessed: FP8 guesses all)
           if (i + 1 < e0 + NBUF) clear_masked(i + 1, std::integral_constant<int, (B + 1) % NBUF>{});
           lds_barrier();   // end of entry i: entry i + 1 ready, buffer B free
           if (nx < e1) stage(nx, buf, Masked{}, BothParts{});
