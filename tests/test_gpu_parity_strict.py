@@ -221,11 +221,11 @@ def test_onehot_prefill_chunks():
 
 # --------------------------------------------------------------------------- wrong speculative starts
 
-def _window_then_dense(tokens, heads):
+def _window_then_dense(tokens, heads, batch=2):
     """Raw rows 0..199 with a 16-row window that ends in raw block 3 for every
     token, then 100 dense compressed rows: the lists are [3, 7, 8, 9, 10] while
     the window arithmetic guesses 3, 4, 5, ... (block 4 onward is skipped)."""
-    return wl.random_problem(121, batch=2, tokens=tokens, heads=heads, head_dim=512, n0=200, window=16,
+    return wl.random_problem(121, batch=batch, tokens=tokens, heads=heads, head_dim=512, n0=200, window=16,
                              q_pos0=111, k_pos0=0, n1=100, r1_mode="all")
 
 
@@ -239,10 +239,10 @@ def _leading_invalid(tokens, heads, r1=False):
     return w
 
 
-def _first_block_invalid(tokens, heads):
+def _first_block_invalid(tokens, heads, batch=2):
     """The window case with raw block 3 invalid: no raw row is visible, so a tile's
     list starts in region 1 while HEADS prefill guesses block 3."""
-    w = _window_then_dense(tokens, heads)
+    w = _window_then_dense(tokens, heads, batch)
     valid = torch.ones(w.r0.k.shape[:2], dtype=torch.uint8)
     valid[:, 96:128] = 0
     return dataclasses.replace(w, r0=dataclasses.replace(w.r0, valid=valid))
@@ -271,6 +271,22 @@ def test_wrong_speculative_start(label, make, mode, fp8):
     assert n > 0
     want = _oracle(w)
     compare(_run(w, mode), want, f"{label}/{mode}/{'fp8' if fp8 else 'f16'} ({n} NaN rows)")
+
+
+@pytest.mark.parametrize("fp8", [False, True], ids=["f16", "fp8"])
+@pytest.mark.parametrize("label,make", [("window_then_dense", _window_then_dense),
+                                        ("first_block_invalid", _first_block_invalid)])
+def test_speculative_start_full_grid(label, make, fp8):
+    """64 sequences x 4 head groups: 256 DIMS workgroups, as many as the chip has
+    CUs.  With lists this short (5 and 4 entries) the float16 producers stage the
+    second entry's V rows late and masked; the second case also stages the first
+    entry again (its guess is wrong)."""
+    w = make(1, 64, batch=64)
+    if fp8:
+        w = wl.fp8_variant(w, 126)
+    w, n = poison_hidden(w)
+    assert n > 0
+    compare(_run(w, "dims"), _oracle(w), f"{label}/full grid/{'fp8' if fp8 else 'f16'} ({n} NaN rows)")
 
 
 def test_split_parts_with_wrong_guesses():
