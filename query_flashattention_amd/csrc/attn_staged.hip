@@ -724,7 +724,7 @@ void attn_staged_kernel(const AttnParams p) {
       // after entry e0's barrier, so that the barriers before it do not wait for
       // them to be issued.  (Measured, 64 sequences: a 4-block window 10.6 -> 10.0
       // us with the late V rows; 12-block lists 20.3 us with early, 20.6 with late
-      // V rows; a single sequence split in 48 workgroups 11.8 early, 12.0 late.)
+      // V rows; a single sequence split in 16 workgroups 11.8 early, 12.0 late.)
       const bool second = !FP8 && e0 + 1 < e1;
       v_late = gridDim.x >= (uint32_t)kNumCus && e1 - e0 <= kLateVMaxEntries;
       if constexpr (!FP8) {
