@@ -673,8 +673,8 @@ def main():
             del r
             torch.cuda.empty_cache()
         # one sequence of the ratio-128 layer (12 key blocks) without the split that
-        # ds4attn_decode picks for it (the decode_r128 line above: 4 parts per head
-        # group plus the combine pass)
+        # ds4attn_decode picks for it (the decode_r128 line above: the planned parts
+        # per head group plus the combine pass)
         r, s_, k = run_workload("decode_r128", 200, 3, 64, 100, splits=1)
         extra["decode_r128_unsplit"] = {"ms_per_step": round(s_ * 1e3 / 200, 5),
                                          "kernel_ms_mean": round(k["mean"], 5),

@@ -168,16 +168,22 @@ int resolve_args(const ds4attn_args *a, bool prefill, Resolved &R) {
 // Dive", Whole-Model Graph Execution: the attention path is chosen by layer type
 // and batch size).  A decode workgroup covers one token's 16 heads; a batch with
 // fewer than 128 such groups leaves most of the 256 CUs idle, so each token's
-// block list is divided over up to 256 / groups workgroups, about three key
-// blocks per part (measured: one sequence of the ratio-128 layer at 32K, 12
-// blocks, runs fastest in 4 parts; 64-sequence batches only lose from splitting).
+// block list is divided over up to 256 / groups workgroups, two key blocks per
+// part and at most 10 parts; lists of up to 5 blocks stay whole (the combine pass
+// costs more than the split saves).  Measured on one sequence (µs, parts in
+// brackets): a 4-block window 7.9 [1], 9.4 [2]; 8 dense blocks 11.8 [2], 10.4 [4];
+// 12 blocks of the ratio-128 layer 12.4 [3], 11.7 [4], 11.7 [6], 13.3 [12]; 16
+// dense blocks 12.6 [4], 11.9 [8], 13.1 [11]; the ratio-4 layer's 20 blocks 15.5
+// [6], 13.9 [10], 14.7 [12]; 32 dense blocks 14.1 [8], 14.3 [11], 14.7 [16].
+// 64-sequence batches only lose from splitting.
 int plan_splits(const Resolved &R, bool prefill) {
   // (a chosen wide split has no split parts)
   if (prefill || R.empty || !R.mfma || R.P.decode_split == 3) return 1;
   const AttnParams &P = R.P;
   const int64_t groups = (int64_t)P.B * P.T * (P.H / 16);
   if (groups >= 128) return 1;
-  const int64_t by_len = list_bound(P) / 3;
+  const int64_t lb = list_bound(P);
+  const int64_t by_len = lb <= 5 ? 1 : std::min<int64_t>(lb / 2, 10);
   const int64_t by_cus = 256 / groups;
   return (int)std::max<int64_t>(1, std::min<int64_t>({(int64_t)kMaxSplits, by_len, by_cus}));
 }

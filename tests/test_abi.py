@@ -440,10 +440,11 @@ def _ratio128_args(batch=1):
 
 def test_workspace_plan():
     """The library splits a decode batch that leaves most CUs idle: one sequence of
-    the ratio-128 layer (4 groups of 16 heads, 12 key blocks) in 4 parts; a
-    64-sequence batch, prefill and the vector-ALU kernel run unsplit."""
+    the ratio-128 layer (4 groups of 16 heads, 12 key blocks) in 6 parts of two
+    blocks; a 64-sequence batch, prefill, short lists and the vector-ALU kernel
+    run unsplit."""
     rec = 16 * 512 * 4 + 128
-    assert da.ds4attn_workspace_bytes(_ratio128_args(), False) == 4 * 4 * rec
+    assert da.ds4attn_workspace_bytes(_ratio128_args(), False) == 4 * 6 * rec
     assert da.ds4attn_workspace_bytes(_ratio128_args(64), False) == 0
     assert da.ds4attn_workspace_bytes(_ratio128_args(), True) == 0
     assert da.ds4attn_workspace_bytes(_good_args(), False) == 0               # 4 blocks: too short to split
@@ -454,7 +455,10 @@ def test_workspace_plan():
     w = _ratio128_args()
     w.window = 128
     w.r0.n_rows = 4096                      # 128-row window: at most 6 blocks reachable + 8
-    assert da.ds4attn_workspace_bytes(w, False) == 4 * 4 * rec
+    assert da.ds4attn_workspace_bytes(w, False) == 4 * 7 * rec
+    long = _ratio128_args()
+    long.r0.n_rows = 4096                   # no window: 128 + 8 blocks, at most 10 parts
+    assert da.ds4attn_workspace_bytes(long, False) == 4 * 10 * rec
     e = _ratio128_args()
     e.batch = 0
     assert da.ds4attn_workspace_bytes(e, False) == 0

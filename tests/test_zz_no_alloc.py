@@ -59,12 +59,12 @@ def _need_gpu():
 def test_noalloc_matches_decode_two_calls_in_a_row():
     big = wl.named("decode_r128")
     got, want, rec = _both(big)
-    assert rec == 16                        # 4 groups of 16 heads x 4 parts
+    assert rec == 24                        # 4 groups of 16 heads x 6 parts
     assert torch.equal(got, want)
     compare(got.double().numpy(), ref.attention(ref.from_workload(big)), "noalloc decode_r128")
     small = _small_split_case()
     got, want, rec = _both(small)
-    assert rec == 2                         # 1 group x 2 parts: a smaller input in the same array
+    assert rec == 3                         # 1 group x 3 parts: a smaller input in the same array
     assert torch.equal(got, want)
     compare(got.double().numpy(), ref.attention(ref.from_workload(small)), "noalloc small split")
 
