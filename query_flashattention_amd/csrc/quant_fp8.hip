@@ -3,9 +3,9 @@
 // Whole-Model Graph Execution, where an FP8 KV quantize step precedes the raw KV
 // store; the element format and the per-row scale are this library's reading).
 //
-// One wave per row, E = D/64 consecutive elements per lane.  In float32: amax by a
-// wave reduction, scale = amax / 448, each element x / scale clamped to +-448 and
-// rounded to the nearest E4M3 value, ties to even.  The rounding is done on the
+// Each wave takes four rows, E = D/64 consecutive elements per lane.  In float32:
+// amax by a wave reduction, scale = amax / 448, each element x / scale clamped to
+// +-448 and rounded to the nearest E4M3 value, ties to even.  The rounding is done on the
 // float32 bits (below 2^-6 the values are multiples of 2^-9, so a scaled
 // round-to-nearest-even gives the code directly; above, the top three mantissa
 // bits are kept with a round-to-nearest-even carry into the exponent), so both
@@ -13,7 +13,9 @@
 // row is read once and written once: 2D or 4D bytes in, D + 4 bytes out.
 //
 // [P-DS4] = "DwarfStar 4 (DS4) -- DeepSeek V4 Flash Inference Engine".
-#include "ds4attn_internal.h"
+#include "mfma_common.h"
+
+#include <type_traits>
 
 namespace ds4attn {
 
@@ -38,73 +40,106 @@ __device__ __forceinline__ uint32_t e4m3_code(float y) {
   return sign | mag;
 }
 
-template <int E, bool F32>
+// Maximum over the wave: DPP within rows of 16 lanes (quad swaps, then half-row
+// and row mirrors), then the swaps of rows across the halves.
+__device__ __forceinline__ float wave_max(float x) {
+  auto dpp = [](float v, auto ctrl) __attribute__((always_inline)) {
+    constexpr int C = decltype(ctrl)::value;
+    return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), C, 0xf, 0xf, false));
+  };
+  x = fmaxf(x, dpp(x, std::integral_constant<int, 0xb1>{}));    // quad_perm(1, 0, 3, 2): lane ^ 1
+  x = fmaxf(x, dpp(x, std::integral_constant<int, 0x4e>{}));    // quad_perm(2, 3, 0, 1): lane ^ 2
+  x = fmaxf(x, dpp(x, std::integral_constant<int, 0x141>{}));   // row_half_mirror: the other quad of 8
+  x = fmaxf(x, dpp(x, std::integral_constant<int, 0x140>{}));   // row_mirror: the other half of 16
+  x = xor_max(x, 16);
+  x = xor_max(x, 32);
+  return x;
+}
+
+// R rows per wave: their loads are all issued before the first reduction, so a
+// wave keeps R row reads in flight instead of one.
+template <int E, bool F32, int R>
 __global__ __launch_bounds__(256) void quant_fp8_kernel(const char *__restrict__ x, int n, int64_t x_sb,
                                                         int64_t x_sr, char *__restrict__ codes, int64_t c_sb,
                                                         int64_t c_sr, char *__restrict__ scales,
                                                         int64_t s_sb, int rows) {
   const int lane = threadIdx.x & 63;
-  const int64_t r = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (r >= rows) return;
-  const int b = (int)(r / n), row = (int)(r % n);
-  const char *src = x + b * x_sb + row * x_sr + (int64_t)lane * E * (F32 ? 4 : 2);
-  // the lane's E elements are contiguous and aligned to their size (row starts and
-  // strides are multiples of 16 bytes)
-  float v[E];
-  if constexpr (F32) {
-    float t[E];
-    __builtin_memcpy(t, __builtin_assume_aligned(src, 4 * E < 16 ? 4 * E : 16), 4 * E);
+  // (rows < 2^31: 32-bit index arithmetic)
+  const uint32_t r0 = ((uint32_t)blockIdx.x * 4u + (uint32_t)(threadIdx.x >> 6)) * (uint32_t)R;
+  if (r0 >= (uint32_t)rows) return;   // whole wave exits together
+  float v[R][E];
+  int bs[R], rs[R];
 #pragma unroll
-    for (int i = 0; i < E; ++i) v[i] = t[i];
-  } else {
-    _Float16 t[E];
-    __builtin_memcpy(t, __builtin_assume_aligned(src, 2 * E < 16 ? 2 * E : 16), 2 * E);
+  for (int j = 0; j < R; ++j) {
+    // (a row past the end reads row r0 again and is not stored: the loads stay
+    // unconditional, so that they all go out before the first wait)
+    const uint32_t r = r0 + (uint32_t)j < (uint32_t)rows ? r0 + (uint32_t)j : r0;
+    bs[j] = (int)(r / (uint32_t)n);
+    rs[j] = (int)(r - (uint32_t)bs[j] * (uint32_t)n);
+    // the lane's E elements are contiguous and aligned to their size (row starts
+    // and strides are multiples of 16 bytes)
+    const char *src = x + bs[j] * x_sb + rs[j] * x_sr + (int64_t)lane * E * (F32 ? 4 : 2);
+    if constexpr (F32) {
+      float t[E];
+      __builtin_memcpy(t, __builtin_assume_aligned(src, 4 * E < 16 ? 4 * E : 16), 4 * E);
 #pragma unroll
-    for (int i = 0; i < E; ++i) v[i] = (float)t[i];
-  }
-  float amax = 0.f;
+      for (int i = 0; i < E; ++i) v[j][i] = t[i];
+    } else {
+      _Float16 t[E];
+      __builtin_memcpy(t, __builtin_assume_aligned(src, 2 * E < 16 ? 2 * E : 16), 2 * E);
 #pragma unroll
-  for (int i = 0; i < E; ++i) amax = fmaxf(amax, fabsf(v[i]));
-#pragma unroll
-  for (int off = 32; off > 0; off >>= 1) amax = fmaxf(amax, __shfl_xor(amax, off));
-  const float scale = amax / kE4M3Max;
-  uint8_t c[E];
-#pragma unroll
-  for (int i = 0; i < E; ++i) {
-    uint32_t code = 0;
-    if (scale != 0.f) {
-      const float y = fminf(fmaxf(v[i] / scale, -kE4M3Max), kE4M3Max);   // keeps the sign of zero
-      code = e4m3_code(y);
+      for (int i = 0; i < E; ++i) v[j][i] = (float)t[i];
     }
-    c[i] = (uint8_t)code;
   }
-  char *dst = codes + b * c_sb + row * c_sr + (int64_t)lane * E;
-  if constexpr (E == 8) {
-    uint2 w;
-    w.x = c[0] | (c[1] << 8) | (c[2] << 16) | ((uint32_t)c[3] << 24);
-    w.y = c[4] | (c[5] << 8) | (c[6] << 16) | ((uint32_t)c[7] << 24);
-    *(uint2 *)dst = w;
-  } else if constexpr (E == 4) {
-    *(uint32_t *)dst = c[0] | (c[1] << 8) | (c[2] << 16) | ((uint32_t)c[3] << 24);
-  } else if constexpr (E == 2) {
-    *(uint16_t *)dst = (uint16_t)(c[0] | (c[1] << 8));
-  } else {
-    *(uint8_t *)dst = c[0];
+#pragma unroll
+  for (int j = 0; j < R; ++j) {
+    if (r0 + (uint32_t)j >= (uint32_t)rows) break;
+    float amax = 0.f;
+#pragma unroll
+    for (int i = 0; i < E; ++i) amax = fmaxf(amax, fabsf(v[j][i]));
+    amax = wave_max(amax);
+    const float scale = amax / kE4M3Max;
+    uint8_t c[E];
+#pragma unroll
+    for (int i = 0; i < E; ++i) {
+      uint32_t code = 0;
+      if (scale != 0.f) {
+        const float y = fminf(fmaxf(v[j][i] / scale, -kE4M3Max), kE4M3Max);   // keeps the sign of zero
+        code = e4m3_code(y);
+      }
+      c[i] = (uint8_t)code;
+    }
+    char *dst = codes + bs[j] * c_sb + rs[j] * c_sr + (int64_t)lane * E;
+    if constexpr (E == 8) {
+      uint2 w;
+      w.x = c[0] | (c[1] << 8) | (c[2] << 16) | ((uint32_t)c[3] << 24);
+      w.y = c[4] | (c[5] << 8) | (c[6] << 16) | ((uint32_t)c[7] << 24);
+      *(uint2 *)dst = w;
+    } else if constexpr (E == 4) {
+      *(uint32_t *)dst = c[0] | (c[1] << 8) | (c[2] << 16) | ((uint32_t)c[3] << 24);
+    } else if constexpr (E == 2) {
+      *(uint16_t *)dst = (uint16_t)(c[0] | (c[1] << 8));
+    } else {
+      *(uint8_t *)dst = c[0];
+    }
+    if (lane == 0) *(float *)(scales + bs[j] * s_sb + 4LL * rs[j]) = scale;
   }
-  if (lane == 0) *(float *)(scales + b * s_sb + 4LL * row) = scale;
 }
+
+constexpr int kRowsPerWave = 4;
 
 template <int E>
 hipError_t launch_e(bool f32, const void *x, int B, int n, int64_t x_sb, int64_t x_sr, uint8_t *codes,
                     int64_t c_sb, int64_t c_sr, float *scales, int64_t s_sb, hipStream_t s) {
   const int rows = B * n;
-  const dim3 grid((unsigned)((rows + 3) / 4)), block(256);
+  constexpr int per_block = 4 * kRowsPerWave;
+  const dim3 grid((unsigned)((rows + per_block - 1) / per_block)), block(256);
   if (f32)
-    hipLaunchKernelGGL((quant_fp8_kernel<E, true>), grid, block, 0, s, (const char *)x, n, x_sb, x_sr,
-                       (char *)codes, c_sb, c_sr, (char *)scales, s_sb, rows);
+    hipLaunchKernelGGL((quant_fp8_kernel<E, true, kRowsPerWave>), grid, block, 0, s, (const char *)x, n, x_sb,
+                       x_sr, (char *)codes, c_sb, c_sr, (char *)scales, s_sb, rows);
   else
-    hipLaunchKernelGGL((quant_fp8_kernel<E, false>), grid, block, 0, s, (const char *)x, n, x_sb, x_sr,
-                       (char *)codes, c_sb, c_sr, (char *)scales, s_sb, rows);
+    hipLaunchKernelGGL((quant_fp8_kernel<E, false, kRowsPerWave>), grid, block, 0, s, (const char *)x, n, x_sb,
+                       x_sr, (char *)codes, c_sb, c_sr, (char *)scales, s_sb, rows);
   return hipGetLastError();
 }
 
