@@ -1318,8 +1318,8 @@ void attn_staged_kernel(const AttnParams p) {
     lds_barrier();   // blocks 0 and 1 ready
   }
 
+  // (buffer B below: `buf`, the entry's tile buffer)
   auto iteration = [&](int i, auto buf) __attribute__((always_inline)) {
-    constexpr int B = decltype(buf)::value;
     // ---- S^T = K Q^T over this wave's head dims; operand reads run KPD steps ahead
     // (kDimsWide: t0, t1 for the second head tile, from the same K operands)
     floatx4 s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
