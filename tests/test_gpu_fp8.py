@@ -89,6 +89,9 @@ def _quant_rows(seed, b, n, d, dtype):
         x[0, 4] *= 1e25                                # huge (float32 only)
     if n > 5:
         x[0, 5, ::3] = -0.0                            # signed zeros inside a row
+    if n > 7 and dtype == torch.float32:
+        x[0, 6] *= 1e-28                               # scale below 2^-80 (float32 only)
+        x[0, 7] *= 1e35                                # near the float32 maximum
     return x.to(dtype)
 
 
