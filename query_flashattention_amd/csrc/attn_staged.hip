@@ -81,10 +81,13 @@ __device__ __forceinline__ void store_acc_rows(char *dst, int64_t stride, const 
 }
 
 // FP8 rows (E4M3 codes, a float32 scale per row): the rows travel to LDS as codes
-// (half the bytes), two rows per transfer, and are converted where the operands
-// are read: K codes to float16 (exact), with the row's scale applied to the fp32
-// scores; V codes through an 8-bit transpose read to float16 (exact), times the
-// rows' scales in float16.  P and the accumulators are as for float16 rows.
+// (half the bytes), two rows per transfer.  Scores: in HEADS the K codes go to the
+// E4M3 matrix cores as they are, against Q carried as two E4M3 terms; in DIMS and
+// KEYS they are converted to float16 (exact) where the operands are read.  Either
+// way the K rows' scales multiply the float32 scores.  V codes come through an
+// 8-bit transpose read and are converted to float16 (exact); the V rows' scales
+// are folded into P (DIMS, HEADS) or multiply the converted codes in float16
+// (KEYS).  The accumulators are float32 as for float16 rows.
 // PARTS (decode only): the launch is a split decode; each workgroup takes one part
 // of its token's block list and leaves a record for the combine pass.
 template <int MODE, bool INDEXED, bool FP8, bool PARTS = false>
@@ -131,11 +134,24 @@ void attn_staged_kernel(const AttnParams p) {
   constexpr int kGuessed = SPLITKV && !FP8 ? 1 : NBUF;
   constexpr int kLateVMaxEntries = 5;   // see the producers' prologue
   constexpr int KPD = KEYS ? 4 : 2;   // K operand reads in flight (k-steps)
-  // FP8 V rows are multiplied by half their row scale in float16, so that a row
+  // FP8 rows outside KEYS: the V rows' scales are folded into P (P'[h, r] = P[h, r]
+  // sv[r], one float16 rounding; P <= 2^8 by the rescale slack and sv <= 65504 /
+  // 448, so P' < 2^16 stays finite), and V codes enter P.V as they are.  The sums
+  // l take P itself.
+  constexpr bool FOLDV = FP8 && !KEYS;
+  // FP8 HEADS: the scores run on the E4M3 matrix cores, K codes against Q carried
+  // as two E4M3 terms (split_e4m3) with a power-of-two factor per head; the K rows'
+  // scales then multiply the scores with the softmax scale.  No K code is
+  // converted.  (The same in DIMS, where each wave's 128 dims are one chunk with a
+  // factor of their own, measured no faster than converting: decode_swa 10.6-10.7
+  // us either way.)
+  constexpr bool F8S = FP8 && MODE == kSplitHeads;
+  constexpr int NQC = DIMS ? 1 : 4;   // F8S: 128-dim chunks per wave
+  // KEYS FP8 V rows are multiplied by half their row scale in float16, so that a row
   // whose values reach the float16 maximum cannot overflow when its scale is
   // rounded to float16 (448 * fp16(65504 / 448) rounds to inf, 224 * fp16(32752 /
   // 448) does not); the output (or a split part's record) gets the factor 2 back.
-  constexpr float kOut = FP8 ? 2.f : 1.f;
+  constexpr float kOut = FP8 && !FOLDV ? 2.f : 1.f;
   // V operand reads in flight (output tiles); FP8 rows in HEADS take one fewer,
   // which keeps their conversions within 256 registers without spilling
   constexpr int VPD = KEYS ? 8 : (MODE == kSplitHeads && FP8 ? 3 : 4);
@@ -831,8 +847,11 @@ void attn_staged_kernel(const AttnParams p) {
     s_first = tid < p.nbd ? (blkrow ? sraw : kPartial) : 0;
   }
 
-  // Q^T operand fragments: head h, dims d0 + 32ks + 8g .. +7
-  half8 qf[NKS];
+  // Q^T operand fragments: head h, dims d0 + 32ks + 8g .. +7 (F8S: the two E4M3
+  // terms of head h, dims 128c + 32g .. +31 in chunk c, and the head's factor)
+  half8 qf[F8S ? 1 : NKS];
+  int8v qhi[NQC], qlo[NQC];
+  float qsc = 1.f;
   half8 qf2[HT == 2 ? NKS : 1];   // kDimsWide: Q^T fragments of heads h + 16
   u32x4 qst[KEYS ? 4 : 1];
   if constexpr (KEYS) {
@@ -859,8 +878,30 @@ void attn_staged_kernel(const AttnParams p) {
     }
   } else {
     const char *qrow = p.q + b * p.q_sb + t * p.q_st + (int64_t)h * p.q_sh;
+    if constexpr (F8S) {
+      half8 qv[NQC][4];
 #pragma unroll
-    for (int ks = 0; ks < NKS; ++ks) qf[ks] = *(const half8 *)(qrow + 2 * (d0 + 32 * ks + 8 * g));
+      for (int c = 0; c < NQC; ++c)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) qv[c][j] = *(const half8 *)(qrow + 2 * (d0 + 128 * c + 32 * g + 8 * j));
+      // max |q| over the head's dims of this wave: this lane's elements, then the
+      // head's four lanes
+      half2v mx = {(_Float16)0.f, (_Float16)0.f};
+#pragma unroll
+      for (int c = 0; c < NQC; ++c)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+#pragma unroll
+          for (int e = 0; e < 8; e += 2)
+            mx = __builtin_elementwise_max(mx, __builtin_elementwise_abs(half2v{qv[c][j][e], qv[c][j][e + 1]}));
+      float amax = fmaxf((float)mx[0], (float)mx[1]);
+      amax = xor_max(amax, 16);
+      amax = xor_max(amax, 32);
+      qsc = split_e4m3(qv, amax, qhi, qlo);
+    } else {
+#pragma unroll
+      for (int ks = 0; ks < NKS; ++ks) qf[ks] = *(const half8 *)(qrow + 2 * (d0 + 32 * ks + 8 * g));
+    }
     if constexpr (HT == 2) {
       const char *qrow2 = qrow + 16 * p.q_sh;
 #pragma unroll
@@ -1325,7 +1366,37 @@ void attn_staged_kernel(const AttnParams p) {
     floatx4 s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
     floatx4 t0 = {0.f, 0.f, 0.f, 0.f}, t1 = {0.f, 0.f, 0.f, 0.f};
     const char *ktc = ktile(buf), *vtc = vtile(buf);
-    if constexpr (FP8) {
+    if constexpr (F8S) {
+      // rows c16 and 16 + c16, dims 128c + 32g .. +31: 32 codes per operand; each K
+      // operand meets the two Q terms (lo weighted 2^-4 by the B-side scale)
+      const char *krow0 = ktc + f8_row_off(c16) + d0 + 32 * g;
+      const char *krow1 = ktc + f8_row_off(16 + c16) + d0 + 32 * g;
+      auto kload = [&](const char *row, int c) __attribute__((always_inline)) -> int8v {
+        const uint4 x = *(const uint4 *)(row + 128 * c), y = *(const uint4 *)(row + 128 * c + 16);
+        return int8v{(int)x.x, (int)x.y, (int)x.z, (int)x.w, (int)y.x, (int)y.y, (int)y.z, (int)y.w};
+      };
+      constexpr int KP8 = 1;   // chunks of K operands read ahead
+      int8v ka[KP8], kb[KP8];
+#pragma unroll
+      for (int u = 0; u < KP8; ++u) {
+        ka[u] = kload(krow0, u);
+        kb[u] = kload(krow1, u);
+      }
+#pragma unroll
+      for (int c = 0; c < NQC; ++c) {
+        s0 = mfma_e4m3<127>(ka[c % KP8], qhi[c], s0);
+        s1 = mfma_e4m3<127>(kb[c % KP8], qhi[c], s1);
+        s0 = mfma_e4m3<123>(ka[c % KP8], qlo[c], s0);
+        s1 = mfma_e4m3<123>(kb[c % KP8], qlo[c], s1);
+        if (c + KP8 < NQC) {
+          ka[c % KP8] = kload(krow0, c + KP8);
+          kb[c % KP8] = kload(krow1, c + KP8);
+        }
+        __builtin_amdgcn_sched_barrier(0);   // keep this order: MFMAs, then the reads they free
+      }
+      s0 *= qsc;   // the Q terms' factor
+      s1 *= qsc;
+    } else if constexpr (FP8) {
       // rows c16 and 16 + c16, dims d0 + 32ks + 8g .. +7: 8 codes
       const char *krow0 = ktc + f8_row_off(c16) + d0 + 8 * g;
       const char *krow1 = ktc + f8_row_off(16 + c16) + d0 + 8 * g;
@@ -1427,6 +1498,15 @@ void attn_staged_kernel(const AttnParams p) {
 #pragma unroll
       for (int i2 = 0; i2 < 8; ++i2) kq[i2] = p.scale_log2;
     }
+    // FOLDV: the V rows' scales of the same slot rows (V at [16w' + 8 + q])
+    float vr[FOLDV ? 8 : 1];
+    if constexpr (FOLDV) {
+      const float *sc = stile(buf);
+      const float4 vlo = *(const float4 *)(sc + 16 * g + 8);
+      const float4 vhi = *(const float4 *)(sc + 16 * (g ^ 2) + 12);
+      vr[0] = vlo.x; vr[1] = vlo.y; vr[2] = vlo.z; vr[3] = vlo.w;
+      vr[4] = vhi.x; vr[5] = vhi.y; vr[6] = vhi.z; vr[7] = vhi.w;
+    }
     const uint32_t vis = __builtin_amdgcn_readfirstlane(vmask[i & (kMaskRing - 1)]);
     const uint32_t sm = slot_mask(vis, g);
     auto softmax = [&](const floatx4 &a0, const floatx4 &a1, float &mm, float &ll, floatx4 *oo)
@@ -1455,9 +1535,15 @@ void attn_staged_kernel(const AttnParams p) {
       float psum = 0.f;
 #pragma unroll
       for (int i2 = 0; i2 < 8; ++i2) {
-        const _Float16 ph = (_Float16)__builtin_amdgcn_exp2f(sv[i2] - msafe);
-        pp[i2] = ph;
-        psum += (float)ph;
+        if constexpr (FOLDV) {
+          const float e = __builtin_amdgcn_exp2f(sv[i2] - msafe);
+          pp[i2] = (_Float16)(e * vr[i2]);
+          psum += e;
+        } else {
+          const _Float16 ph = (_Float16)__builtin_amdgcn_exp2f(sv[i2] - msafe);
+          pp[i2] = ph;
+          psum += (float)ph;
+        }
       }
       ll = alpha * ll + psum;
       mm = mref;
@@ -1481,13 +1567,7 @@ void attn_staged_kernel(const AttnParams p) {
       const int trow = trk < 4 ? 4 * g + trk : 16 + 4 * g + (trk - 4);
       const lds_char *vsrc = (const lds_char *)(__attribute__((address_space(3))) const void *)vtc +
                              f8_row_off(trow) + d0 + 8 * (lane & 1);
-      // half the V row scales of the slot rows, in float16 (see kOut)
-      const float *sc = stile(buf);
-      const float4 vlo = *(const float4 *)(sc + 16 * g + 8);
-      const float4 vhi = *(const float4 *)(sc + 16 * (g ^ 2) + 12);
-      const half8 vsc = {(_Float16)(0.5f * vlo.x), (_Float16)(0.5f * vlo.y), (_Float16)(0.5f * vlo.z),
-                         (_Float16)(0.5f * vlo.w), (_Float16)(0.5f * vhi.x), (_Float16)(0.5f * vhi.y),
-                         (_Float16)(0.5f * vhi.z), (_Float16)(0.5f * vhi.w)};
+      // (the V rows' scales are in P: FOLDV)
       auto vload = [&](int dt) __attribute__((always_inline)) -> uint2 {
         const int2v r = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
             (__attribute__((address_space(3))) int2v *)(vsrc + 16 * dt));
@@ -1498,7 +1578,7 @@ void attn_staged_kernel(const AttnParams p) {
       for (int u = 0; u < VPD; ++u) vq[u] = vload(u);
 #pragma unroll
       for (int dt = 0; dt < NDT; ++dt) {
-        const half8 vop = e4m3x8_to_half8(vq[dt % VPD]) * vsc;
+        const half8 vop = e4m3x8_to_half8(vq[dt % VPD]);
         o[dt] = mfma16(vop, pf, o[dt]);
         if constexpr (HT == 2) o2[dt] = mfma16(vop, pf2, o2[dt]);
         if (dt + VPD < NDT) vq[dt % VPD] = vload(dt + VPD);

@@ -25,6 +25,55 @@ __device__ __forceinline__ half8 e4m3x8_to_half8(uint2 w) {
   return __builtin_shufflevector(ab, cd, 0, 1, 2, 3, 4, 5, 6, 7);
 }
 
+// E4M3 x E4M3 products on the matrix cores (v_mfma_scale_f32_16x16x128_f8f6f4):
+// operand lane l holds row (column) l % 16 and 32 codes of the 128-long k range;
+// A and B pair their codes by lane group and byte, so any k order both operands
+// share gives the same sums (the hardware takes bytes 0-15 of group G as k = 16G..
+// and bytes 16-31 as k = 64 + 16G..).  Both operands are scaled by 2^(SB - 127) on
+// the B side only (uniform E8M0 scale, byte 0 of the scale register).
+typedef int int8v __attribute__((ext_vector_type(8)));
+template <int SB>
+__device__ __forceinline__ floatx4 mfma_e4m3(const int8v &a, const int8v &b, const floatx4 &c) {
+  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 0, 0, 0, 127, 0, SB);
+}
+
+// A float16 query row as two E4M3 terms for those matrix cores: with s = 2^(E - 7),
+// where 2^(E - 1) <= max |q| < 2^E over the head (E at least -8), hi = RN(q / s) and
+// lo = RN((q - s hi) / (s / 16)), so that q = s (hi + lo / 16) to within 2^-8 |q|
+// or 2^-14 s, whichever is larger (s <= 2^-6 max |q|).  Every term stays below 128
+// (the E4M3 encoding has no saturation: beyond 448 it gives NaN), and s hi is
+// exact in float16 for E >= -8, so the residual is exact too.  `q` holds this
+// lane's NC x 32 elements (chunk c, elements 8j .. 8j + 7 in q[c][j]); element e
+// of a chunk goes to byte e of the chunk's 32-byte operand.  `amax` is the max |q|
+// over every element the factor covers (all lanes concerned agree).  Returns s.
+template <int NC>
+__device__ __forceinline__ float split_e4m3(const half8 (&q)[NC][4], float amax, int8v (&hi)[NC],
+                                            int8v (&lo)[NC]) {
+  typedef short short2_t __attribute__((ext_vector_type(2)));
+  int e = (int)(__float_as_uint(amax) >> 23) - 126;   // amax = m 2^e, m in [0.5, 1)
+  e = e < -8 ? -8 : e;
+  const float s = __uint_as_float((uint32_t)(e - 7 + 127) << 23), s16 = s * 0.0625f;
+#pragma unroll
+  for (int c = 0; c < NC; ++c) {
+#pragma unroll
+    for (int d = 0; d < 8; ++d) {
+      const half8 &v = q[c][d >> 1];
+      const half2v x0 = {v[4 * (d & 1)], v[4 * (d & 1) + 1]};
+      const half2v x1 = {v[4 * (d & 1) + 2], v[4 * (d & 1) + 3]};
+      short2_t t = __builtin_amdgcn_cvt_scalef32_pk_fp8_f16(short2_t{0, 0}, x0, s, false);
+      t = __builtin_amdgcn_cvt_scalef32_pk_fp8_f16(t, x1, s, true);
+      const int h = __builtin_bit_cast(int, t);
+      const half2v r0 = x0 - __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(h, s, false);
+      const half2v r1 = x1 - __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(h, s, true);
+      short2_t u = __builtin_amdgcn_cvt_scalef32_pk_fp8_f16(short2_t{0, 0}, r0, s16, false);
+      u = __builtin_amdgcn_cvt_scalef32_pk_fp8_f16(u, r1, s16, true);
+      hi[c][d] = h;
+      lo[c][d] = __builtin_bit_cast(int, u);
+    }
+  }
+  return s;
+}
+
 // One row: 16 bytes per lane from `row` + 16 * lane (`row` uniform) into LDS at
 // `lds` + 16 * lane (`lds` uniform).  The row address travels in scalar registers
 // and the lane offset is one shared vector register.  Issued through asm, so the

@@ -8,7 +8,8 @@ Covered: the quantizer on float16 and float32 rows of every supported head dim,
 rows of zeros, negative zeros, tiny and huge magnitudes, constant rows, strided
 rows; attention on the decode workloads with FP8 rows at full size (ring
 window, ratio-128 with a partly valid tail, ratio-4 indexed), the ratio-4
-prefill chunk on sampled tokens, general ragged cases through both kernels
+prefill chunk in full, heads of very different query magnitudes (the scores'
+E4M3 query terms), general ragged cases through both kernels
 (validity masks whose hidden rows hold NaN codes and NaN scales, windows, index
 lists with unused entries, two regions), and the chain quantize -> attention.
 """
@@ -188,6 +189,26 @@ def test_attention_fp8_random(label, kw, entry, bq):
     _compare(out, want, label)
     if label == "f8_masked_tokens":
         assert (out[0, :3] == 0).all()   # tokens 0..2 see no row: exact zeros
+
+
+@pytest.mark.parametrize("entry,bq", [("prefill", 16), ("decode", 1)])
+def test_attention_fp8_query_magnitudes(entry, bq):
+    """Heads whose queries differ by many binary orders of magnitude, one of them all
+    zeros.  On FP8 rows the prefill and decode kernels compute the scores on the E4M3
+    matrix cores, each head's query carried as two E4M3 terms under a power-of-two
+    factor of its own: no term may leave the E4M3 range (past 448 the encoding is
+    NaN), and tiny queries must keep their precision down to float16's own."""
+    seed = 977
+    tokens = 20 if entry == "prefill" else 1
+    base = wl.random_problem(seed, batch=2, tokens=tokens, heads=64, head_dim=512, n0=160, window=48,
+                             q_pos0=140, k_pos0=0)
+    factors = [0.0, 2.0 ** -24, 2.0 ** -14, 2.0 ** -9, 2.0 ** -8, 2.0 ** -3, 1.0, 3.0]
+    f = torch.tensor([factors[h % len(factors)] for h in range(64)], dtype=torch.float32)
+    q = (base.q.float() * f[None, None, :, None]).to(base.q.dtype)
+    q[0, :, 9, 17] = 60000.0 * 2.0 ** -9   # one element far above the rest of its head
+    w = wl.fp8_variant(dataclasses.replace(base, q=q), seed + 1)
+    out = _run(w, entry, bq)
+    _compare(out, ref.attention(_oracle_problem(w)), f"fp8 {entry}, query magnitudes")
 
 
 def test_quantize_then_attend():
