@@ -72,13 +72,19 @@ enum { DS4ATTN_F16 = 0, DS4ATTN_F32 = 1, DS4ATTN_E4M3 = 2 };
  *              "Architecture Deep Dive", Whole-Model Graph Execution: K/V rows are
  *              quantized to FP8 before they are stored; the element format and the
  *              per-row scale are this library's choice, the pages give none).
- *              In the attention a K row's scale multiplies its scores in float32;
- *              a V row's values are formed in float16 as decode(code) times half
- *              the row scale (rounded to float16), the output doubled in float32.
- *              V values therefore keep float16's range (any row whose values lie
- *              within +-65504, the range ds4attn_quantize_fp8 accepts from float16
- *              rows) and its absolute resolution near zero (2^-25 on the halved
- *              value). */
+ *              In the attention a K row's scale multiplies its scores in float32.
+ *              The prefill kernel takes its scores from E4M3 x E4M3 matrix-core
+ *              products of the K codes and the query carried as two E4M3 terms
+ *              under a power-of-two factor per head, which reproduce each query
+ *              element to within 2^-8 of itself (or 2^-14 of the factor, if that
+ *              is larger); the decode kernels convert K codes to float16.  A V
+ *              row's scale is folded into the softmax weight of that row: the
+ *              weight P times the scale times a power of two, rounded once to
+ *              float16, where the power of two follows the largest V scale seen
+ *              so far and comes off the output in float32.  The weights thus keep
+ *              float16's relative precision at any V magnitude, and every finite
+ *              scale (ds4attn_quantize_fp8 writes amax/448 of finite rows) stays in
+ *              range: the factor keeps scale times factor below 2^7 and P <= 2^8. */
 enum { DS4ATTN_KV_PLAIN = 0, DS4ATTN_KV_FP8_E4M3 = 1 };
 
 /* Status byte values of the block map ([P-Metal] "Mask Handling and Block Skipping":

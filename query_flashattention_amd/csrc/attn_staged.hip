@@ -134,11 +134,15 @@ void attn_staged_kernel(const AttnParams p) {
   constexpr int kGuessed = SPLITKV && !FP8 ? 1 : NBUF;
   constexpr int kLateVMaxEntries = 5;   // see the producers' prologue
   constexpr int KPD = KEYS ? 4 : 2;   // K operand reads in flight (k-steps)
-  // FP8 rows outside KEYS: the V rows' scales are folded into P (P'[h, r] = P[h, r]
-  // sv[r], one float16 rounding; P <= 2^8 by the rescale slack and sv <= 65504 /
-  // 448, so P' < 2^16 stays finite), and V codes enter P.V as they are.  The sums
-  // l take P itself.
-  constexpr bool FOLDV = FP8 && !KEYS;
+  // FP8 rows: the V rows' scales are folded into P, and V codes enter P.V as they
+  // are: P'[h, r] = fp16(P[h, r] sv[r] vfac), one rounding.  vfac is a power of two
+  // that the workgroup (KEYS: each wave) takes from the first block's largest V
+  // scale and lowers, rescaling O exactly, only when a later block's largest scale
+  // times vfac passes 2^7; O gets 1 / vfac back at the end.  So P' < 2^15 (P <=
+  // 2^8 by the rescale slack) and, whatever the rows' magnitude, the largest
+  // weights keep float16's full precision instead of sinking into its subnormals.
+  // The sums l take P itself.
+  constexpr bool FOLDV = FP8;
   // FP8 HEADS: the scores run on the E4M3 matrix cores, K codes against Q carried
   // as two E4M3 terms (split_e4m3) with a power-of-two factor per head; the K rows'
   // scales then multiply the scores with the softmax scale.  No K code is
@@ -147,11 +151,6 @@ void attn_staged_kernel(const AttnParams p) {
   // us either way.)
   constexpr bool F8S = FP8 && MODE == kSplitHeads;
   constexpr int NQC = DIMS ? 1 : 4;   // F8S: 128-dim chunks per wave
-  // KEYS FP8 V rows are multiplied by half their row scale in float16, so that a row
-  // whose values reach the float16 maximum cannot overflow when its scale is
-  // rounded to float16 (448 * fp16(65504 / 448) rounds to inf, 224 * fp16(32752 /
-  // 448) does not); the output (or a split part's record) gets the factor 2 back.
-  constexpr float kOut = FP8 && !FOLDV ? 2.f : 1.f;
   // V operand reads in flight (output tiles); FP8 rows in HEADS take one fewer,
   // which keeps their conversions within 256 registers without spilling
   constexpr int VPD = KEYS ? 8 : (MODE == kSplitHeads && FP8 ? 3 : 4);
@@ -1006,6 +1005,46 @@ void attn_staged_kernel(const AttnParams p) {
 #pragma unroll
   for (int dt = 0; dt < (HT == 2 ? NDT : 1); ++dt) o2[dt] = floatx4{0.f, 0.f, 0.f, 0.f};
   float m2 = -INFINITY, l2 = 0.f;
+  // FOLDV: the V scales' running power-of-two factor vfac = 2^-vexp (0 until a
+  // block has a nonzero V scale), and its update for a block whose V row scales
+  // (this lane's eight slot rows) are in vr: afterwards vr holds the folded factors
+  // sv vfac, and the result is the factor (a power of two, 1 if unchanged) the
+  // outputs must take, which the softmax applies with its own rescale (vfold_update
+  // only moves the factor).  The update sits on each block's chain from its scales
+  // to P': about 0.5 us of a 4-block FP8 decode and 3 % of the FP8 prefill, the
+  // same wherever it was placed (at the block's start, behind a vote, on scalar
+  // registers) -- the price of full precision at any V magnitude.
+  int vexp = 0;
+  bool vset = false;
+  auto vfold_update = [&](const float (&vr)[8]) __attribute__((always_inline)) -> float {
+    // the block's largest V scale: the four lane groups hold its 32 rows (the
+    // lanes of a group the same eight), as the score max does
+    float mx = fmaxf(fmaxf(fmaxf(vr[0], vr[1]), fmaxf(vr[2], vr[3])), fmaxf(fmaxf(vr[4], vr[5]), fmaxf(vr[6], vr[7])));
+    mx = xor_max(mx, 16);
+    mx = xor_max(mx, 32);
+    // mx = f 2^e with f in [0.5, 1) (a subnormal mx counts as 2^-126; e <= 128, the
+    // scales being finite).  A new factor 2^-e when none is set yet, or when mx
+    // vfac may pass 2^7 (e - vexp > 7), so that P' < 2^8 * 2^7.  Selects only: a
+    // branch here makes the wave wait for the scales before anything else.
+    const uint32_t mb = __float_as_uint(mx);
+    int e = (int)((mb >> 23) & 0xffu) - 126;
+    e = e > -125 ? e : -125;
+    const bool upd = (mb != 0u) & (!vset | (e - vexp > 7));
+    // the outputs' factor 2^(vexp - e) (at least 2^-126: blocks so much smaller
+    // than the new one no longer matter)
+    const int dd = vexp - e;
+    const int d = (upd & vset) ? (dd > -126 ? dd : -126) : 0;
+    vexp = upd ? e : vexp;
+    vset = vset | upd;
+    return __uint_as_float((uint32_t)(127 + d) << 23);
+  };
+  auto vfold = [&](float (&vr)[8]) __attribute__((always_inline)) -> float {
+    const float r = vfold_update(vr);
+    const float vfac = vset ? __uint_as_float((uint32_t)(127 - vexp) << 23) : 0.f;
+#pragma unroll
+    for (int i2 = 0; i2 < 8; ++i2) vr[i2] *= vfac;
+    return r;
+  };
 
   // transpose-read roles: this lane points at row slot_row(g, e) of the V tile,
   // 4 dims starting at 16dt + 4a, for the lanes 16g + 4a + (0..3) to receive
@@ -1164,33 +1203,33 @@ void attn_staged_kernel(const AttnParams p) {
         const float mref = grow ? mx : m;
         const float msafe = (mref == -INFINITY) ? 0.f : mref;
         const float alpha = __builtin_amdgcn_exp2f(m - msafe);
+        // the V rows' scales of the same slot rows, folded into P
+        const float4 vlo = *(const float4 *)(sct + 32 + 4 * g);
+        const float4 vhi = *(const float4 *)(sct + 48 + 4 * g);
+        float vr[8] = {vlo.x, vlo.y, vlo.z, vlo.w, vhi.x, vhi.y, vhi.z, vhi.w};
+        const float vrs = vfold(vr);
         half8 pf;
         float psum = 0.f;
 #pragma unroll
         for (int i2 = 0; i2 < 8; ++i2) {
-          const _Float16 ph = (_Float16)__builtin_amdgcn_exp2f(sv[i2] - msafe);
-          pf[i2] = ph;
-          psum += (float)ph;
+          const float e = __builtin_amdgcn_exp2f(sv[i2] - msafe);
+          pf[i2] = (_Float16)(e * vr[i2]);
+          psum += e;
         }
         l = alpha * l + psum;
         m = mref;
-        if (__ballot(grow)) {
+        if (__ballot(grow || vrs != 1.f)) {
+          const float f = alpha * vrs;
 #pragma unroll
-          for (int dt = 0; dt < NDT; ++dt) o[dt] *= alpha;
+          for (int dt = 0; dt < NDT; ++dt) o[dt] *= f;
         }
         // O^T += V^T P^T, 32 keys per MFMA: the 8-bit transpose read hands lane
         // 16g + c dim 16dt + c of its group's eight slot rows (this lane supplies
-        // row slot_row(g, (lane & 15) >> 1), dims 16dt + 8(lane & 1) .. +7); times
-        // the rows' V scales in float16
+        // row slot_row(g, (lane & 15) >> 1), dims 16dt + 8(lane & 1) .. +7)
         const int trk = (lane & 15) >> 1;
         const int trow = trk < 4 ? 4 * g + trk : 16 + 4 * g + (trk - 4);
         const lds_char *vsrc = (const lds_char *)(__attribute__((address_space(3))) const void *)vtw +
                                f8_row_off(trow) + 8 * (lane & 1);
-        const float4 vlo = *(const float4 *)(sct + 32 + 4 * g);
-        const float4 vhi = *(const float4 *)(sct + 48 + 4 * g);
-        const half8 vsc = {(_Float16)(0.5f * vlo.x), (_Float16)(0.5f * vlo.y), (_Float16)(0.5f * vlo.z),
-                           (_Float16)(0.5f * vlo.w), (_Float16)(0.5f * vhi.x), (_Float16)(0.5f * vhi.y),
-                           (_Float16)(0.5f * vhi.z), (_Float16)(0.5f * vhi.w)};
         auto vload = [&](int dt) __attribute__((always_inline)) -> uint2 {
           const int2v rv = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
               (__attribute__((address_space(3))) int2v *)(vsrc + 16 * dt));
@@ -1201,7 +1240,7 @@ void attn_staged_kernel(const AttnParams p) {
         for (int u2 = 0; u2 < VPD; ++u2) vq[u2] = vload(u2);
 #pragma unroll
         for (int dt = 0; dt < NDT; ++dt) {
-          o[dt] = mfma16(e4m3x8_to_half8(vq[dt % VPD]) * vsc, pf, o[dt]);
+          o[dt] = mfma16(e4m3x8_to_half8(vq[dt % VPD]), pf, o[dt]);
           if (dt + VPD < NDT) vq[dt % VPD] = vload(dt + VPD);
           __builtin_amdgcn_sched_barrier(0);   // keep this order: MFMA, then the read it frees
         }
@@ -1293,7 +1332,10 @@ void attn_staged_kernel(const AttnParams p) {
       const float mw = mlw[ww * 16 + c16];
       lall += (mw == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(mw - mall)) * mlw[64 + ww * 16 + c16];
     }
-    const float f = m == -INFINITY ? 0.f : kOut * __builtin_amdgcn_exp2f(m - mall);
+    // (this wave's own V factor, FP8; a wave whose V scales were all zero has O = 0)
+    const float f = m == -INFINITY ? 0.f
+                                   : (FP8 ? (vset ? __uint_as_float((uint32_t)(127 + vexp) << 23) : 0.f) : 1.f) *
+                                         __builtin_amdgcn_exp2f(m - mall);
     // wave w finishes output tiles 8w .. 8w+7 (dims 128w .. 128w+127); the others
     // hand it theirs through LDS: xo[wave][tile][lane].  Instantiated per wave
     // index, so that the tile selection is resolved at compile time.
@@ -1366,6 +1408,7 @@ void attn_staged_kernel(const AttnParams p) {
     floatx4 s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
     floatx4 t0 = {0.f, 0.f, 0.f, 0.f}, t1 = {0.f, 0.f, 0.f, 0.f};
     const char *ktc = ktile(buf), *vtc = vtile(buf);
+    uint32_t kdep = 0;   // FP8: a register of the last K operand read (see the scale tile below)
     if constexpr (F8S) {
       // rows c16 and 16 + c16, dims 128c + 32g .. +31: 32 codes per operand; each K
       // operand meets the two Q terms (lo weighted 2^-4 by the B-side scale)
@@ -1421,6 +1464,7 @@ void attn_staged_kernel(const AttnParams p) {
         }
         __builtin_amdgcn_sched_barrier(0);   // keep this order: MFMAs, then the reads they free
       }
+      kdep = kb[(NKS - 1) % KPD].y;
     } else {
       const char *krow0 = ktc + c16 * kKRow + 2 * (d0 + 8 * g), *krow1 = krow0 + 16 * kKRow;
       uint4 ka[KPD], kb[KPD];
@@ -1485,27 +1529,44 @@ void attn_staged_kernel(const AttnParams p) {
     // kDimsWide, of head h + 16): the scores' factors (softmax scale, and FP8: the
     // K rows' scales), then one pass per head tile
     float kq[8];
+    // FP8: the scale tile's address is tied to the last K operand read (DIMS), so
+    // that its loads and the V factor below go out after the score phase's reads,
+    // while its last MFMAs run (scheduled at the top of the block, their wait held
+    // back the K reads), or to the scores (HEADS: during the last MFMAs their
+    // registers push the query terms out to scratch)
+    typedef __attribute__((address_space(3))) const float lds_float;
+    uint32_t sca = lds_addr(stile(buf));
+    if constexpr (F8S) asm volatile("" : "+v"(sca) : "v"(s0[0]), "v"(s1[0]));
+    else if constexpr (FP8) asm volatile("" : "+v"(sca) : "v"(kdep));
+    lds_float *sct8 = (lds_float *)(size_t)sca;
     if constexpr (FP8) {
       // K row scales of slot rows 4g..4g+3 (first rows of wave g's pairs) and
       // 16+4g..16+4g+3 (second rows of wave (g ^ 2)'s pairs)
-      const float *sc = stile(buf);
-      const float4 klo = *(const float4 *)(sc + 16 * g);
-      const float4 khi = *(const float4 *)(sc + 16 * (g ^ 2) + 4);
-      const float kr[8] = {klo.x, klo.y, klo.z, klo.w, khi.x, khi.y, khi.z, khi.w};
+      lds_float *sc = sct8;
+      typedef __attribute__((address_space(3))) const floatx4 lds_f4;
+      const floatx4 klo = *(lds_f4 *)(sc + 16 * g);
+      const floatx4 khi = *(lds_f4 *)(sc + 16 * (g ^ 2) + 4);
+      const float kr[8] = {klo[0], klo[1], klo[2], klo[3], khi[0], khi[1], khi[2], khi[3]};
 #pragma unroll
       for (int i2 = 0; i2 < 8; ++i2) kq[i2] = p.scale_log2 * kr[i2];
     } else {
 #pragma unroll
       for (int i2 = 0; i2 < 8; ++i2) kq[i2] = p.scale_log2;
     }
-    // FOLDV: the V rows' scales of the same slot rows (V at [16w' + 8 + q])
+    // FOLDV: the V rows' scales of the same slot rows (V at [16w' + 8 + q]) times
+    // the V factor
     float vr[FOLDV ? 8 : 1];
+    float vrs = 1.f;   // FOLDV: the outputs' factor from the V factor's update
     if constexpr (FOLDV) {
-      const float *sc = stile(buf);
-      const float4 vlo = *(const float4 *)(sc + 16 * g + 8);
-      const float4 vhi = *(const float4 *)(sc + 16 * (g ^ 2) + 12);
-      vr[0] = vlo.x; vr[1] = vlo.y; vr[2] = vlo.z; vr[3] = vlo.w;
-      vr[4] = vhi.x; vr[5] = vhi.y; vr[6] = vhi.z; vr[7] = vhi.w;
+      typedef __attribute__((address_space(3))) const floatx4 lds_f4;
+      const floatx4 vlo = *(lds_f4 *)(sct8 + 16 * g + 8);
+      const floatx4 vhi = *(lds_f4 *)(sct8 + 16 * (g ^ 2) + 12);
+#pragma unroll
+      for (int i2 = 0; i2 < 4; ++i2) {
+        vr[i2] = vlo[i2];
+        vr[4 + i2] = vhi[i2];
+      }
+      vrs = vfold(vr);
     }
     const uint32_t vis = __builtin_amdgcn_readfirstlane(vmask[i & (kMaskRing - 1)]);
     const uint32_t sm = slot_mask(vis, g);
@@ -1547,9 +1608,10 @@ void attn_staged_kernel(const AttnParams p) {
       }
       ll = alpha * ll + psum;
       mm = mref;
-      if (__ballot(grow)) {
+      if (__ballot(grow || vrs != 1.f)) {
+        const float f = alpha * vrs;
 #pragma unroll
-        for (int dt = 0; dt < NDT; ++dt) oo[dt] *= alpha;
+        for (int dt = 0; dt < NDT; ++dt) oo[dt] *= f;
       }
       return pp;
     };
@@ -1647,13 +1709,15 @@ void attn_staged_kernel(const AttnParams p) {
   lt = xor_sum(lt, 16);
   lt = xor_sum(lt, 32);
   const float inv = lt > 0.f ? 1.f / lt : 0.f;
+  // FP8: the V scales' factor comes off (O = 0 if it was never set)
+  const float ivf = !FP8 ? 1.f : (vset ? __uint_as_float((uint32_t)(127 + vexp) << 23) : 0.f);
   if constexpr (DIMS) {
     // DIMS: wave w writes dims 128w .. 128w + 127 of the workgroup's 16 (kDimsWide:
     // 32) heads, or, for a split part, of its unnormalised partial record (read
     // back by the combine pass: cached stores)
     if constexpr (PARTS) {
       char *rec = p.ws + ((int64_t)L * nsplit + split) * kSplitRecord;
-      store_acc_rows<NDT, false>(rec + 4 * d0, 512 * 4, o, kOut, lane);
+      store_acc_rows<NDT, false>(rec + 4 * d0, 512 * 4, o, ivf, lane);
       if (w == 0 && g == 0) {
         // then the maxima and the sums
         ((float *)(rec + 16 * 512 * 4))[c16] = m;
@@ -1661,12 +1725,12 @@ void attn_staged_kernel(const AttnParams p) {
       }
     } else {
       char *orow = p.o + b * p.o_sb + t * p.o_st + (int64_t)(hg * HG) * p.o_sh + 4 * d0;
-      store_acc_rows<NDT, true>(orow, p.o_sh, o, inv * kOut, lane);
+      store_acc_rows<NDT, true>(orow, p.o_sh, o, inv * ivf, lane);
       if constexpr (HT == 2) {
         float lt2 = l2;
         lt2 = xor_sum(lt2, 16);
         lt2 = xor_sum(lt2, 32);
-        store_acc_rows<NDT, true>(orow + 16 * p.o_sh, p.o_sh, o2, (lt2 > 0.f ? 1.f / lt2 : 0.f) * kOut, lane);
+        store_acc_rows<NDT, true>(orow + 16 * p.o_sh, p.o_sh, o2, (lt2 > 0.f ? 1.f / lt2 : 0.f) * ivf, lane);
       }
     }
     return;
@@ -1694,7 +1758,7 @@ void attn_staged_kernel(const AttnParams p) {
         lds_w *row = slot(16 * wj + c16) + 16 * g;
 #pragma unroll
         for (int dt = 0; dt < NDT; ++dt)
-          *(__attribute__((address_space(3))) floatx4 *)(row + 64 * dt) = o[dt] * (inv * kOut);
+          *(__attribute__((address_space(3))) floatx4 *)(row + 64 * dt) = o[dt] * (inv * ivf);
       }
       lds_barrier();
 #pragma unroll

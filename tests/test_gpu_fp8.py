@@ -9,7 +9,9 @@ rows of zeros, negative zeros, tiny and huge magnitudes, constant rows, strided
 rows; attention on the decode workloads with FP8 rows at full size (ring
 window, ratio-128 with a partly valid tail, ratio-4 indexed), the ratio-4
 prefill chunk in full, heads of very different query magnitudes (the scores'
-E4M3 query terms), general ragged cases through both kernels
+E4M3 query terms), V rows of tiny, huge and block-to-block changing scales (the
+V scales folded into the weights under a running power of two), general ragged
+cases through both kernels
 (validity masks whose hidden rows hold NaN codes and NaN scales, windows, index
 lists with unused entries, two regions), and the chain quantize -> attention.
 """
@@ -313,6 +315,51 @@ def test_attention_fp8_split_over_workgroups(split):
     w = wl.fp8_variant(wl.random_problem(77, **kw), 78)
     want = ref.attention(_oracle_problem(w))
     _compare(_run_flags(w, FP8_SPLITS[split], splits=3), want, f"fp8 index/{split} x3")
+
+
+@pytest.mark.parametrize("mode", ["prefill", "dims", "keys"])
+@pytest.mark.parametrize("pattern", ["tiny", "huge", "rising", "falling"])
+def test_attention_fp8_small_and_uneven_v_scales(mode, pattern):
+    """V rows whose scales are tiny or huge (as float32 rows can give), or change
+    by many binary orders of magnitude from one 32-row block to the next.  The
+    kernels fold the V scales into the softmax weights under a running
+    power-of-two factor: the weights must keep float16's precision at any
+    magnitude (without the factor, V rows of magnitude 1e-4 lose tens of percent,
+    and scales past 65504 overflow), and a block whose scales outgrow the factor
+    must rescale what is already summed.  Errors are relative to the output's
+    largest magnitude, since O scales with V."""
+    tokens = 16 if mode == "prefill" else 1
+    w = wl.random_problem(151, batch=2, tokens=tokens, heads=64, head_dim=512, n0=160, q_pos0=200,
+                          k_pos0=0)
+    g = torch.Generator().manual_seed(152)
+    kc, ks = ofp8.quantize_rows(w.r0.k.numpy())
+    vc, vs = ofp8.quantize_rows(torch.randn(w.r0.v.shape, generator=g).half().numpy())
+    block = np.arange(vs.shape[1]) // 32
+    if pattern == "tiny":
+        f = np.full(vs.shape[1], 1e-5)
+    elif pattern == "huge":
+        f = np.full(vs.shape[1], 1e25)
+    elif pattern == "rising":
+        f = 2.0 ** (10.0 * block - 40.0)      # 2^-40 .. 2^0, a factor 2^10 per block
+    else:
+        f = 2.0 ** (-10.0 * block)            # 1 .. 2^-40
+    vs = (vs * f[None, :]).astype(np.float32)
+    r0 = wl.RegionInputs(torch.from_numpy(kc), torch.from_numpy(vc), w.r0.n_rows, None, None,
+                         torch.from_numpy(ks), torch.from_numpy(vs))
+    w8 = dataclasses.replace(w, r0=r0)
+    want = ref.attention(_oracle_problem(w8))
+    dp = pipeline.to_device(w8, DEV)
+    if mode == "prefill":
+        out = pipeline.step(dp, "prefill", da.ds4attn_prefill_bq(), splits=1)
+    else:
+        dp.flags = da.FLAG_DECODE_DIMS if mode == "dims" else da.FLAG_DECODE_KEYS
+        out = pipeline.step(dp, "decode", 1, splits=1)
+    torch.cuda.synchronize()
+    out = out.cpu().double().numpy()
+    assert np.isfinite(out).all()
+    ref_mag = float(np.abs(want).max())
+    assert ref_mag > 0.0
+    _compare(out / ref_mag, want / ref_mag, f"fp8 V scales {pattern}/{mode}")
 
 
 @pytest.mark.parametrize("mode", ["prefill", "dims", "keys"])
