@@ -348,18 +348,21 @@ def test_attention_fp8_small_and_uneven_v_scales(mode, pattern):
                          torch.from_numpy(ks), torch.from_numpy(vs))
     w8 = dataclasses.replace(w, r0=r0)
     want = ref.attention(_oracle_problem(w8))
-    dp = pipeline.to_device(w8, DEV)
-    if mode == "prefill":
-        out = pipeline.step(dp, "prefill", da.ds4attn_prefill_bq(), splits=1)
-    else:
-        dp.flags = da.FLAG_DECODE_DIMS if mode == "dims" else da.FLAG_DECODE_KEYS
-        out = pipeline.step(dp, "decode", 1, splits=1)
-    torch.cuda.synchronize()
-    out = out.cpu().double().numpy()
-    assert np.isfinite(out).all()
     ref_mag = float(np.abs(want).max())
     assert ref_mag > 0.0
-    _compare(out / ref_mag, want / ref_mag, f"fp8 V scales {pattern}/{mode}")
+    # decode also in three split parts, each with a V factor of its own, whose
+    # records the combine pass must take in their true units
+    for splits in ((1,) if mode == "prefill" else (1, 3)):
+        dp = pipeline.to_device(w8, DEV)
+        if mode == "prefill":
+            out = pipeline.step(dp, "prefill", da.ds4attn_prefill_bq(), splits=1)
+        else:
+            dp.flags = da.FLAG_DECODE_DIMS if mode == "dims" else da.FLAG_DECODE_KEYS
+            out = pipeline.step(dp, "decode", 1, splits=splits)
+        torch.cuda.synchronize()
+        out = out.cpu().double().numpy()
+        assert np.isfinite(out).all()
+        _compare(out / ref_mag, want / ref_mag, f"fp8 V scales {pattern}/{mode} x{splits}")
 
 
 @pytest.mark.parametrize("mode", ["prefill", "dims", "keys"])
