@@ -5,12 +5,12 @@
 //
 // Each wave takes four rows, E = D/64 consecutive elements per lane.  In float32:
 // amax by a wave reduction, scale = amax / 448, each element x / scale clamped to
-// +-448 and rounded to the nearest E4M3 value, ties to even.  The rounding is done on the
-// float32 bits (below 2^-6 the values are multiples of 2^-9, so a scaled
-// round-to-nearest-even gives the code directly; above, the top three mantissa
-// bits are kept with a round-to-nearest-even carry into the exponent), so both
-// the codes and the scale are exactly determined by float32 arithmetic.  Each
-// row is read once and written once: 2D or 4D bytes in, D + 4 bytes out.
+// +-448 and rounded to the nearest E4M3 value, ties to even, by v_cvt_pk_fp8_f32
+// (two elements per instruction; on values within +-448 it gives the round-to-
+// nearest-even code, exact ties and subnormals included, measured against that rule
+// on the device), so both the codes and the scale are exactly determined by
+// float32 arithmetic.  Each row is read once and written once: 2D or 4D bytes in,
+// D + 4 bytes out.
 //
 // [P-DS4] = "DwarfStar 4 (DS4) -- DeepSeek V4 Flash Inference Engine".
 #include "mfma_common.h"
@@ -22,23 +22,6 @@ namespace ds4attn {
 namespace {
 
 constexpr float kE4M3Max = 448.0f;
-
-// E4M3 code of a float32 value with |y| <= 448.
-__device__ __forceinline__ uint32_t e4m3_code(float y) {
-  const uint32_t u = __float_as_uint(y);
-  const uint32_t sign = (u >> 24) & 0x80u;
-  const uint32_t a = u & 0x7fffffffu;
-  uint32_t mag;
-  if (a < 0x3c800000u) {
-    // below 2^-6: steps of 2^-9; the product is exact, the rounding is to even
-    mag = (uint32_t)__builtin_rintf(__uint_as_float(a) * 512.0f);
-  } else {
-    // keep 3 mantissa bits, round to nearest even (the carry may reach the
-    // exponent), then move the exponent bias from 127 to 7
-    mag = ((a + 0x7ffffu + ((a >> 20) & 1u)) >> 20) - (120u << 3);
-  }
-  return sign | mag;
-}
 
 // Maximum over the wave: DPP within rows of 16 lanes (quad swaps, then half-row
 // and row mirrors), then the swaps of rows across the halves.
@@ -108,35 +91,38 @@ __global__ __launch_bounds__(256) void quant_fp8_kernel(const char *__restrict__
     // every normal quotient equal.)
     const bool fast = scale >= 0x1p-80f && scale <= 3.4028235e38f;
     const float inv = 1.0f / scale;
-    uint8_t c[E];
+    float y[E < 2 ? 2 : E];
 #pragma unroll
     for (int i = 0; i < E; ++i) {
-      uint32_t code = 0;
+      float q = 0.f;   // (a row with scale 0 gets zero codes)
       if (scale != 0.f) {
-        float q;
         if (fast) {
           const float q0 = v[j][i] * inv;
           q = __builtin_copysignf(__builtin_fmaf(__builtin_fmaf(-q0, scale, v[j][i]), inv, q0), v[j][i]);
         } else {
           q = v[j][i] / scale;
         }
-        const float y = fminf(fmaxf(q, -kE4M3Max), kE4M3Max);   // keeps the sign of zero
-        code = e4m3_code(y);
       }
-      c[i] = (uint8_t)code;
+      y[i] = fminf(fmaxf(q, -kE4M3Max), kE4M3Max);   // keeps the sign of zero
+    }
+    if constexpr (E == 1) y[1] = 0.f;
+    // codes of elements 4k .. 4k + 3 in dword k, element 4k in its low byte
+    uint32_t w[E < 4 ? 1 : E / 4];
+#pragma unroll
+    for (int k = 0; k < (E < 4 ? 1 : E / 4); ++k) {
+      w[k] = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(y[4 * k], y[4 * k + 1], 0, false);
+      if constexpr (E >= 4)
+        w[k] = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(y[4 * k + 2], y[4 * k + 3], (int)w[k], true);
     }
     char *dst = codes + bs[j] * c_sb + rs[j] * c_sr + (int64_t)lane * E;
     if constexpr (E == 8) {
-      uint2 w;
-      w.x = c[0] | (c[1] << 8) | (c[2] << 16) | ((uint32_t)c[3] << 24);
-      w.y = c[4] | (c[5] << 8) | (c[6] << 16) | ((uint32_t)c[7] << 24);
-      *(uint2 *)dst = w;
+      *(uint2 *)dst = make_uint2(w[0], w[1]);
     } else if constexpr (E == 4) {
-      *(uint32_t *)dst = c[0] | (c[1] << 8) | (c[2] << 16) | ((uint32_t)c[3] << 24);
+      *(uint32_t *)dst = w[0];
     } else if constexpr (E == 2) {
-      *(uint16_t *)dst = (uint16_t)(c[0] | (c[1] << 8));
+      *(uint16_t *)dst = (uint16_t)w[0];
     } else {
-      *(uint8_t *)dst = c[0];
+      *(uint8_t *)dst = (uint8_t)w[0];
     }
     if (lane == 0) *(float *)(scales + bs[j] * s_sb + 4LL * rs[j]) = scale;
   }
