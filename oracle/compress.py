@@ -6,7 +6,7 @@ ratio boundary is reached, with a rolling KV/score state holding the rows of the
 group not yet complete ([P-DS4] "Architecture Deep Dive", Layer Compression and
 KV Cache Design; "GPU Backend Architecture" lists compressor update and prefill
 among the GPU operations).  The pages name the state (pending KV rows and their
-scores) but give no formula.  Readings taken (each is listed in the design doc):
+scores) but give no formula.  Readings taken:
 
 * a score accompanies every element of a raw row (the state holds KV and score
   rows of the same shape); the learned projection that produces the scores is

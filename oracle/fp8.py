@@ -5,8 +5,7 @@ the attention reads the quantized rows ([P-DS4] "Architecture Deep Dive",
 Whole-Model Graph Execution, where the layer schedule puts an FP8 quantize step
 between the Q/KV projections and the raw KV store; "GPU Backend Architecture"
 counts an FP8 KV quantization among the GPU operations).  The pages do not give
-the format.  Readings taken (each is listed
-in DESIGN.md):
+the format.  Readings taken:
 
 * element format: OCP FP8 E4M3 ("e4m3fn"): 1 sign, 4 exponent bits (bias 7), 3
   mantissa bits; exponent field 0 is subnormal (m/8 * 2^-6); 0x7F / 0xFF are NaN;

@@ -19,7 +19,7 @@ What is computed, and where the pages say so:
   on Metal Device Buffers"); the skip map holds one status byte per block
   ([P-Metal] "Mask Handling and Block Skipping").
 
-Readings taken where the pages are silent (each is listed in the design doc):
+Readings taken where the pages are silent:
 
 * padded rows hold +0.0 and are never attended;
 * status byte: 0 = every pair masked (skip), 1 = some pairs allowed, 2 = every

@@ -6,7 +6,7 @@ Backend Architecture" lists the indexed mixed attention that consumes the list).
 How the indexer scores rows is learned and not on the pages; what is defined
 here is the selection step on given scores.
 
-Readings taken where the pages are silent (each is listed in the design doc):
+Readings taken where the pages are silent:
 
 * order: float32 scores compare by the IEEE total order of their bit patterns
   (-0 < +0; a NaN with the sign bit clear ranks above +inf, one with it set
