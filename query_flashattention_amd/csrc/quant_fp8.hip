@@ -15,29 +15,11 @@
 // [P-DS4] = "DwarfStar 4 (DS4) -- DeepSeek V4 Flash Inference Engine".
 #include "mfma_common.h"
 
-#include <type_traits>
-
 namespace ds4attn {
 
 namespace {
 
 constexpr float kE4M3Max = 448.0f;
-
-// Maximum over the wave: DPP within rows of 16 lanes (quad swaps, then half-row
-// and row mirrors), then the swaps of rows across the halves.
-__device__ __forceinline__ float wave_max(float x) {
-  auto dpp = [](float v, auto ctrl) __attribute__((always_inline)) {
-    constexpr int C = decltype(ctrl)::value;
-    return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), C, 0xf, 0xf, false));
-  };
-  x = fmaxf(x, dpp(x, std::integral_constant<int, 0xb1>{}));    // quad_perm(1, 0, 3, 2): lane ^ 1
-  x = fmaxf(x, dpp(x, std::integral_constant<int, 0x4e>{}));    // quad_perm(2, 3, 0, 1): lane ^ 2
-  x = fmaxf(x, dpp(x, std::integral_constant<int, 0x141>{}));   // row_half_mirror: the other quad of 8
-  x = fmaxf(x, dpp(x, std::integral_constant<int, 0x140>{}));   // row_mirror: the other half of 16
-  x = xor_max(x, 16);
-  x = xor_max(x, 32);
-  return x;
-}
 
 // R rows per wave: their loads are all issued before the first reduction, so a
 // wave keeps R row reads in flight instead of one.
