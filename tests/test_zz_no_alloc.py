@@ -5,7 +5,8 @@ Two split calls in a row share the device's static scratch array: the ratio-128
 layer at 32K for one sequence (the plan splits it over 4 parts per group of 16
 heads: 16 records), then a smaller one (16 heads, 96 compressed rows: 2 parts, 2
 records), whose records must not mix with the first call's.  A 64-sequence batch
-(no split) takes the unsplit path.  Each output equals ds4attn_decode's bit for
+(no split) takes the unsplit path, and the single sequence on FP8 rows splits
+too.  Each output equals ds4attn_decode's bit for
 bit (same kernels, same split) and is within the attention tolerance of the
 float64 oracle.
 """
@@ -75,3 +76,16 @@ def test_noalloc_unsplit_batch():
     assert rec == 0
     assert torch.equal(got, want)
     compare(got.double().numpy(), ref.attention(ref.from_workload(w)), "noalloc decode_swa")
+
+
+def test_noalloc_fp8_rows_split():
+    """FP8 rows through the split: each part folds its V scales into the weights
+    under a factor of its own and leaves its record in true units, in the static
+    array as in a caller's workspace."""
+    from tests.test_gpu_fp8 import _oracle_problem
+    w = wl.fp8_variant(wl.named("decode_r128"), 5)
+    got, want, rec = _both(w)
+    assert rec > 0                          # the plan splits the single sequence
+    assert torch.equal(got, want)
+    compare(got.double().numpy(), ref.attention(_oracle_problem(w)), "noalloc decode_r128 fp8")
+
