@@ -317,7 +317,7 @@ def test_attention_fp8_split_over_workgroups(split):
     _compare(_run_flags(w, FP8_SPLITS[split], splits=3), want, f"fp8 index/{split} x3")
 
 
-@pytest.mark.parametrize("mode", ["prefill", "dims", "keys"])
+@pytest.mark.parametrize("mode", ["prefill", "dims", "keys", "wide"])
 @pytest.mark.parametrize("pattern", ["tiny", "huge", "rising", "falling"])
 def test_attention_fp8_small_and_uneven_v_scales(mode, pattern):
     """V rows whose scales are tiny or huge (as float32 rows can give), or change
@@ -351,13 +351,15 @@ def test_attention_fp8_small_and_uneven_v_scales(mode, pattern):
     ref_mag = float(np.abs(want).max())
     assert ref_mag > 0.0
     # decode also in three split parts, each with a V factor of its own, whose
-    # records the combine pass must take in their true units
-    for splits in ((1,) if mode == "prefill" else (1, 3)):
+    # records the combine pass must take in their true units (wide DIMS, two head
+    # tiles per wave whose outputs both take the factor, has no split parts)
+    for splits in ((1,) if mode in ("prefill", "wide") else (1, 3)):
         dp = pipeline.to_device(w8, DEV)
         if mode == "prefill":
             out = pipeline.step(dp, "prefill", da.ds4attn_prefill_bq(), splits=1)
         else:
-            dp.flags = da.FLAG_DECODE_DIMS if mode == "dims" else da.FLAG_DECODE_KEYS
+            dp.flags = {"dims": da.FLAG_DECODE_DIMS, "keys": da.FLAG_DECODE_KEYS,
+                        "wide": da.FLAG_DECODE_WIDE}[mode]
             out = pipeline.step(dp, "decode", 1, splits=splits)
         torch.cuda.synchronize()
         out = out.cpu().double().numpy()
