@@ -84,7 +84,10 @@ enum { DS4ATTN_F16 = 0, DS4ATTN_F32 = 1, DS4ATTN_E4M3 = 2 };
  *              so far and comes off the output in float32.  The weights thus keep
  *              float16's relative precision at any V magnitude, and every finite
  *              scale (ds4attn_quantize_fp8 writes amax/448 of finite rows) stays in
- *              range: the factor keeps scale times factor below 2^7 and P <= 2^8. */
+ *              range: the factor keeps scale times factor below 2^7 and P <= 2^8.
+ *              No output or partial sum exceeds the V rows' magnitude, so the
+ *              outputs are finite wherever every visible row's values (code times
+ *              scale) are finite float32 values. */
 enum { DS4ATTN_KV_PLAIN = 0, DS4ATTN_KV_FP8_E4M3 = 1 };
 
 /* Status byte values of the block map ([P-Metal] "Mask Handling and Block Skipping":
@@ -311,9 +314,11 @@ int32_t ds4attn_prefill_bq(void);
  * small to fill the chip (one sequence of a long-context layer: [P-DS4] "Architecture Deep Dive",
  * 32K-1M contexts; the fused step of [P-Metal] "FlashAttention Kernel
  * Architecture" run on parts of the block list).  Each part keeps its own running
- * maximum, sum and unnormalised output in `workspace`; a second kernel combines
- * them: O = sum_s 2^(m_s - M) O_s / sum_s 2^(m_s - M) l_s with M = max_s m_s (the
- * online-softmax rescale, applied once across parts).  The result equals
+ * maximum m_s, sum l_s and output O_s (normalised by l_s) in `workspace`; a second
+ * kernel combines them: O = sum_s w_s O_s / sum_s w_s with w_s = 2^(m_s - M) l_s
+ * and M = max_s m_s (the online-softmax rescale, applied once across parts; the
+ * weights are normalised before the outputs are summed, so that no partial sum
+ * exceeds the V rows' magnitude).  The result equals
  * ds4attn_decode's up to rounding.  (ds4attn_decode picks the split itself; this
  * entry point fixes it, for measurement and cross-checks.)
  *   splits     1..64; 1 runs unsplit (no workspace needed)

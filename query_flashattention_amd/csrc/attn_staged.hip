@@ -1022,13 +1022,14 @@ void attn_staged_kernel(const AttnParams p) {
     float mx = fmaxf(fmaxf(fmaxf(vr[0], vr[1]), fmaxf(vr[2], vr[3])), fmaxf(fmaxf(vr[4], vr[5]), fmaxf(vr[6], vr[7])));
     mx = xor_max(mx, 16);
     mx = xor_max(mx, 32);
-    // mx = f 2^e with f in [0.5, 1) (a subnormal mx counts as 2^-126; e <= 128, the
-    // scales being finite).  A new factor 2^-e when none is set yet, or when mx
+    // mx = f 2^e with f in [0.5, 1), e taken within [-125, 126] so that 2^-e and 2^e
+    // are normal floats (a subnormal mx counts as 2^-125; a finite mx of 2^126 or
+    // more gives mx vfac < 4).  A new factor 2^-e when none is set yet, or when mx
     // vfac may pass 2^7 (e - vexp > 7), so that P' < 2^8 * 2^7.  Selects only: a
     // branch here makes the wave wait for the scales before anything else.
     const uint32_t mb = __float_as_uint(mx);
     int e = (int)((mb >> 23) & 0xffu) - 126;
-    e = e > -125 ? e : -125;
+    e = e > -125 ? (e < 126 ? e : 126) : -125;
     const bool upd = (mb != 0u) & (!vset | (e - vexp > 7));
     // the outputs' factor 2^(vexp - e) (at least 2^-126: blocks so much smaller
     // than the new one no longer matter)
@@ -1332,10 +1333,13 @@ void attn_staged_kernel(const AttnParams p) {
       const float mw = mlw[ww * 16 + c16];
       lall += (mw == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(mw - mall)) * mlw[64 + ww * 16 + c16];
     }
-    // (this wave's own V factor, FP8; a wave whose V scales were all zero has O = 0)
-    const float f = m == -INFINITY ? 0.f
-                                   : (FP8 ? (vset ? __uint_as_float((uint32_t)(127 + vexp) << 23) : 0.f) : 1.f) *
-                                         __builtin_amdgcn_exp2f(m - mall);
+    // Each wave's share of the normalised output, so that no sum exceeds the V
+    // rows' own magnitude: 2^(m - mall) / lall, times this wave's V factor (FP8; a
+    // wave whose V scales were all zero has O = 0).
+    const float f = m == -INFINITY || !(lall > 0.f)
+                        ? 0.f
+                        : (FP8 ? (vset ? __uint_as_float((uint32_t)(127 + vexp) << 23) : 0.f) : 1.f) *
+                              (__builtin_amdgcn_exp2f(m - mall) / lall);
     // wave w finishes output tiles 8w .. 8w+7 (dims 128w .. 128w+127); the others
     // hand it theirs through LDS: xo[wave][tile][lane].  Instantiated per wave
     // index, so that the tile selection is resolved at compile time.
@@ -1361,7 +1365,7 @@ void attn_staged_kernel(const AttnParams p) {
     else if (w == 2) merge(std::integral_constant<int, 2>{});
     else merge(std::integral_constant<int, 3>{});
     if constexpr (PARTS) {
-      // partial record of this split: unnormalised O, then the maxima and the sums
+      // partial record of this split: its normalised O, then the maxima and the sums
       char *rec = p.ws + ((int64_t)L * nsplit + split) * kSplitRecord;
       store_acc_rows<8, false>(rec + 512 * w, 512 * 4, acc, 1.f, lane);
       if (w == 0 && g == 0) {
@@ -1370,9 +1374,8 @@ void attn_staged_kernel(const AttnParams p) {
       }
       return;
     }
-    const float inv = lall > 0.f ? 1.f / lall : 0.f;
     store_acc_rows<8, true>(p.o + b * p.o_sb + t * p.o_st + (int64_t)(hg * HG) * p.o_sh + 512 * w, p.o_sh, acc,
-                            inv, lane);
+                            1.f, lane);
     return;
   }
 
@@ -1713,11 +1716,12 @@ void attn_staged_kernel(const AttnParams p) {
   const float ivf = !FP8 ? 1.f : (vset ? __uint_as_float((uint32_t)(127 + vexp) << 23) : 0.f);
   if constexpr (DIMS) {
     // DIMS: wave w writes dims 128w .. 128w + 127 of the workgroup's 16 (kDimsWide:
-    // 32) heads, or, for a split part, of its unnormalised partial record (read
-    // back by the combine pass: cached stores)
+    // 32) heads, or, for a split part, of its partial record (normalised like an
+    // output, so that it never exceeds the V rows' magnitude; read back by the
+    // combine pass: cached stores)
     if constexpr (PARTS) {
       char *rec = p.ws + ((int64_t)L * nsplit + split) * kSplitRecord;
-      store_acc_rows<NDT, false>(rec + 4 * d0, 512 * 4, o, ivf, lane);
+      store_acc_rows<NDT, false>(rec + 4 * d0, 512 * 4, o, inv * ivf, lane);
       if (w == 0 && g == 0) {
         // then the maxima and the sums
         ((float *)(rec + 16 * 512 * 4))[c16] = m;
@@ -1834,12 +1838,14 @@ hipError_t launch_attn_decode(const AttnParams &p, hipStream_t s) {
   return launch_staged<kSplitDims>(p, s);
 }
 // Combine the split partials of one (token, head group): 16 heads x 512 dims over
-// 1024 threads, thread = (head, 8 dims).  The partials were accumulated
-// against their own running maxima m_s (base 2); with M = max m_s the result is
-// sum_s 2^(m_s - M) O_s / sum_s 2^(m_s - M) l_s, zero when no split saw a row.  The
-// maxima and sums of all parts are staged in LDS first (one load per thread), and
-// the parts' outputs are read eight parts at a time, so the pass costs a few
-// memory round trips whatever the split count.
+// 1024 threads, thread = (head, 8 dims).  Each part's record holds its own
+// normalised output O_s (its rows' weights summing to one) with the running
+// maximum m_s (base 2) and the sum l_s its weights were taken against; with
+// M = max m_s and w_s = 2^(m_s - M) l_s the result is sum_s (w_s / sum_t w_t) O_s,
+// zero when no split saw a row.  The weights are normalised before the outputs
+// meet, so no sum exceeds the V rows' magnitude.  The maxima and sums of all
+// parts are staged in LDS, and the parts' outputs are read eight parts at a time,
+// so the pass costs a few memory round trips whatever the split count.
 __global__ __launch_bounds__(1024) void split_combine_kernel(const AttnParams p) {
   __shared__ float ml[2][16][kMaxSplits];   // [m | l][head][part]
   const int ngroups = p.H / 16;
@@ -1852,42 +1858,86 @@ __global__ __launch_bounds__(1024) void split_combine_kernel(const AttnParams p)
   const int tid = threadIdx.x, hh = tid >> 6, dq = (tid & 63) * 4;
   const int ns = p.nsplit;
   const char *rec0 = p.ws + L * ns * kSplitRecord;
-  for (int e = tid; e < 32 * ns; e += 1024) {   // e = part * 32 + (0..15 maxima, 16..31 sums)
-    const int sp = e >> 5, k = e & 31;
-    ml[k >> 4][k & 15][sp] = ((const float *)(rec0 + sp * kSplitRecord + 16 * 512 * 4))[k];
+  floatx4 v0[8], v1[8];
+  // (every load below is unconditional -- parts past the last re-read the last
+  // part's record, whose copies are never used -- so that the compiler's wait
+  // counts know how many loads are younger than each one and need not drain them)
+  auto load8 = [&](int s0) {
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int sp = s0 + u < ns ? s0 + u : ns - 1;
+      const floatx4 *src = (const floatx4 *)((const float *)(rec0 + sp * kSplitRecord) + hh * 512 + dq);
+      v0[u] = src[0];
+      v1[u] = src[64];
+    }
+  };
+  // The maxima and sums of all parts go to LDS, padded to a multiple of eight
+  // parts with m = -inf and l = 0 so that they are reduced eight independent reads
+  // at a time.  Each thread stages at most two of them (32 x 64 entries at most);
+  // they are loaded before the first eight parts' outputs, so that waiting for
+  // them leaves the outputs in flight through the reductions (one memory round
+  // trip for the whole pass when there are at most eight parts).
+  const int ns8 = (ns + 7) & ~7;
+  float st[2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int e = tid + 1024 * i, sp = e >> 5, k = e & 31;   // part, then 0..15 maxima, 16..31 sums
+    const float x = ((const float *)(rec0 + (sp < ns ? sp : ns - 1) * kSplitRecord + 16 * 512 * 4))[k];
+    st[i] = sp < ns ? x : (k < 16 ? -INFINITY : 0.f);
   }
-  __syncthreads();
+  load8(0);
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int e = tid + 1024 * i, sp = e >> 5, k = e & 31;
+    if (sp < ns8) ml[k >> 4][k & 15][sp] = st[i];
+  }
+  lds_barrier();
   float mmax = -INFINITY;
-  for (int sp = 0; sp < ns; ++sp) mmax = fmaxf(mmax, ml[0][hh][sp]);
+  for (int s0 = 0; s0 < ns8; s0 += 8) {
+#pragma unroll
+    for (int u = 0; u < 8; ++u) mmax = fmaxf(mmax, ml[0][hh][s0 + u]);
+  }
+  auto weight = [&](int sp) {   // (both read first: a select, not a branch per part)
+    const float ms = ml[0][hh][sp], ls = ml[1][hh][sp];
+    const float x = __builtin_amdgcn_exp2f(ms - mmax) * ls;
+    return ms == -INFINITY ? 0.f : x;
+  };
+  float w8[8], lsum = 0.f;   // (the first eight parts' weights stay in registers)
+#pragma unroll
+  for (int u = 0; u < 8; ++u) {
+    w8[u] = weight(u);
+    lsum += w8[u];
+  }
+  for (int s0 = 8; s0 < ns8; s0 += 8) {
+#pragma unroll
+    for (int u = 0; u < 8; ++u) lsum += weight(s0 + u);
+  }
+  const float inv = lsum > 0.f ? 1.f / lsum : 0.f;
   floatx4 acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f};
-  float lsum = 0.f;
   if (mmax != -INFINITY) {
-    for (int s0 = 0; s0 < ns; s0 += 8) {
-      floatx4 v0[8], v1[8];
+    // normalised weights: no sum exceeds the V rows' magnitude
 #pragma unroll
-      for (int u = 0; u < 8; ++u) {
-        if (s0 + u < ns) {
-          const floatx4 *src = (const floatx4 *)((const float *)(rec0 + (s0 + u) * kSplitRecord) + hh * 512 + dq);
-          v0[u] = src[0];
-          v1[u] = src[64];
-        }
+    for (int u = 0; u < 8; ++u) {
+      if (u < ns) {
+        acc0 += (w8[u] * inv) * v0[u];
+        acc1 += (w8[u] * inv) * v1[u];
       }
+    }
+    for (int s0 = 8; s0 < ns; s0 += 8) {
+      load8(s0);
 #pragma unroll
       for (int u = 0; u < 8; ++u) {
         if (s0 + u < ns) {
-          const float ms = ml[0][hh][s0 + u];
-          const float wgt = ms == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(ms - mmax);
-          lsum += wgt * ml[1][hh][s0 + u];
+          const float wgt = weight(s0 + u) * inv;
           acc0 += wgt * v0[u];
           acc1 += wgt * v1[u];
         }
       }
     }
   }
-  const float inv = lsum > 0.f ? 1.f / lsum : 0.f;
   float *ob = (float *)(p.o + b * p.o_sb + t * p.o_st + (int64_t)(hg * 16 + hh) * p.o_sh) + dq;
-  *(floatx4 *)ob = acc0 * inv;
-  *(floatx4 *)(ob + 256) = acc1 * inv;
+  *(floatx4 *)ob = acc0;
+  *(floatx4 *)(ob + 256) = acc1;
 }
 
 hipError_t launch_attn_decode_split(const AttnParams &p, hipStream_t s) {

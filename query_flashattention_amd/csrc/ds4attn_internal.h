@@ -163,8 +163,8 @@ hipError_t launch_attn_generic(const AttnParams &p, int elem_bytes, hipStream_t 
 // workgroups of 16; prefill keeps 64 heads of a token in one workgroup.
 hipError_t launch_attn_decode(const AttnParams &p, hipStream_t s);
 // Split decode: the partial pass (p.nsplit > 1, p.ws set) then the combine pass.
-// A partial record: unnormalised O of 16 heads x 512 dims (float32, head-major),
-// then the 16 running maxima (base-2 scores) and the 16 sums.
+// A partial record: the part's normalised O of 16 heads x 512 dims (float32,
+// head-major), then the 16 running maxima (base-2 scores) and the 16 sums.
 constexpr int kMaxSplits = 64;
 constexpr int64_t kSplitRecord = 16 * 512 * 4 + 16 * 4 * 2;
 hipError_t launch_attn_decode_split(const AttnParams &p, hipStream_t s);

@@ -318,7 +318,7 @@ def test_attention_fp8_split_over_workgroups(split):
 
 
 @pytest.mark.parametrize("mode", ["prefill", "dims", "keys", "wide"])
-@pytest.mark.parametrize("pattern", ["tiny", "huge", "rising", "falling"])
+@pytest.mark.parametrize("pattern", ["tiny", "huge", "rising", "falling", "top"])
 def test_attention_fp8_small_and_uneven_v_scales(mode, pattern):
     """V rows whose scales are tiny or huge (as float32 rows can give), or change
     by many binary orders of magnitude from one 32-row block to the next.  The
@@ -326,8 +326,11 @@ def test_attention_fp8_small_and_uneven_v_scales(mode, pattern):
     power-of-two factor: the weights must keep float16's precision at any
     magnitude (without the factor, V rows of magnitude 1e-4 lose tens of percent,
     and scales past 65504 overflow), and a block whose scales outgrow the factor
-    must rescale what is already summed.  Errors are relative to the output's
-    largest magnitude, since O scales with V."""
+    must rescale what is already summed.  "top" takes the scales to the top of
+    float32's range (up to 1.9 * 2^127, with codes of magnitude at most 1 so that
+    every row value is a finite float32), where the factor's exponent meets its
+    limit and any sum of unnormalised partial outputs would overflow.  Errors are
+    relative to the output's largest magnitude, since O scales with V."""
     tokens = 16 if mode == "prefill" else 1
     w = wl.random_problem(151, batch=2, tokens=tokens, heads=64, head_dim=512, n0=160, q_pos0=200,
                           k_pos0=0)
@@ -335,7 +338,19 @@ def test_attention_fp8_small_and_uneven_v_scales(mode, pattern):
     kc, ks = ofp8.quantize_rows(w.r0.k.numpy())
     vc, vs = ofp8.quantize_rows(torch.randn(w.r0.v.shape, generator=g).half().numpy())
     block = np.arange(vs.shape[1]) // 32
-    if pattern == "tiny":
+    if pattern == "top":
+        # codes of |value| <= 1, scales 1.9 * 2^127 * u (u in [0.5, 1)) but in blocks
+        # 0 and 2, 2^-60 and 2^-30 lower: the factor set by block 0 must rise to its
+        # limit at block 1, rescaling what is summed (in a split, the parts and
+        # the KEYS waves each see a different mix of the two)
+        x = (torch.randn(w.r0.v.shape, generator=g) * 0.3).clamp(-1.0, 1.0).numpy().astype(np.float32)
+        vc = ofp8.encode(x)
+        u = 0.5 + 0.5 * torch.rand(vs.shape, generator=g).numpy()
+        drop = np.array([-60.0, 0.0, -30.0, 0.0, 0.0])[np.minimum(block, 4)]
+        vs = (1.9 * 2.0 ** 127 * u * 2.0 ** drop[None, :]).astype(np.float32)
+        assert np.isfinite(vs).all() and float(vs.max()) > 2.0 ** 127
+        f = np.ones(vs.shape[1])
+    elif pattern == "tiny":
         f = np.full(vs.shape[1], 1e-5)
     elif pattern == "huge":
         f = np.full(vs.shape[1], 1e25)
