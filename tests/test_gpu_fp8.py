@@ -367,8 +367,11 @@ def test_attention_fp8_small_and_uneven_v_scales(mode, pattern):
     assert ref_mag > 0.0
     # decode also in three split parts, each with a V factor of its own, whose
     # records the combine pass must take in their true units (wide DIMS, two head
-    # tiles per wave whose outputs both take the factor, has no split parts)
-    for splits in ((1,) if mode in ("prefill", "wide") else (1, 3)):
+    # tiles per wave whose outputs both take the factor, has no split parts); at
+    # the top of the range also in 12 parts over the 5 blocks: more than one batch
+    # of eight records in the combine, and empty parts beside near-maximal ones
+    splits_list = (1, 3, 12) if pattern == "top" else (1, 3)
+    for splits in ((1,) if mode in ("prefill", "wide") else splits_list):
         dp = pipeline.to_device(w8, DEV)
         if mode == "prefill":
             out = pipeline.step(dp, "prefill", da.ds4attn_prefill_bq(), splits=1)
