@@ -168,14 +168,16 @@ int resolve_args(const ds4attn_args *a, bool prefill, Resolved &R) {
 // Dive", Whole-Model Graph Execution: the attention path is chosen by layer type
 // and batch size).  A decode workgroup covers one token's 16 heads; a batch with
 // fewer than 128 such groups leaves most of the 256 CUs idle, so each token's
-// block list is divided over up to 256 / groups workgroups, two key blocks per
-// part and at most 10 parts; lists of up to 5 blocks stay whole (the combine pass
-// costs more than the split saves).  Measured on one sequence (µs, parts in
-// brackets): a 4-block window 7.9 [1], 9.4 [2]; 8 dense blocks 11.8 [2], 10.4 [4];
-// 12 blocks of the ratio-128 layer 12.4 [3], 11.7 [4], 11.7 [6], 13.3 [12]; 16
-// dense blocks 12.6 [4], 11.9 [8], 13.1 [11]; the ratio-4 layer's 20 blocks 15.5
-// [6], 13.9 [10], 14.7 [12]; 32 dense blocks 14.1 [8], 14.3 [11], 14.7 [16].
-// 64-sequence batches only lose from splitting.
+// block list is divided over up to 256 / groups workgroups, at least two key
+// blocks per part and at most 8 parts (the combine pass reads eight parts' records
+// per memory round trip), then over as few parts as keep the longest part that
+// short; lists of up to 5 blocks stay whole (the combine pass costs more than the
+// split saves).  Measured on one sequence (µs, parts in brackets): a 4-block
+// window 7.9 [1], 9.4 [2]; 8 dense blocks 11.8 [2], 10.4 [4]; 12 blocks of the
+// ratio-128 layer 13.3 [3], 12.5 [4], 11.9 [6], 13.6 [12]; 16 dense blocks 12.6
+// [4], 11.9 [8], 13.1 [11]; the ratio-4 layer's 20 blocks 15.6 [6], 14.1 [7],
+// 14.3 [8], 14.5 [10]; 32 dense blocks 13.8 [8], 15.6 [10].  64-sequence batches
+// only lose from splitting.
 int plan_splits(const Resolved &R, bool prefill) {
   // (a chosen wide split has no split parts)
   if (prefill || R.empty || !R.mfma || R.P.decode_split == 3) return 1;
@@ -183,9 +185,11 @@ int plan_splits(const Resolved &R, bool prefill) {
   const int64_t groups = (int64_t)P.B * P.T * (P.H / 16);
   if (groups >= 128) return 1;
   const int64_t lb = list_bound(P);
-  const int64_t by_len = lb <= 5 ? 1 : std::min<int64_t>(lb / 2, 10);
-  const int64_t by_cus = 256 / groups;
-  return (int)std::max<int64_t>(1, std::min<int64_t>({(int64_t)kMaxSplits, by_len, by_cus}));
+  if (lb <= 5) return 1;
+  const int64_t cap = std::min<int64_t>({lb / 2, 8, 256 / groups, (int64_t)kMaxSplits});
+  if (cap <= 1) return 1;
+  const int64_t per = (lb + cap - 1) / cap;   // blocks in the longest part
+  return (int)((lb + per - 1) / per);
 }
 
 // Pointer checks and the launch of a resolved call with `splits` parts (> 1: the

@@ -457,8 +457,12 @@ def test_workspace_plan():
     w.r0.n_rows = 4096                      # 128-row window: at most 6 blocks reachable + 8
     assert da.ds4attn_workspace_bytes(w, False) == 4 * 7 * rec
     long = _ratio128_args()
-    long.r0.n_rows = 4096                   # no window: 128 + 8 blocks, at most 10 parts
-    assert da.ds4attn_workspace_bytes(long, False) == 4 * 10 * rec
+    long.r0.n_rows = 4096                   # no window: 128 + 8 blocks, at most 8 parts
+    assert da.ds4attn_workspace_bytes(long, False) == 4 * 8 * rec
+    r4 = _ratio128_args()
+    r4.r1.n_rows = 32 * 20 - 128            # 20 blocks: 8 parts would hold 3 blocks at most, as 7 do
+    r4.r1.stride_b = r4.r1.n_rows * 1024
+    assert da.ds4attn_workspace_bytes(r4, False) == 4 * 7 * rec
     e = _ratio128_args()
     e.batch = 0
     assert da.ds4attn_workspace_bytes(e, False) == 0
